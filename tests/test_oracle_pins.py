@@ -1,0 +1,349 @@
+"""Pins for the CPU oracle, each fixed by something other than the oracle.
+
+Sources of truth used here:
+* hand-worked streams (tests/golden/), derived by hand from "Compressing DMA
+  Engine: Leveraging Activation Sparsity for Training Deep Neural Networks",
+  §V.A Compression Algorithm and §VII.A Compression Efficiency;
+* the page's own figure for an all-zero window (§V.A: 32x for 32 four-byte
+  values, one all-zero mask word -- which also fixes the mask polarity);
+* closed forms: ZVC size = 4*ceil(n/32) + esz*nnz, RLE size = 8(Wr+1) +
+  2*sum(padded runs) + esz*nnz, with nnz and runs counted by brute force;
+* the page's claim that ZVC's ratio does not depend on the layout of the
+  activations while run-length coding's does (§VII.A);
+* the library-routine form (np.packbits + boolean compaction, np.diff runs);
+* exhaustive enumeration of every zero/nonzero pattern for tiny n;
+* bitwise round trips over random and special bit patterns.
+"""
+
+import itertools
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+import oracle
+from oracle import np_forms
+
+import golden_io
+
+CASES = golden_io.all_cases()
+
+
+# --------------------------------------------------------------------------
+# hand-worked streams
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("case", CASES, ids=[c["name"] for c in CASES])
+def test_golden_stream_c_oracle(case):
+    comp = oracle.zvc_compress if case["algo"] == "zvc" else oracle.rle_compress
+    s = comp(case["x"])
+    assert s.size == case["size"]
+    assert bytes(s) == bytes(case["stream"])
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c["name"] for c in CASES])
+def test_golden_stream_numpy_form(case):
+    comp = np_forms.zvc_compress if case["algo"] == "zvc" else np_forms.rle_compress
+    assert bytes(comp(case["x"])) == bytes(case["stream"])
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c["name"] for c in CASES])
+def test_golden_decode(case):
+    dec = oracle.zvc_decompress if case["algo"] == "zvc" else oracle.rle_decompress
+    out, err = dec(case["stream"], case["n"], case["esz"])
+    assert err == 0
+    assert np.array_equal(out, case["x"])
+    ndec = np_forms.zvc_decompress if case["algo"] == "zvc" else np_forms.rle_decompress
+    assert np.array_equal(ndec(case["stream"], case["n"], case["esz"]), case["x"])
+
+
+# --------------------------------------------------------------------------
+# the page's all-zero window figure
+# --------------------------------------------------------------------------
+
+def test_all_zero_window_is_one_zero_mask_32x():
+    x = np.zeros(32, dtype=np.float32)
+    s = oracle.zvc_compress(x)
+    assert s.size == 4 and not s.any()
+    assert x.nbytes / s.size == 32.0
+
+
+def test_all_zero_many_windows_32x():
+    x = np.zeros(32 * 1000, dtype=np.float32)
+    assert x.nbytes / oracle.zvc_compress(x).size == 32.0
+
+
+# --------------------------------------------------------------------------
+# closed forms with brute-force counts
+# --------------------------------------------------------------------------
+
+def _brute_nnz(b):
+    return sum(1 for v in b.tolist() if v != 0)
+
+
+@pytest.mark.parametrize("esz", [2, 4])
+@pytest.mark.parametrize("n", [0, 1, 5, 31, 32, 33, 63, 64, 65, 1000, 4097])
+@pytest.mark.parametrize("dens", [0.0, 0.3, 1.0])
+def test_zvc_size_closed_form(esz, n, dens):
+    rng = np.random.default_rng(n * 7 + esz)
+    dt = np.uint32 if esz == 4 else np.uint16
+    x = rng.integers(1, 2 ** (8 * esz), size=n, dtype=np.uint64).astype(dt)
+    x[rng.random(n) >= dens] = 0
+    expect = 4 * ((n + 31) // 32) + esz * _brute_nnz(x)
+    assert oracle.zvc_compress(x).size == expect
+    assert oracle.zvc_size(x) == expect
+
+
+def _brute_runs(nzlist):
+    """Alternating run count, zero run first, by walking the list."""
+    runs, cur, kind = [], 0, False
+    for v in nzlist:
+        if v == kind:
+            cur += 1
+        else:
+            runs.append(cur)
+            kind, cur = v, 1
+    runs.append(cur)
+    return runs
+
+
+@pytest.mark.parametrize("esz", [2, 4])
+@pytest.mark.parametrize("n", [1, 2, 3, 1023, 1024, 1025, 2047, 2048, 2049, 5000])
+def test_rle_size_closed_form(esz, n):
+    rng = np.random.default_rng(n * 11 + esz)
+    dt = np.uint32 if esz == 4 else np.uint16
+    # clustered indicator: a two-state Markov chain
+    nz = np.zeros(n, dtype=bool)
+    state = False
+    for i in range(n):
+        if rng.random() < 0.05:
+            state = not state
+        nz[i] = state
+    x = np.where(nz, rng.integers(1, 2 ** (8 * esz), size=n, dtype=np.uint64), 0).astype(dt)
+    E = 4096 // esz
+    wr = (n + E - 1) // E
+    ent = 0
+    for w in range(wr):
+        r = len(_brute_runs([bool(v) for v in nz[w * E:(w + 1) * E]]))
+        ent += r + (r % 2 if esz == 4 else 0)
+    expect = 8 * (wr + 1) + 2 * ent + esz * _brute_nnz(x)
+    assert oracle.rle_compress(x).size == expect
+    assert oracle.rle_size(x) == expect
+
+
+def test_rle_runs_brute_force_small():
+    rng = np.random.default_rng(5)
+    for _ in range(200):
+        n = int(rng.integers(1, 40))
+        x = (rng.random(n) < 0.5).astype(np.uint32) * 0x3F800000
+        s = oracle.rle_compress(x)
+        p = int(s[4:8].view("<u4")[0])
+        runs = s[16:16 + 2 * p].view("<u2").tolist()
+        want = _brute_runs([bool(v) for v in x])
+        if len(want) % 2:
+            want = want + [0]
+        assert runs == want
+
+
+# --------------------------------------------------------------------------
+# exhaustive tiny inputs
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("esz", [2, 4])
+def test_exhaustive_patterns_small_n(esz):
+    dt = np.uint32 if esz == 4 else np.uint16
+    for n in range(1, 11):
+        for pat in itertools.product((0, 1), repeat=n):
+            x = np.array([(i + 1) * 0x101 if p else 0 for i, p in enumerate(pat)], dtype=dt)
+            for comp, ncomp, dec in ((oracle.zvc_compress, np_forms.zvc_compress, oracle.zvc_decompress),
+                                     (oracle.rle_compress, np_forms.rle_compress, oracle.rle_decompress)):
+                s = comp(x)
+                assert bytes(s) == bytes(ncomp(x))
+                out, err = dec(s, n, esz)
+                assert err == 0 and np.array_equal(out, x)
+
+
+# --------------------------------------------------------------------------
+# layout invariance (ZVC) vs layout sensitivity (RLE), §VII.A
+# --------------------------------------------------------------------------
+
+def test_zvc_size_is_layout_invariant_rle_is_not():
+    from synth import clustered_relu
+    x = clustered_relu((2, 8, 28, 28), 0.7, 2.0, seed=9)
+    nchw = x.reshape(-1)
+    nhwc = np.ascontiguousarray(x.transpose(0, 2, 3, 1)).reshape(-1)
+    perm = np.random.default_rng(3).permutation(nchw)
+    z = {k: oracle.zvc_compress(v).size for k, v in (("nchw", nchw), ("nhwc", nhwc), ("perm", perm))}
+    r = {k: oracle.rle_compress(v).size for k, v in (("nchw", nchw), ("nhwc", nhwc), ("perm", perm))}
+    assert len(set(z.values())) == 1
+    assert len(set(r.values())) == 3
+    assert r["nchw"] < r["perm"]
+
+
+# --------------------------------------------------------------------------
+# cross-form invariants
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("esz", [2, 4])
+def test_rle_and_zvc_carry_the_same_values_and_bitmap(esz):
+    from synth import clustered_relu
+    dt = np.float32 if esz == 4 else np.float16
+    x = clustered_relu((1, 4, 40, 40), 0.6, 2.0, seed=11, dtype=dt).reshape(-1)
+    b = x.view(np.uint32 if esz == 4 else np.uint16)
+    n = b.size
+    z = oracle.zvc_compress(b)
+    W = (n + 31) // 32
+    zvals = z[4 * W:]
+    r = oracle.rle_compress(b)
+    E = 4096 // esz
+    wr = (n + E - 1) // E
+    idx = r[:8 * (wr + 1)].view("<u4")
+    run_off, val_off = idx[:wr + 1], idx[wr + 1:]
+    rvals, bitmap = [], np.zeros(n, dtype=bool)
+    for w in range(wr):
+        p, nv = int(run_off[w + 1] - run_off[w]), int(val_off[w + 1] - val_off[w])
+        at = 8 * (wr + 1) + 2 * int(run_off[w]) + esz * int(val_off[w])
+        runs = r[at:at + 2 * p].view("<u2").astype(int)
+        pos = w * E
+        for k, ln in enumerate(runs):
+            if k % 2:
+                bitmap[pos:pos + ln] = True
+            pos += ln
+        rvals.append(r[at + 2 * p: at + 2 * p + esz * nv])
+    assert bytes(np.concatenate(rvals)) == bytes(zvals)
+    masks = z[:4 * W].view("<u4")
+    unpacked = np.unpackbits(masks.view(np.uint8), bitorder="little")[:n].astype(bool)
+    assert np.array_equal(unpacked, bitmap)
+
+
+@pytest.mark.parametrize("algo", ["zvc", "rle"])
+def test_encode_of_decode_is_identity(algo):
+    rng = np.random.default_rng(17)
+    x = rng.integers(0, 3, size=3001).astype(np.uint32) * 0x40000001
+    comp = oracle.zvc_compress if algo == "zvc" else oracle.rle_compress
+    dec = oracle.zvc_decompress if algo == "zvc" else oracle.rle_decompress
+    s = comp(x)
+    out, err = dec(s, x.size, 4)
+    assert err == 0
+    assert bytes(comp(out)) == bytes(s)
+
+
+# --------------------------------------------------------------------------
+# bitwise round trips, including patterns a float compare would mangle
+# --------------------------------------------------------------------------
+
+_special32 = st.sampled_from([0, 0x80000000, 1, 0x007FFFFF, 0x80000001, 0x7FC00000,
+                              0x7F800001, 0x7F800000, 0xFF800000, 0x3F800000])
+_special16 = st.sampled_from([0, 0x8000, 1, 0x03FF, 0x8001, 0x7E00, 0x7C01, 0x7C00, 0xFC00, 0x3C00])
+
+
+@settings(max_examples=150, deadline=None)
+@given(st.lists(st.one_of(_special32, st.integers(0, 2 ** 32 - 1)), max_size=2500),
+       st.sampled_from(["zvc", "rle"]))
+def test_round_trip_fp32_patterns(vals, algo):
+    x = np.array(vals, dtype=np.uint32)
+    comp = oracle.zvc_compress if algo == "zvc" else oracle.rle_compress
+    dec = oracle.zvc_decompress if algo == "zvc" else oracle.rle_decompress
+    s = comp(x)
+    out, err = dec(s, x.size, 4)
+    assert err == 0 and np.array_equal(out, x)
+    ncomp = np_forms.zvc_compress if algo == "zvc" else np_forms.rle_compress
+    assert bytes(ncomp(x)) == bytes(s)
+
+
+@settings(max_examples=150, deadline=None)
+@given(st.lists(st.one_of(_special16, st.integers(0, 2 ** 16 - 1)), max_size=5000),
+       st.sampled_from(["zvc", "rle"]))
+def test_round_trip_fp16_patterns(vals, algo):
+    x = np.array(vals, dtype=np.uint16)
+    comp = oracle.zvc_compress if algo == "zvc" else oracle.rle_compress
+    dec = oracle.zvc_decompress if algo == "zvc" else oracle.rle_decompress
+    s = comp(x)
+    out, err = dec(s, x.size, 2)
+    assert err == 0 and np.array_equal(out, x)
+    ncomp = np_forms.zvc_compress if algo == "zvc" else np_forms.rle_compress
+    assert bytes(ncomp(x)) == bytes(s)
+
+
+def test_negative_zero_is_kept():
+    x = np.array([0.0, -0.0, 0.0, 1.0], dtype=np.float32)
+    s = oracle.zvc_compress(x)
+    assert s.size == 4 + 8
+    out, _ = oracle.zvc_decompress(s, 4, 4)
+    assert out.tolist() == [0, 0x80000000, 0, 0x3F800000]
+
+
+# --------------------------------------------------------------------------
+# statistics: iid zeros give the expected ratio (a loose check)
+# --------------------------------------------------------------------------
+
+def test_iid_ratio_matches_expectation():
+    from synth import iid_relu
+    x = iid_relu(1 << 20, 0.5, seed=1)
+    ratio = x.nbytes / oracle.zvc_compress(x).size
+    assert abs(ratio - 4 / (0.125 + 4 * 0.5)) < 0.01
+
+
+# --------------------------------------------------------------------------
+# corrupt streams are reported
+# --------------------------------------------------------------------------
+
+def test_zvc_corruptions():
+    x = np.array([0, 5, 0, 7, 0, 0, 9], dtype=np.uint32)
+    s = oracle.zvc_compress(x)
+    bad = s.copy()
+    bad[0] |= 0x80  # bit 7 is past n = 7
+    assert oracle.zvc_decompress(bad, 7, 4)[1] & oracle.E_MASK_PAST_N
+    assert oracle.zvc_decompress(s[:-1], 7, 4)[1] == oracle.E_SIZE
+    assert oracle.zvc_decompress(np.concatenate([s, s[:4]]), 7, 4)[1] == oracle.E_SIZE
+    bad = s.copy()
+    bad[0] &= 0xFD  # drop element 1: one value too many
+    assert oracle.zvc_decompress(bad, 7, 4)[1] == oracle.E_SIZE
+    assert oracle.zvc_decompress(s[:2], 7, 4)[1] == oracle.E_SIZE
+
+
+def test_rle_corruptions():
+    x = np.zeros(1030, dtype=np.uint32)
+    x[5:8] = 1
+    x[1000:1026] = 2
+    s = oracle.rle_compress(x)
+    assert oracle.rle_decompress(s, 1030, 4)[1] == 0
+    # run 1 of window 0 from 3 to 4: runs no longer sum to 1024, one nonzero too many
+    bad = s.copy()
+    bad[24 + 2] = 4
+    e = oracle.rle_decompress(bad, 1030, 4)[1]
+    assert e & oracle.E_RUN_SUM and e & oracle.E_VAL_COUNT
+    # a zero-length run that is not the first
+    bad = s.copy()
+    bad[24 + 2] = 0
+    assert oracle.rle_decompress(bad, 1030, 4)[1] & oracle.E_RUN_FORM
+    # index decreasing
+    bad = s.copy()
+    bad[4] = 9  # run_off[1] = 9 > run_off[2] = 8
+    assert oracle.rle_decompress(bad, 1030, 4)[1] & oracle.E_INDEX
+    # truncation
+    assert oracle.rle_decompress(s[:-2], 1030, 4)[1] & oracle.E_SIZE
+    # odd entry count for 4-byte elements
+    y = np.zeros(8, dtype=np.uint32)
+    t = oracle.rle_compress(y)  # runs [8, 0]: p = 2
+    bad = t.copy()
+    bad[4] = 1  # run_off[1] = 1 (odd)
+    assert oracle.rle_decompress(bad, 8, 4)[1] & oracle.E_RUN_FORM
+
+
+# --------------------------------------------------------------------------
+# offload image = chunk streams back to back
+# --------------------------------------------------------------------------
+
+def test_offload_stream_is_chunk_concatenation():
+    from synth import iid_relu
+    x = iid_relu(10000, 0.6, seed=4)
+    img, sizes = oracle.offload_stream(x, 4096)
+    assert len(sizes) == 3 and sum(sizes) == img.size
+    b = x.view(np.uint32)
+    lo = 0
+    for k, sz in enumerate(sizes):
+        part = img[lo:lo + sz]
+        out, err = oracle.zvc_decompress(part, min(4096, b.size - 4096 * k), 4)
+        assert err == 0 and np.array_equal(out, b[4096 * k: 4096 * (k + 1)])
+        lo += sz
