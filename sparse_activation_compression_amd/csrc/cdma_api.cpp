@@ -1,0 +1,92 @@
+// cdma_api.cpp -- the C ABI of libcdma: argument checks, sizing and dispatch.
+//
+// Every check that can be made on the host is made here, before anything is
+// enqueued, so a bad call never reaches the GPU.
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+#include "cdma.h"
+#include "launch.hpp"
+
+namespace {
+
+bool algo_ok(int algo) { return algo == CDMA_ALGO_ZVC || algo == CDMA_ALGO_RLE; }
+bool esz_ok(int esz) { return esz == 2 || esz == 4; }
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+uint64_t max_n(int algo) { return algo == CDMA_ALGO_ZVC ? CDMA_ZVC_MAX_N : CDMA_RLE_MAX_N; }
+uint64_t rle_window(int esz) { return 4096u / (unsigned)esz; }
+
+uint64_t tiles(int algo, int esz, uint64_t n) {
+  return algo == CDMA_ALGO_ZVC ? cdma::zvc_tiles(esz, n) : cdma::rle_tiles(esz, n);
+}
+
+}  // namespace
+
+extern "C" {
+
+uint64_t cdma_max_compressed_bytes(int algo, int esz, uint64_t n) {
+  if (!algo_ok(algo) || !esz_ok(esz) || n > max_n(algo)) return 0;
+  if (algo == CDMA_ALGO_ZVC) return 4 * ((n + 31) / 32) + (uint64_t)esz * n;
+  const uint64_t wr = (n + rle_window(esz) - 1) / rle_window(esz);
+  return 8 * (wr + 1) + 2 * (n + 2 * wr) + (uint64_t)esz * n;
+}
+
+uint64_t cdma_workspace_bytes(int algo, int esz, uint64_t n) {
+  if (!algo_ok(algo) || !esz_ok(esz) || n > max_n(algo)) return 0;
+  // counter, one scan status word per tile, and (ZVC) one value offset per tile
+  const uint64_t t = tiles(algo, esz, n);
+  return algo == CDMA_ALGO_ZVC ? cdma::kWsHeader + 12 * t + 16 : cdma::kWsHeader + 8 * t;
+}
+
+int cdma_compress(int algo, int esz, const void* d_src, uint64_t n, void* d_dst, uint64_t dst_capacity,
+                  uint64_t* d_out_bytes, void* d_ws, uint64_t ws_bytes, void* stream) {
+  if (!algo_ok(algo) || !esz_ok(esz) || n > max_n(algo)) return CDMA_ERR_INVALID_ARG;
+  if (!d_out_bytes || !aligned(d_out_bytes, 8)) return CDMA_ERR_INVALID_ARG;
+  if (!d_dst || !aligned(d_dst, 16)) {
+    if (n > 0 || algo == CDMA_ALGO_RLE) return CDMA_ERR_INVALID_ARG;  // an empty RLE stream is 8 bytes
+  }
+  if (dst_capacity < cdma_max_compressed_bytes(algo, esz, n)) return CDMA_ERR_CAPACITY;
+  if (n > 0) {
+    if (!d_src || !d_ws) return CDMA_ERR_INVALID_ARG;
+    if (!aligned(d_src, 16) || !aligned(d_ws, 8)) return CDMA_ERR_INVALID_ARG;
+    if (ws_bytes < cdma_workspace_bytes(algo, esz, n)) return CDMA_ERR_CAPACITY;
+  }
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = algo == CDMA_ALGO_ZVC
+                           ? cdma::zvc_compress_launch(esz, d_src, n, d_dst, d_out_bytes, d_ws, s)
+                           : cdma::rle_compress_launch(esz, d_src, n, d_dst, d_out_bytes, d_ws, s);
+  return e == hipSuccess ? CDMA_OK : CDMA_ERR_HIP;
+}
+
+int cdma_decompress(int algo, int esz, const void* d_src, uint64_t src_capacity, const uint64_t* d_src_bytes,
+                    uint64_t n, void* d_dst, uint32_t* d_error, void* d_ws, uint64_t ws_bytes, void* stream) {
+  if (!algo_ok(algo) || !esz_ok(esz) || n > max_n(algo)) return CDMA_ERR_INVALID_ARG;
+  if (d_src_bytes && !aligned(d_src_bytes, 8)) return CDMA_ERR_INVALID_ARG;
+  if (d_error && !aligned(d_error, 4)) return CDMA_ERR_INVALID_ARG;
+  if (n > 0) {
+    if (!d_dst || !d_ws || (src_capacity > 0 && !d_src)) return CDMA_ERR_INVALID_ARG;
+    if (!aligned(d_src, 16) || !aligned(d_dst, 16) || !aligned(d_ws, 8)) return CDMA_ERR_INVALID_ARG;
+    if (ws_bytes < cdma_workspace_bytes(algo, esz, n)) return CDMA_ERR_CAPACITY;
+  }
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e =
+      algo == CDMA_ALGO_ZVC
+          ? cdma::zvc_decompress_launch(esz, d_src, src_capacity, d_src_bytes, n, d_dst, d_error, d_ws, s)
+          : cdma::rle_decompress_launch(esz, d_src, src_capacity, d_src_bytes, n, d_dst, d_error, d_ws, s);
+  return e == hipSuccess ? CDMA_OK : CDMA_ERR_HIP;
+}
+
+const char* cdma_status_string(int status) {
+  switch (status) {
+    case CDMA_OK: return "ok";
+    case CDMA_ERR_INVALID_ARG: return "invalid argument";
+    case CDMA_ERR_CAPACITY: return "buffer too small";
+    case CDMA_ERR_CORRUPT: return "corrupt stream";
+    case CDMA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int cdma_version(void) { return 100; }
+
+}  // extern "C"

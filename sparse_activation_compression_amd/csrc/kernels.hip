@@ -1,0 +1,214 @@
+// kernels.hip -- instantiations and launchers of the gfx950 codec kernels.
+#include <mutex>
+
+#include "launch.hpp"
+#include "zvc_kernels.hpp"
+#include "rle_kernels.hpp"
+
+namespace cdma {
+
+// 16-byte vectors per lane per tile: 4 -> 16 KB of input per workgroup.
+#ifndef CDMA_ZVC_V
+#define CDMA_ZVC_V 4
+#endif
+constexpr int kZvcV = CDMA_ZVC_V;
+
+__global__ void fill_zero_u64_kernel(uint64_t* __restrict__ p, uint64_t count) {
+  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count;
+       i += (uint64_t)gridDim.x * blockDim.x)
+    p[i] = 0;
+}
+
+__global__ void store_u64_kernel(uint64_t* p, uint64_t v) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) *p = v;
+}
+
+// Clear the ticket counter and the per-tile status words with a kernel (not a
+// memset node), so the sequence stays correct if a caller captures it.
+static hipError_t clear_workspace(void* ws, uint64_t tiles, hipStream_t s) {
+  const uint64_t words = (kWsHeader + 8 * tiles) / 8;
+  uint64_t blocks = (words + 255) / 256;
+  if (blocks > 2048) blocks = 2048;
+  fill_zero_u64_kernel<<<(unsigned)blocks, 256, 0, s>>>(static_cast<uint64_t*>(ws), words);
+  return hipGetLastError();
+}
+
+static uint32_t* ws_counter(void* ws) { return static_cast<uint32_t*>(ws); }
+static uint64_t* ws_status(void* ws) {
+  return reinterpret_cast<uint64_t*>(static_cast<uint8_t*>(ws) + kWsHeader);
+}
+
+uint64_t zvc_tiles(int esz, uint64_t n) {
+  const uint64_t te = esz == 4 ? ZvcShape<4, kZvcV>::TE : ZvcShape<2, kZvcV>::TE;
+  return (n + te - 1) / te;
+}
+
+uint64_t zvc_compress_tiles(int esz, uint64_t n) {
+  const uint64_t te = esz == 4 ? ZvcCShape<4>::TE : ZvcCShape<2>::TE;
+  return (n + te - 1) / te;
+}
+
+// Workgroups of `kernel` that fit on the current device at once (all CUs),
+// cached per (kernel, device).
+static uint64_t resident_groups(const void* kernel, int block = kBlock) {
+  struct Entry {
+    const void* k;
+    int dev;
+    uint64_t groups;
+  };
+  static Entry cache[64];
+  static int used = 0;
+  static std::mutex mu;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  std::lock_guard<std::mutex> lock(mu);
+  for (int i = 0; i < used; ++i)
+    if (cache[i].k == kernel && cache[i].dev == dev) return cache[i].groups;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 1;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, 0) != hipSuccess || per_cu <= 0)
+    per_cu = 1;
+  const uint64_t groups = (uint64_t)cus * (uint64_t)per_cu;
+  if (used < 64) cache[used++] = Entry{kernel, dev, groups};
+  return groups;
+}
+
+template <int ESZ>
+static hipError_t zvc_compress_t(const void* src, uint64_t n, void* dst, uint64_t* out_bytes, void* ws,
+                                 hipStream_t s) {
+  const uint64_t tiles = zvc_compress_tiles(ESZ, n);
+  hipError_t e = clear_workspace(ws, tiles, s);
+  if (e != hipSuccess) return e;
+  // co-resident persistent grid: launched cooperatively so every workgroup
+  // is running at once (the static tile order relies on it)
+  auto kern = zvc_compress_kernel<ESZ>;
+  const uint64_t res = resident_groups(reinterpret_cast<const void*>(kern), kCBlock);
+  const unsigned grid = (unsigned)(tiles < res ? tiles : res);
+  const uint8_t* a_src = static_cast<const uint8_t*>(src);
+  uint8_t* a_dst = static_cast<uint8_t*>(dst);
+  uint64_t* a_status = ws_status(ws);
+  uint32_t a_tiles = (uint32_t)tiles;
+  void* args[] = {&a_src, &n, &a_dst, &out_bytes, &a_status, &a_tiles};
+  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kern), dim3(grid), dim3(kCBlock), args, 0, s);
+}
+
+// per-tile value offsets live after the status words of the super tiles
+static uint32_t* ws_offsets(void* ws, uint64_t tiles) {
+  return reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + kWsHeader + 8 * tiles);
+}
+
+template <int ESZ>
+static hipError_t zvc_decompress_t(const void* src, uint64_t cap, const uint64_t* src_bytes, uint64_t n,
+                                   void* dst, uint32_t* error, void* ws, hipStream_t s) {
+  using C = ZvcScanShape<ESZ, kZvcV>;
+  const uint64_t tiles = zvc_tiles(ESZ, n);
+  const uint64_t supers = (tiles + C::SUPER - 1) / C::SUPER;
+  hipError_t e = clear_workspace(ws, supers, s);
+  if (e != hipSuccess) return e;
+  uint32_t* offsets = ws_offsets(ws, tiles);
+  zvc_offsets_kernel<ESZ, kZvcV><<<(unsigned)supers, kBlock, 0, s>>>(
+      static_cast<const uint8_t*>(src), cap, src_bytes, n, offsets, error, ws_counter(ws), ws_status(ws),
+      (uint32_t)tiles, (uint32_t)supers);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  auto kern = zvc_expand_kernel<ESZ, kZvcV>;
+  const uint64_t res = resident_groups(reinterpret_cast<const void*>(kern));
+  const unsigned grid = (unsigned)(tiles < res ? tiles : res);
+  kern<<<grid, kBlock, 0, s>>>(static_cast<const uint8_t*>(src), cap, src_bytes, n, static_cast<uint8_t*>(dst),
+                               error, offsets, (uint32_t)tiles);
+  return hipGetLastError();
+}
+
+// n = 0: the stream must be empty (ZVC) or the 8-byte zero index (RLE).
+__global__ void empty_stream_check_kernel(const uint8_t* src, uint64_t cap, const uint64_t* src_bytes,
+                                          uint32_t* error, int rle) {
+  if (threadIdx.x != 0 || blockIdx.x != 0 || !error) return;
+  const uint64_t claimed = src_bytes ? *src_bytes : cap;
+  const uint64_t eff = claimed < cap ? claimed : cap;
+  uint32_t e = 0;
+  if (rle) {
+    uint32_t idx = 0;
+    for (uint64_t b = 0; b < 8 && b < eff; ++b) idx |= src[b];
+    if (idx) e |= CDMA_E_INDEX;
+    if (src_bytes && *src_bytes != 8) e |= CDMA_E_SIZE;
+  } else if (src_bytes && *src_bytes != 0) {
+    e |= CDMA_E_SIZE;
+  }
+  if (e) atomicOr(error, e);
+}
+
+hipError_t zvc_compress_launch(int esz, const void* src, uint64_t n, void* dst, uint64_t* out_bytes,
+                               void* ws, hipStream_t s) {
+  if (n == 0) {
+    store_u64_kernel<<<1, 64, 0, s>>>(out_bytes, 0);
+    return hipGetLastError();
+  }
+  return esz == 4 ? zvc_compress_t<4>(src, n, dst, out_bytes, ws, s)
+                  : zvc_compress_t<2>(src, n, dst, out_bytes, ws, s);
+}
+
+hipError_t zvc_decompress_launch(int esz, const void* src, uint64_t cap, const uint64_t* src_bytes,
+                                 uint64_t n, void* dst, uint32_t* error, void* ws, hipStream_t s) {
+  if (n == 0) {
+    empty_stream_check_kernel<<<1, 64, 0, s>>>(static_cast<const uint8_t*>(src), cap, src_bytes, error, 0);
+    return hipGetLastError();
+  }
+  return esz == 4 ? zvc_decompress_t<4>(src, cap, src_bytes, n, dst, error, ws, s)
+                  : zvc_decompress_t<2>(src, cap, src_bytes, n, dst, error, ws, s);
+}
+
+uint64_t rle_tiles(int esz, uint64_t n) {
+  const uint64_t te = esz == 4 ? RleShape<4>::TE : RleShape<2>::TE;
+  return (n + te - 1) / te;
+}
+
+template <int ESZ>
+static hipError_t rle_compress_t(const void* src, uint64_t n, void* dst, uint64_t* out_bytes, void* ws,
+                                 hipStream_t s) {
+  const uint64_t tiles = rle_tiles(ESZ, n);
+  hipError_t e = clear_workspace(ws, tiles, s);
+  if (e != hipSuccess) return e;
+  rle_compress_kernel<ESZ><<<(unsigned)tiles, kBlock, 0, s>>>(
+      static_cast<const uint8_t*>(src), n, static_cast<uint8_t*>(dst), out_bytes, ws_counter(ws),
+      ws_status(ws), (uint32_t)tiles);
+  return hipGetLastError();
+}
+
+template <int ESZ>
+static hipError_t rle_decompress_t(const void* src, uint64_t cap, const uint64_t* src_bytes, uint64_t n,
+                                   void* dst, uint32_t* error, hipStream_t s) {
+  const uint64_t tiles = rle_tiles(ESZ, n);
+  rle_decompress_kernel<ESZ><<<(unsigned)tiles, kBlock, 0, s>>>(
+      static_cast<const uint8_t*>(src), cap, src_bytes, n, static_cast<uint8_t*>(dst), error, (uint32_t)tiles);
+  return hipGetLastError();
+}
+
+// n = 0 still has a stream: the index of one window offset pair (8 bytes of zeros).
+__global__ void rle_empty_kernel(uint8_t* dst, uint64_t* out_bytes) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) {
+    reinterpret_cast<uint32_t*>(dst)[0] = 0;
+    reinterpret_cast<uint32_t*>(dst)[1] = 0;
+    *out_bytes = 8;
+  }
+}
+
+hipError_t rle_compress_launch(int esz, const void* src, uint64_t n, void* dst, uint64_t* out_bytes, void* ws,
+                               hipStream_t s) {
+  if (n == 0) {
+    rle_empty_kernel<<<1, 64, 0, s>>>(static_cast<uint8_t*>(dst), out_bytes);
+    return hipGetLastError();
+  }
+  return esz == 4 ? rle_compress_t<4>(src, n, dst, out_bytes, ws, s)
+                  : rle_compress_t<2>(src, n, dst, out_bytes, ws, s);
+}
+
+hipError_t rle_decompress_launch(int esz, const void* src, uint64_t cap, const uint64_t* src_bytes, uint64_t n,
+                                 void* dst, uint32_t* error, void*, hipStream_t s) {
+  if (n == 0) {
+    empty_stream_check_kernel<<<1, 64, 0, s>>>(static_cast<const uint8_t*>(src), cap, src_bytes, error, 1);
+    return hipGetLastError();
+  }
+  return esz == 4 ? rle_decompress_t<4>(src, cap, src_bytes, n, dst, error, s)
+                  : rle_decompress_t<2>(src, cap, src_bytes, n, dst, error, s);
+}
+
+}  // namespace cdma

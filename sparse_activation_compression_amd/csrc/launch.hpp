@@ -1,0 +1,26 @@
+// launch.hpp -- host-side entry points into the device code (kernels.hip).
+// Arguments are already validated by the C ABI layer; these only size grids,
+// clear workspaces and enqueue kernels on the given stream.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace cdma {
+
+constexpr uint64_t kWsHeader = 256;  // tile-ticket counter, padded
+
+uint64_t zvc_tiles(int esz, uint64_t n);           // decompress tiles
+uint64_t zvc_compress_tiles(int esz, uint64_t n);  // compress tiles (fewer, larger)
+uint64_t rle_tiles(int esz, uint64_t n);
+
+hipError_t zvc_compress_launch(int esz, const void* src, uint64_t n, void* dst, uint64_t* out_bytes,
+                               void* ws, hipStream_t s);
+hipError_t zvc_decompress_launch(int esz, const void* src, uint64_t src_capacity, const uint64_t* src_bytes,
+                                 uint64_t n, void* dst, uint32_t* error, void* ws, hipStream_t s);
+hipError_t rle_compress_launch(int esz, const void* src, uint64_t n, void* dst, uint64_t* out_bytes,
+                               void* ws, hipStream_t s);
+hipError_t rle_decompress_launch(int esz, const void* src, uint64_t src_capacity, const uint64_t* src_bytes,
+                                 uint64_t n, void* dst, uint32_t* error, void* ws, hipStream_t s);
+
+}  // namespace cdma

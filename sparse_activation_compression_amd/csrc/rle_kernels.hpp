@@ -1,0 +1,404 @@
+// rle_kernels.hpp -- run-length variant of the activation codec for gfx950.
+//
+// "Compressing DMA Engine: Leveraging Activation Sparsity for Training Deep
+// Neural Networks", §V.A Compression Algorithm: run-length coding exploits
+// clustered zeros and nonzeros; §VII.A Compression Efficiency: 4 KB window.
+//
+// Stream: u32 run_off[Wr+1], u32 val_off[Wr+1], then per window of
+// E = 4096/ESZ elements a block of p_w u16 run lengths (alternating zero and
+// nonzero runs, zero run first; for ESZ == 4 an odd list gets one 0 pad
+// entry) followed by its v_w nonzero elements.  run_off / val_off are the
+// exclusive prefix sums of p_w / v_w.
+//
+// One wavefront owns one window: 4 vectors of 16 bytes per lane cover exactly
+// E elements, so each window's bitmap (E/32 mask words), runs and values are
+// produced by one wave, and a workgroup of 4 waves handles 4 windows.
+//
+// compress:   load -> nonzero bits -> window masks in LDS (DPP OR) -> run
+//             boundaries = mask XOR (mask shifted by one element) -> per-wave
+//             counts of boundaries and nonzeros -> one decoupled lookback over
+//             the packed pair (entries, nonzeros) gives the tile's byte offset
+//             -> run lengths (gaps between boundaries) and values compacted
+//             into LDS at their final alignment -> aligned 16-byte stores.
+// decompress: the index gives each window's block offset directly (no scan)
+//             -> block read into LDS -> run starts by a wave prefix sum ->
+//             boundary bitmap (LDS XOR) -> prefix-XOR turns boundaries back
+//             into the nonzero bitmap -> the same expansion as ZVC.
+#pragma once
+
+#include "zvc_kernels.hpp"
+
+namespace cdma {
+
+template <int ESZ>
+struct RleShape {
+  static constexpr int V = 4;                      // 16-byte vectors per lane
+  static constexpr int EPL = 16 / ESZ;             // elements per vector
+  static constexpr int LPW = 32 / EPL;             // lanes per 32-element mask word
+  static constexpr int E = 4096 / ESZ;             // window = one wavefront's elements
+  static constexpr int TE = kWaves * E;            // elements per tile (4 windows)
+  static constexpr int WPW = E / 32;               // mask words per window (32 or 64)
+  static constexpr int MAXENT = E + 2;             // run entries incl. padding, upper bound
+  static constexpr int BLK = 2 * MAXENT + ESZ * E;  // largest block in bytes
+  static constexpr int STAGE = kWaves * BLK + 32;  // compress: the tile's blocks + alignment
+  static constexpr int WSTAGE = BLK + 32;          // decompress: one window's block + alignment
+  static_assert(V * 64 * EPL == E, "a wavefront must cover one window");
+};
+
+constexpr uint32_t kLow31 = (1u << 31) - 1;
+
+__device__ __forceinline__ uint32_t wave_incl_max(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, true));   // row_shr:1
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, true));   // row_shr:2
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, true));   // row_shr:4
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, true));   // row_shr:8
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false));  // row_bcast:15
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false));  // row_bcast:31
+  return v;
+}
+
+__device__ __forceinline__ void lds_u16(uint8_t* base, uint32_t byte, uint32_t v) {
+  *reinterpret_cast<uint16_t*>(base + byte) = (uint16_t)v;
+}
+
+// ---------------------------------------------------------------------------
+// compress
+// ---------------------------------------------------------------------------
+
+template <int ESZ>
+__global__ __launch_bounds__(kBlock) void rle_compress_kernel(
+    const uint8_t* __restrict__ src, uint64_t n, uint8_t* __restrict__ dst,
+    uint64_t* __restrict__ out_bytes, uint32_t* __restrict__ counter,
+    uint64_t* __restrict__ status, uint32_t num_tiles) {
+  using S = RleShape<ESZ>;
+  constexpr int V = S::V;
+  __shared__ uint32_t s_ticket;
+  __shared__ uint64_t s_excl;
+  __shared__ bool s_stuck;
+  __shared__ uint32_t s_tot[kWaves * V];
+  __shared__ uint32_t s_mask[kWaves * S::WPW];
+  __shared__ uint32_t s_p[kWaves], s_v[kWaves];
+  __shared__ __attribute__((aligned(16))) uint8_t s_stage[S::STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = (int)lane_id();
+  const int wave = tid >> 6;
+  if (tid == 0) s_ticket = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const uint32_t t = s_ticket;
+  const uint64_t Wr = (n + S::E - 1) / S::E;
+  const uint64_t H = 8 * (Wr + 1);
+  const uint64_t gw = (uint64_t)t * kWaves + wave;  // this wave's window
+  const uint64_t e_win = gw * S::E;
+  const uint32_t Lw = gw < Wr ? (uint32_t)(n - e_win < (uint64_t)S::E ? n - e_win : S::E) : 0;
+
+  u32x4 v[V];
+#pragma unroll
+  for (int j = 0; j < V; ++j) v[j] = load_vec<ESZ>(src, e_win + (uint64_t)(j * 64 + lane) * S::EPL, n);
+
+  uint32_t bits[V], ex[V];
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    const uint32_t c = (uint32_t)(j * 64 + lane);  // vector index inside the window
+    bits[j] = vec_nz_bits<ESZ>(v[j]);
+    const uint32_t m = group_or<S::LPW>(bits[j] << ((lane % S::LPW) * S::EPL));
+    if (lane % S::LPW == 0) s_mask[wave * S::WPW + c / S::LPW] = m;
+    const uint32_t cnt = (uint32_t)__builtin_popcount(bits[j]);
+    const uint32_t inc = wave_incl_scan(cnt);
+    ex[j] = inc - cnt;
+    if (lane == 63) s_tot[wave * V + j] = inc;
+  }
+  __syncthreads();
+
+  uint32_t vbase[V], v_w = 0;
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    vbase[j] = v_w;
+    v_w += s_tot[wave * V + j];
+  }
+
+  // run boundaries of this wave's window: lane g holds mask word g
+  const uint32_t g = (uint32_t)lane;
+  uint32_t T = 0;
+  if (g < (uint32_t)S::WPW && 32 * g < Lw) {
+    const uint32_t m = s_mask[wave * S::WPW + g];
+    const uint32_t prev = g ? s_mask[wave * S::WPW + g - 1] : 0u;
+    T = m ^ ((m << 1) | (prev >> 31));  // element before the window counts as zero
+    const uint32_t rem = Lw - 32 * g;
+    if (rem < 32) T &= (1u << rem) - 1;
+  }
+  const uint32_t tc = (uint32_t)__builtin_popcount(T);
+  const uint32_t tinc = wave_incl_scan(tc);
+  const uint32_t texcl = tinc - tc;
+  const uint32_t r_w = Lw ? 1 + read_lane(tinc, 63) : 0;
+  const uint32_t p_w = ESZ == 4 ? r_w + (r_w & 1) : r_w;
+  if (lane == 0) {
+    s_p[wave] = p_w;
+    s_v[wave] = v_w;
+  }
+  __syncthreads();
+
+  uint32_t P = 0, Vs = 0, blk = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    if (w == wave) blk = 2 * P + ESZ * Vs;
+    P += s_p[w];
+    Vs += s_v[w];
+  }
+  const uint32_t span = 2 * P + ESZ * Vs;
+  if (wave == 0) {
+    bool stuck;
+    const uint64_t x = lookback_exclusive(status, t, ((uint64_t)P << 31) | Vs, &stuck);
+    if (lane == 0) {
+      s_excl = x;
+      s_stuck = stuck;
+    }
+  }
+  __syncthreads();
+  const uint64_t RX = s_excl >> 31, VX = s_excl & kLow31;
+  const uint64_t O = H + 2 * RX + (uint64_t)ESZ * VX;  // first byte of this tile's blocks
+  const uint32_t shift = (uint32_t)(O & 15);
+
+  // index entries of this tile's windows (fixed offsets)
+  if (tid < kWaves) {
+    const uint64_t w = (uint64_t)t * kWaves + tid;
+    if (w < Wr) {
+      uint32_t pr = 0, vr = 0;
+      for (int k = 0; k < tid; ++k) {
+        pr += s_p[k];
+        vr += s_v[k];
+      }
+      reinterpret_cast<uint32_t*>(dst)[w] = (uint32_t)(RX + pr);
+      reinterpret_cast<uint32_t*>(dst + 4 * (Wr + 1))[w] = (uint32_t)(VX + vr);
+    }
+  }
+  if (t == num_tiles - 1 && tid == 0) {
+    reinterpret_cast<uint32_t*>(dst)[Wr] = (uint32_t)(RX + P);
+    reinterpret_cast<uint32_t*>(dst + 4 * (Wr + 1))[Wr] = (uint32_t)(VX + Vs);
+  }
+
+  // run lengths: the gap from the previous boundary (0 at the window start)
+  const uint32_t bw = shift + blk;
+  if (Lw) {
+    const uint32_t lastpos = T ? 32 * g + 31 - (uint32_t)__builtin_clz(T) : 0u;
+    const uint32_t imax = wave_incl_max(lastpos);
+    const uint32_t before = __shfl_up(imax, 1, 64);
+    uint32_t prev = lane ? before : 0u;
+    const uint32_t tau_last = read_lane(imax, 63);
+    uint32_t x = T, k = 1 + texcl;
+    while (x) {
+      const uint32_t b = (uint32_t)__builtin_ctz(x);
+      x &= x - 1;
+      const uint32_t pos = 32 * g + b;
+      lds_u16(s_stage, bw + 2 * (k - 1), pos - prev);
+      prev = pos;
+      ++k;
+    }
+    if (lane == 0) {
+      lds_u16(s_stage, bw + 2 * (r_w - 1), Lw - tau_last);
+      if (p_w > r_w) lds_u16(s_stage, bw + 2 * r_w, 0);
+    }
+  }
+  // values follow the runs
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    uint32_t pos = bw + 2 * p_w + ESZ * (vbase[j] + ex[j]);
+#pragma unroll
+    for (int k = 0; k < S::EPL; ++k) {
+      if ((bits[j] >> k) & 1u) {
+        store_elem<ESZ>(s_stage + pos, vec_elem<ESZ>(v[j], k));
+        pos += ESZ;
+      }
+    }
+  }
+  __syncthreads();
+
+  const uint64_t beg = O, end = O + span;
+  const uint64_t q0 = beg >> 4, q1 = (end + 15) >> 4;
+  for (uint64_t q = q0 + tid; q < q1; q += kBlock) {
+    const uint64_t qb = q << 4;
+    const uint32_t lo = (uint32_t)(qb - (q0 << 4));
+    if (qb >= beg && qb + 16 <= end) {
+      *reinterpret_cast<u32x4*>(dst + qb) = *reinterpret_cast<const u32x4*>(s_stage + lo);
+    } else {
+      for (int k = 0; k < 16; k += 2) {
+        const uint64_t b = qb + k;
+        if (b >= beg && b < end) *reinterpret_cast<uint16_t*>(dst + b) = *reinterpret_cast<const uint16_t*>(s_stage + lo + k);
+      }
+    }
+  }
+  if (t == num_tiles - 1 && tid == 0) *out_bytes = s_stuck ? kSizeInternalError : end;
+}
+
+// ---------------------------------------------------------------------------
+// decompress
+// ---------------------------------------------------------------------------
+
+// Read a little-endian u32 at stream byte off; bytes at or past eff read as 0.
+__device__ __forceinline__ uint32_t stream_u32(const uint8_t* __restrict__ src, uint64_t eff, uint64_t off) {
+  if (off + 4 <= eff && (off & 3) == 0) return *reinterpret_cast<const uint32_t*>(src + off);
+  uint32_t v = 0;
+  for (int b = 0; b < 4; ++b)
+    if (off + b < eff) v |= (uint32_t)src[off + b] << (8 * b);
+  return v;
+}
+
+template <int ESZ>
+__global__ __launch_bounds__(kBlock) void rle_decompress_kernel(
+    const uint8_t* __restrict__ src, uint64_t src_capacity, const uint64_t* __restrict__ src_bytes,
+    uint64_t n, uint8_t* __restrict__ dst, uint32_t* __restrict__ error, uint32_t num_tiles) {
+  using S = RleShape<ESZ>;
+  constexpr int V = S::V;
+  __shared__ uint32_t s_err;
+  __shared__ uint32_t s_map[kWaves * S::WPW];  // boundary bitmap, then nonzero bitmap
+  __shared__ __attribute__((aligned(16))) uint8_t s_blk[kWaves][S::WSTAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = (int)lane_id();
+  const int wave = tid >> 6;
+  const uint32_t t = blockIdx.x;
+  if (tid == 0) s_err = 0;
+  for (int i = tid; i < kWaves * S::WPW; i += kBlock) s_map[i] = 0;
+  const uint64_t claimed = src_bytes ? *src_bytes : src_capacity;
+  const uint64_t eff = claimed < src_capacity ? claimed : src_capacity;
+  const uint64_t Wr = (n + S::E - 1) / S::E;
+  const uint64_t H = 8 * (Wr + 1);
+  const uint64_t gw = (uint64_t)t * kWaves + wave;
+  const uint64_t e_win = gw * S::E;
+  const uint32_t Lw = gw < Wr ? (uint32_t)(n - e_win < (uint64_t)S::E ? n - e_win : S::E) : 0;
+  uint32_t err = 0;
+  if (t == 0 && tid == 0 && (stream_u32(src, eff, 0) | stream_u32(src, eff, 4 * (Wr + 1))))
+    err |= CDMA_E_INDEX;
+  if (t == num_tiles - 1 && tid == 0 && src_bytes) {
+    const uint64_t rt = stream_u32(src, eff, 4 * Wr), vt = stream_u32(src, eff, 4 * (Wr + 1) + 4 * Wr);
+    if (H + 2 * rt + (uint64_t)ESZ * vt != *src_bytes) err |= CDMA_E_SIZE;
+  }
+  __syncthreads();
+
+  // this wave's block
+  bool valid = false;
+  uint32_t p = 0, nv = 0, nvs = 0;
+  uint64_t B = 0;
+  if (Lw) {
+    const uint32_t r0 = stream_u32(src, eff, 4 * gw), r1 = stream_u32(src, eff, 4 * gw + 4);
+    const uint32_t v0 = stream_u32(src, eff, 4 * (Wr + 1) + 4 * gw);
+    const uint32_t v1 = stream_u32(src, eff, 4 * (Wr + 1) + 4 * gw + 4);
+    if (r1 < r0 || v1 < v0) {
+      err |= CDMA_E_INDEX;
+    } else {
+      p = r1 - r0;
+      nv = v1 - v0;
+      if (p == 0 || p > Lw + 2) {
+        err |= CDMA_E_RUN_FORM;
+      } else {
+        valid = true;
+        nvs = nv < Lw ? nv : Lw;  // never stage more values than the window holds
+        B = H + 2 * (uint64_t)r0 + (uint64_t)ESZ * v0;
+      }
+    }
+  }
+  uint8_t* blk = s_blk[wave];
+  uint32_t shift = 0;
+  if (valid) {
+    const uint64_t beg = B, end = B + 2 * (uint64_t)p + (uint64_t)ESZ * nvs;
+    shift = (uint32_t)(beg & 15);
+    const uint64_t q0 = beg >> 4, q1 = (end + 15) >> 4;
+    bool short_read = false;
+    for (uint64_t q = q0 + lane; q < q1; q += 64) {
+      const uint64_t qb = q << 4;
+      const uint32_t lo = (uint32_t)(qb - (q0 << 4));
+      if (qb + 16 <= eff) {
+        *reinterpret_cast<u32x4*>(blk + lo) = *reinterpret_cast<const u32x4*>(src + qb);
+      } else {
+        for (int k = 0; k < 16; k += 2) {
+          const uint64_t b = qb + k;
+          uint32_t e = 0;
+          if (b + 2 <= eff) e = *reinterpret_cast<const uint16_t*>(src + b);
+          else if (b >= beg && b < end) short_read = true;
+          lds_u16(blk, lo + k, e);
+        }
+      }
+    }
+    if (__ballot(short_read)) err |= CDMA_E_SIZE;
+  }
+  __syncthreads();
+
+  // run starts -> boundary bitmap; checks
+  if (valid) {
+    auto entry = [&](uint32_t k) -> uint32_t { return *reinterpret_cast<const uint16_t*>(blk + shift + 2 * k); };
+    uint32_t r = p;
+    if (ESZ == 4) {
+      if (p & 1) err |= CDMA_E_RUN_FORM;
+      else if (entry(p - 1) == 0) r = p - 1;
+    }
+    const uint32_t per = (r + 63) / 64;
+    const uint32_t k0 = (uint32_t)lane * per < r ? (uint32_t)lane * per : r;
+    const uint32_t k1 = k0 + per < r ? k0 + per : r;
+    uint32_t sum = 0, odd = 0;
+    bool zero_len = false;
+    for (uint32_t k = k0; k < k1; ++k) {
+      const uint32_t len = entry(k);
+      sum += len;
+      if (k & 1) odd += len;
+      if (len == 0 && k != 0) zero_len = true;
+    }
+    const uint32_t inc = wave_incl_scan(sum);
+    uint32_t start = inc - sum;
+    for (uint32_t k = k0; k < k1; ++k) {
+      if (k > 0 && start < Lw) atomicXor(&s_map[wave * S::WPW + start / 32], 1u << (start % 32));
+      start += entry(k);
+    }
+    const uint32_t total = read_lane(inc, 63);
+    const uint32_t odd_total = read_lane(wave_incl_scan(odd), 63);
+    if (total != Lw) err |= CDMA_E_RUN_SUM;
+    if (odd_total != nv) err |= CDMA_E_VAL_COUNT;
+    if (__ballot(zero_len)) err |= CDMA_E_RUN_FORM;
+  }
+  __syncthreads();
+
+  // boundaries -> nonzero bitmap (prefix XOR across the window)
+  {
+    const uint32_t g = (uint32_t)lane;
+    uint32_t x = 0;
+    if (g < (uint32_t)S::WPW) x = s_map[wave * S::WPW + g];
+    const uint32_t par = wave_incl_scan((uint32_t)__builtin_popcount(x) & 1u) - ((uint32_t)__builtin_popcount(x) & 1u);
+    x ^= x << 1;
+    x ^= x << 2;
+    x ^= x << 4;
+    x ^= x << 8;
+    x ^= x << 16;
+    if (par & 1u) x = ~x;
+    if (!valid || 32 * g >= Lw) x = 0;
+    else if (Lw - 32 * g < 32) x &= (1u << (Lw - 32 * g)) - 1;
+    if (g < (uint32_t)S::WPW) s_map[wave * S::WPW + g] = x;
+  }
+  __syncthreads();
+
+  // expand
+  const uint32_t vals = shift + 2 * p;
+  uint32_t base = 0;
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    const uint32_t c = (uint32_t)(j * 64 + lane);
+    const uint32_t b = (s_map[wave * S::WPW + c / S::LPW] >> ((c % S::LPW) * S::EPL)) & ((1u << S::EPL) - 1);
+    const uint32_t cnt = (uint32_t)__builtin_popcount(b);
+    const uint32_t inc = wave_incl_scan(cnt);
+    uint32_t q = base + inc - cnt;
+    u32x4 o = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int k = 0; k < S::EPL; ++k) {
+      if ((b >> k) & 1u) {
+        if (q < nvs) vec_set<ESZ>(o, k, load_elem<ESZ>(blk + vals + ESZ * q));
+        ++q;
+      }
+    }
+    base += read_lane(inc, 63);
+    if (Lw) store_vec<ESZ>(dst, e_win + (uint64_t)c * S::EPL, n, o);
+  }
+
+  if (err) atomicOr(&s_err, err);
+  __syncthreads();
+  if (tid == 0 && s_err && error) atomicOr(error, s_err);
+}
+
+}  // namespace cdma

@@ -1,0 +1,628 @@
+// zvc_kernels.hpp -- zero-value compression and decompression for gfx950.
+//
+// Format ("Compressing DMA Engine: Leveraging Activation Sparsity for Training
+// Deep Neural Networks", §V.A Compression Algorithm): per window of 32
+// consecutive elements a 32-bit mask (bit i = element i is nonzero), then the
+// nonzero elements.  All W = ceil(n/32) masks come first, then all values in
+// index order, so every mask sits at a fixed offset and a single prefix sum
+// over nonzero counts places every value.
+//
+// One workgroup handles one tile of TE elements (V 16-byte vectors per lane,
+// 256 lanes).  Vector j of wave w covers bytes [(w*V + j) * 1024, +1024) of the
+// tile, so every global load and store instruction moves 1 KB of contiguous
+// memory per wavefront.  A 32-element window spans LPW = 32/EPL lanes (8 for
+// fp32, 4 for fp16), so its mask is an OR across a DPP lane group.
+//
+// compress:   load -> per-lane nonzero bits -> window masks (DPP OR) and
+//             per-lane counts (DPP wave scan) -> LDS pass over the 4*V wave
+//             segments -> masks stored -> decoupled lookback gives the tile's
+//             value offset -> nonzeros compacted into LDS at their final byte
+//             alignment -> aligned 16-byte stores (element stores only for the
+//             two partial 16-byte quads at the ends of the tile's span).
+// decompress: masks -> counts -> same scan and lookback -> the tile's value
+//             span is read into LDS with aligned 16-byte loads -> each lane
+//             expands its vector from LDS -> aligned 16-byte stores.
+#pragma once
+
+#include "device_common.hpp"
+
+namespace cdma {
+
+template <int ESZ, int V>
+struct ZvcShape {
+  static constexpr int EPL = 16 / ESZ;              // elements per 16-byte vector
+  static constexpr int TE = kBlock * V * EPL;       // elements per tile
+  static constexpr int LPW = 32 / EPL;              // lanes per 32-element window
+  static constexpr int WPT = TE / 32;               // windows per tile
+  static constexpr int SEG = kWaves * V;            // wave segments per tile
+  static constexpr int STAGE = TE * ESZ + 32;       // LDS staging bytes
+};
+
+// Per-element nonzero bits of one 16-byte vector (bit k = element k).
+template <int ESZ>
+__device__ __forceinline__ uint32_t vec_nz_bits(u32x4 v) {
+  if constexpr (ESZ == 4) {
+    return (uint32_t)(v.x != 0) | ((uint32_t)(v.y != 0) << 1) | ((uint32_t)(v.z != 0) << 2) |
+           ((uint32_t)(v.w != 0) << 3);
+  } else {
+    uint32_t r = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t w = v[k];
+      r |= ((uint32_t)((w & 0xFFFFu) != 0) << (2 * k)) | ((uint32_t)((w >> 16) != 0) << (2 * k + 1));
+    }
+    return r;
+  }
+}
+
+template <int ESZ>
+__device__ __forceinline__ uint32_t vec_elem(u32x4 v, int k) {
+  if constexpr (ESZ == 4) return v[k];
+  else return (v[k >> 1] >> ((k & 1) * 16)) & 0xFFFFu;
+}
+
+template <int ESZ>
+__device__ __forceinline__ void vec_set(u32x4& v, int k, uint32_t e) {
+  if constexpr (ESZ == 4) v[k] = e;
+  else v[k >> 1] |= e << ((k & 1) * 16);
+}
+
+template <int ESZ>
+__device__ __forceinline__ uint32_t load_elem(const uint8_t* p) {
+  if constexpr (ESZ == 4) return *reinterpret_cast<const uint32_t*>(p);
+  else return *reinterpret_cast<const uint16_t*>(p);
+}
+
+template <int ESZ>
+__device__ __forceinline__ void store_elem(uint8_t* p, uint32_t e) {
+  if constexpr (ESZ == 4) *reinterpret_cast<uint32_t*>(p) = e;
+  else *reinterpret_cast<uint16_t*>(p) = (uint16_t)e;
+}
+
+// Load the 16-byte vector of elements [e0, e0 + EPL); elements >= n read as 0.
+template <int ESZ>
+__device__ __forceinline__ u32x4 load_vec(const uint8_t* __restrict__ src, uint64_t e0, uint64_t n) {
+  constexpr int EPL = 16 / ESZ;
+  if (e0 + EPL <= n) return *reinterpret_cast<const u32x4*>(src + e0 * ESZ);
+  u32x4 v = {0u, 0u, 0u, 0u};
+  for (int k = 0; k < EPL; ++k)
+    if (e0 + k < n) vec_set<ESZ>(v, k, load_elem<ESZ>(src + (e0 + k) * ESZ));
+  return v;
+}
+
+// Store the vector of elements [e0, e0 + EPL); elements >= n are not stored.
+template <int ESZ>
+__device__ __forceinline__ void store_vec(uint8_t* __restrict__ dst, uint64_t e0, uint64_t n, u32x4 v) {
+  constexpr int EPL = 16 / ESZ;
+  if (e0 + EPL <= n) {
+    *reinterpret_cast<u32x4*>(dst + e0 * ESZ) = v;
+    return;
+  }
+  for (int k = 0; k < EPL; ++k)
+    if (e0 + k < n) store_elem<ESZ>(dst + (e0 + k) * ESZ, vec_elem<ESZ>(v, k));
+}
+
+// Tile-local bases of this wave's V segments and the tile total, from the
+// per-segment totals in LDS (segment order = element order).
+template <int V>
+__device__ __forceinline__ uint32_t segment_bases(const uint32_t* s_tot, int wave, uint32_t (&base)[V]) {
+  uint32_t acc = 0, total = 0;
+  for (int k = 0; k < wave * V; ++k) acc += s_tot[k];
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    base[j] = acc;
+    acc += s_tot[wave * V + j];
+  }
+  for (int k = 0; k < kWaves * V; ++k) total += s_tot[k];
+  return total;
+}
+
+// ---------------------------------------------------------------------------
+// compress: one 1024-thread workgroup per CU, 64 KB tiles, lag-1 pipeline
+// ---------------------------------------------------------------------------
+//
+// The grid is launched cooperatively with G workgroups, all resident at once;
+// workgroup w handles tiles w, w+G, w+2G, ... in order.  Iteration i of a
+// workgroup:
+//   1. wave 0 issues the first lookback round for the previous tile p = t-G,
+//      whose aggregate (and that of every tile of its band) was published one
+//      iteration earlier;
+//   2. all waves classify tile t (prefetched into registers): window masks go
+//      straight to their fixed place in the stream, the nonzeros are compacted
+//      into LDS buffer i%2, and t's aggregate is published;
+//   3. the next tile t+G is prefetched;
+//   4. wave 0 resolves p's lookback (its reads have returned meanwhile) and
+//      publishes p's inclusive prefix;
+//   5. all waves store p's values from LDS buffer (i-1)%2, realigned to their
+//      byte position in the stream.
+// Vector-memory counters retire in order, so the lookback reads of step 1 are
+// consumed in step 4 without waiting for the prefetch of step 3.
+// Progress: the smallest unclassified tile's workgroup has classified every
+// tile before it in its own order, and a lookback only waits for unclassified
+// predecessors; with all workgroups resident it always advances.
+
+constexpr int kCBlock = 1024;
+constexpr int kCWaves = kCBlock / 64;
+
+template <int ESZ>
+struct ZvcCShape {
+  static constexpr int V = 4;                      // 16-byte vectors per lane
+  static constexpr int EPL = 16 / ESZ;
+  static constexpr int TE = kCBlock * V * EPL;     // elements per tile (64 KB)
+  static constexpr int LPW = 32 / EPL;
+  static constexpr int WPT = TE / 32;              // windows per tile
+  static constexpr int SEG = kCWaves * V;          // wave segments per tile
+  static constexpr int STAGE = TE * ESZ + 16;
+  static_assert(SEG == 64, "one lane per wave segment in the tile scan");
+  static_assert(WPT <= kCBlock, "one mask store per thread");
+};
+
+template <int ESZ>
+struct ZvcCLds {
+  using S = ZvcCShape<ESZ>;
+  uint64_t excl;         // exclusive prefix of the tile being stored
+  uint32_t total[2];     // nonzeros held in stage[b]
+  bool stuck;
+  uint32_t tot[S::SEG];
+  uint32_t mask[S::WPT];
+  __attribute__((aligned(16))) uint8_t stage[2][S::STAGE];
+};
+
+template <int ESZ>
+__device__ __forceinline__ void zvc_c_load_full(u32x4 (&v)[ZvcCShape<ESZ>::V], const uint8_t* __restrict__ src,
+                                                uint32_t t, int wave, int lane) {
+  using S = ZvcCShape<ESZ>;
+  const uint8_t* p = src + (uint64_t)t * (S::TE * ESZ) + (uint64_t)(wave * S::V * 64 + lane) * 16;
+#pragma unroll
+  for (int j = 0; j < S::V; ++j) v[j] = *reinterpret_cast<const u32x4*>(p + j * 1024);
+}
+
+template <int ESZ>
+__device__ __forceinline__ void zvc_c_load_bounded(u32x4 (&v)[ZvcCShape<ESZ>::V], const uint8_t* __restrict__ src,
+                                                   uint64_t n, uint32_t t, int wave, int lane) {
+  using S = ZvcCShape<ESZ>;
+  const uint64_t e_tile = (uint64_t)t * S::TE;
+#pragma unroll
+  for (int j = 0; j < S::V; ++j) {
+    const uint32_t c = (uint32_t)((wave * S::V + j) * 64 + lane);
+    v[j] = load_vec<ESZ>(src, e_tile + (uint64_t)c * S::EPL, n);
+  }
+}
+
+// Store the T staged values of a tile to stream bytes [A, A + ESZ*T): aligned
+// 16-byte stores, the staged bytes shifted into place on the way.
+template <int ESZ>
+__device__ __forceinline__ void zvc_c_store_values(const uint8_t* __restrict__ st, uint32_t T, uint64_t A,
+                                                   uint8_t* __restrict__ dst, int tid) {
+  const uint64_t end = A + (uint64_t)ESZ * T;
+  const uint64_t q0 = A >> 4, q1 = (end + 15) >> 4;
+  const uint32_t d = (uint32_t)(A & 15);
+  const uint32_t* sw = reinterpret_cast<const uint32_t*>(st);
+  for (uint64_t q = q0 + tid; q < q1; q += kCBlock) {
+    const uint64_t qb = q << 4;
+    if (qb >= A && qb + 16 <= end) {
+      const uint32_t o = (uint32_t)(qb - A);  // staged byte of the quad's first byte
+      u32x4 out;
+      if (d == 0) {
+        out = *reinterpret_cast<const u32x4*>(st + o);
+      } else if ((d & 3) == 0) {
+        const uint32_t i = o >> 2;
+        out = u32x4{sw[i], sw[i + 1], sw[i + 2], sw[i + 3]};
+      } else {  // 16-bit elements, 2 bytes off a word boundary
+        const uint32_t i = o >> 2;
+        const uint32_t w0 = sw[i], w1 = sw[i + 1], w2 = sw[i + 2], w3 = sw[i + 3], w4 = sw[i + 4];
+        out = u32x4{__builtin_amdgcn_alignbyte(w1, w0, 2), __builtin_amdgcn_alignbyte(w2, w1, 2),
+                    __builtin_amdgcn_alignbyte(w3, w2, 2), __builtin_amdgcn_alignbyte(w4, w3, 2)};
+      }
+      *reinterpret_cast<u32x4*>(dst + qb) = out;
+    } else {
+      for (int k = 0; k < 16; k += ESZ) {
+        const uint64_t b = qb + k;
+        if (b >= A && b < end) store_elem<ESZ>(dst + b, load_elem<ESZ>(st + (b - A)));
+      }
+    }
+  }
+}
+
+// One pipeline iteration: classify tile t from `cur` (if t < num_tiles),
+// prefetch t+G into `nxt`, resolve and store the previous tile t-G (if
+// have_prev).  Returns with the workgroup synchronised.
+template <int ESZ>
+__device__ __forceinline__ void zvc_c_iteration(ZvcCLds<ESZ>& L, u32x4 (&cur)[ZvcCShape<ESZ>::V],
+                                                u32x4 (&nxt)[ZvcCShape<ESZ>::V], uint32_t t, bool have_prev,
+                                                int buf, uint32_t G, uint32_t full, uint64_t W,
+                                                const uint8_t* __restrict__ src, uint64_t n,
+                                                uint8_t* __restrict__ dst, uint64_t* __restrict__ out_bytes,
+                                                uint64_t* __restrict__ status, uint32_t num_tiles, int tid,
+                                                int wave, int lane) {
+  using S = ZvcCShape<ESZ>;
+  constexpr int V = S::V;
+  const bool have_cur = t < num_tiles;
+  const uint32_t tp = t - G;  // tile to store (valid when have_prev)
+
+  uint32_t bits[V], ex[V];
+  if (have_cur) {
+    if (t >= full) {  // the one partial tile: load bounded, drain so nothing stays pending on cur
+      zvc_c_load_bounded<ESZ>(cur, src, n, t, wave, lane);
+      __builtin_amdgcn_s_waitcnt(0);
+    }
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      const uint32_t c = (uint32_t)((wave * V + j) * 64 + lane);
+      bits[j] = vec_nz_bits<ESZ>(cur[j]);
+      const uint32_t m = group_or<S::LPW>(bits[j] << ((lane % S::LPW) * S::EPL));
+      if (lane % S::LPW == 0) L.mask[c / S::LPW] = m;
+      const uint32_t cnt = (uint32_t)__builtin_popcount(bits[j]);
+      const uint32_t inc = wave_incl_scan(cnt);
+      ex[j] = inc - cnt;
+      if (lane == 63) L.tot[wave * V + j] = inc;
+    }
+  }
+  __syncthreads();
+
+  // The previous tile's lookback reads go out now; its aggregate and those of
+  // its band were published an iteration ago.  They return while this tile's
+  // values are compacted and the next tile's loads are issued.
+  LookbackRound r;
+  if (wave == 0 && have_prev && tp > 0) lookback_issue(status, (int64_t)tp - 1, r);
+
+  if (have_cur) {
+    // segment bases: lane l of every wave scans the 64 segment totals
+    const uint32_t x = L.tot[lane];
+    const uint32_t inc = wave_incl_scan(x);
+    const uint32_t T = read_lane(inc, 63);
+    if (tid == 0) {
+      L.total[buf] = T;
+      status_store(&status[t], (t == 0 ? kFlagPrefix : kFlagAggregate) | T);
+    }
+    if (tid < S::WPT) {
+      const uint64_t g = (uint64_t)t * S::WPT + tid;
+      if (g < W) reinterpret_cast<uint32_t*>(dst)[g] = L.mask[tid];
+    }
+    uint8_t* st = L.stage[buf];
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      uint32_t pos = ESZ * (read_lane(inc - x, wave * V + j) + ex[j]);
+#pragma unroll
+      for (int k = 0; k < S::EPL; ++k) {
+        if ((bits[j] >> k) & 1u) {
+          store_elem<ESZ>(st + pos, vec_elem<ESZ>(cur[j], k));
+          pos += ESZ;
+        }
+      }
+    }
+    if (t + G < full) zvc_c_load_full<ESZ>(nxt, src, t + G, wave, lane);
+  }
+  if (wave == 0 && have_prev) {
+    bool stuck = false;
+    const uint64_t X = tp > 0 ? lookback_resolve(status, tp, r, &stuck) : 0;
+    if (lane == 0) {
+      L.excl = X;
+      L.stuck = stuck;
+      if (tp > 0) status_store(&status[tp], kFlagPrefix | (X + L.total[buf ^ 1]));
+    }
+  }
+  __syncthreads();
+
+  if (have_prev) {
+    const uint32_t T = L.total[buf ^ 1];
+    const uint64_t A = 4 * W + (uint64_t)ESZ * L.excl;
+    zvc_c_store_values<ESZ>(L.stage[buf ^ 1], T, A, dst, tid);
+    // Only the last tile reports the size; its lookback passes over every
+    // tile, so if any lookback could not finish, neither could this one.
+    if (tp == num_tiles - 1 && tid == 0) *out_bytes = L.stuck ? kSizeInternalError : A + (uint64_t)ESZ * T;
+  }
+  __syncthreads();
+}
+
+template <int ESZ>
+__global__ __launch_bounds__(kCBlock) void zvc_compress_kernel(
+    const uint8_t* __restrict__ src, uint64_t n, uint8_t* __restrict__ dst,
+    uint64_t* __restrict__ out_bytes, uint64_t* __restrict__ status, uint32_t num_tiles) {
+  using S = ZvcCShape<ESZ>;
+  __shared__ ZvcCLds<ESZ> L;
+  const int tid = threadIdx.x;
+  const int lane = (int)lane_id();
+  const int wave = tid >> 6;
+  const uint32_t G = gridDim.x;
+  const uint64_t W = (n + 31) / 32;
+  const uint32_t full = (uint32_t)(n / S::TE);  // tiles with no element past n
+  uint32_t t = blockIdx.x;                      // < num_tiles: the grid never exceeds the tiles
+  u32x4 ra[S::V], rb[S::V];
+  if (t < full) zvc_c_load_full<ESZ>(ra, src, t, wave, lane);
+  // two iterations per trip so the register sets swap roles without copies;
+  // the iteration with no tile left to classify only stores the last one
+  bool have_prev = false;
+  for (;;) {
+    zvc_c_iteration<ESZ>(L, ra, rb, t, have_prev, 0, G, full, W, src, n, dst, out_bytes, status, num_tiles,
+                         tid, wave, lane);
+    if (t >= num_tiles) break;
+    t += G;
+    have_prev = true;
+    zvc_c_iteration<ESZ>(L, rb, ra, t, have_prev, 1, G, full, W, src, n, dst, out_bytes, status, num_tiles,
+                         tid, wave, lane);
+    if (t >= num_tiles) break;
+    t += G;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// decompress, pass 1: value offset of every tile from the masks alone
+// ---------------------------------------------------------------------------
+//
+// A super tile is SUPER consecutive ZVC tiles (32 KB of masks).  Each
+// workgroup popcounts its masks, scans the per-tile counts and joins a
+// decoupled lookback over super tiles; it writes offsets[t] = number of
+// nonzeros before tile t (offsets[num_tiles] = total).  Mask bytes at or past
+// the readable size count as 0; mask bits for indices >= n are not counted.
+
+template <int ESZ, int V>
+struct ZvcScanShape {
+  using S = ZvcShape<ESZ, V>;
+  static constexpr int WORDS = 8192;                 // mask words per super tile
+  static constexpr int SUPER = WORDS / S::WPT;       // ZVC tiles per super tile
+  static constexpr int WPTH = WORDS / kBlock;        // mask words per thread (32)
+  static constexpr int TPT = S::WPT / WPTH;          // threads per ZVC tile
+  static_assert(SUPER <= 64 && TPT >= 1 && S::WPT % WPTH == 0, "super tile shape");
+};
+
+template <int ESZ, int V>
+__global__ __launch_bounds__(kBlock) void zvc_offsets_kernel(
+    const uint8_t* __restrict__ src, uint64_t src_capacity, const uint64_t* __restrict__ src_bytes,
+    uint64_t n, uint32_t* __restrict__ offsets, uint32_t* __restrict__ error,
+    uint32_t* __restrict__ counter, uint64_t* __restrict__ status, uint32_t num_tiles,
+    uint32_t num_super) {
+  using C = ZvcScanShape<ESZ, V>;
+  __shared__ uint32_t s_ticket;
+  __shared__ uint32_t s_cnt[C::SUPER];
+  const int tid = threadIdx.x;
+  const int lane = (int)lane_id();
+  const int wave = tid >> 6;
+  if (tid == 0) s_ticket = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int i = tid; i < C::SUPER; i += kBlock) s_cnt[i] = 0;
+  __syncthreads();
+  const uint32_t u = s_ticket;
+  const uint64_t W = (n + 31) / 32;
+  const uint64_t claimed = src_bytes ? *src_bytes : src_capacity;
+  const uint64_t eff = claimed < src_capacity ? claimed : src_capacity;
+  const uint64_t g0 = (uint64_t)u * C::WORDS + (uint64_t)tid * C::WPTH;  // first mask word of this thread
+  uint32_t cnt = 0, err = 0;
+#pragma unroll
+  for (int k = 0; k < C::WPTH; k += 4) {
+    const uint64_t g = g0 + k;
+    u32x4 m = {0u, 0u, 0u, 0u};
+    if (g + 4 <= W && 4 * (g + 4) <= eff) {
+      m = *reinterpret_cast<const u32x4*>(src + 4 * g);
+    } else {
+      for (int i = 0; i < 4; ++i) {
+        if (g + i >= W) break;
+        uint32_t w = 0;
+        for (int b = 0; b < 4; ++b)
+          if (4 * (g + i) + b < eff) w |= (uint32_t)src[4 * (g + i) + b] << (8 * b);
+        m[i] = w;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t w = m[i];
+      if (g + i == W - 1 && (n & 31)) {
+        const uint32_t valid = (1u << (n & 31)) - 1;
+        if (w & ~valid) err |= CDMA_E_MASK_PAST_N;
+        w &= valid;
+      }
+      cnt += (uint32_t)__builtin_popcount(w);
+    }
+  }
+  if (cnt) atomicAdd(&s_cnt[tid / C::TPT], cnt);
+  __syncthreads();
+  uint32_t c = 0, inc = 0, total = 0;
+  if (wave == 0) {
+    c = lane < C::SUPER ? s_cnt[lane] : 0u;
+    inc = wave_incl_scan(c);
+    total = read_lane(inc, 63);
+    bool stuck;
+    const uint64_t x = lookback_exclusive(status, u, total, &stuck);
+    if (stuck) err |= CDMA_E_INTERNAL;
+    const uint64_t t = (uint64_t)u * C::SUPER + lane;
+    if (lane < C::SUPER && t < num_tiles) offsets[t] = (uint32_t)(x + inc - c);
+    if (u == num_super - 1 && lane == 0) offsets[num_tiles] = (uint32_t)(x + total);
+  }
+  if (err && error) atomicOr(error, err);
+}
+
+// ---------------------------------------------------------------------------
+// decompress, pass 2: expand, persistent grid-stride with prefetch
+// ---------------------------------------------------------------------------
+//
+// With the offsets known, tiles are independent.  Each workgroup walks tiles
+// t, t+G, t+2G, ...; while it expands tile a from LDS it already has the
+// masks and value quads of tile b = a+G in flight in registers, and the
+// offsets of tile b+G on their way.
+
+template <int ESZ, int V>
+struct ZvcExpandShape {
+  using S = ZvcShape<ESZ, V>;
+  static constexpr int QPT = (S::TE * ESZ / 16 + 2 + kBlock - 1) / kBlock;  // value quads per thread
+  static constexpr int MPT = (S::WPT + kBlock - 1) / kBlock;                // mask words per thread
+};
+
+template <int ESZ, int V>
+struct ZvcTileIn {
+  using X = ZvcExpandShape<ESZ, V>;
+  u32x4 q[X::QPT];
+  uint32_t m[X::MPT];
+  uint64_t beg, end;  // value span in the stream
+  bool short_read;
+};
+
+template <int ESZ, int V>
+__device__ __forceinline__ void zvc_fetch_tile(ZvcTileIn<ESZ, V>& in, const uint8_t* __restrict__ src, uint64_t eff,
+                                               uint64_t W, uint32_t t, uint32_t o0, uint32_t o1, int tid) {
+  using S = ZvcShape<ESZ, V>;
+  using X = ZvcExpandShape<ESZ, V>;
+#pragma unroll
+  for (int k = 0; k < X::MPT; ++k) {
+    const int i = tid + k * kBlock;
+    const uint64_t g = (uint64_t)t * S::WPT + i;
+    uint32_t w = 0;
+    if (i < S::WPT && g < W) {
+      if (4 * g + 4 <= eff) {
+        w = reinterpret_cast<const uint32_t*>(src)[g];
+      } else {
+        for (int b = 0; b < 4; ++b)
+          if (4 * g + b < eff) w |= (uint32_t)src[4 * g + b] << (8 * b);
+      }
+    }
+    in.m[k] = w;
+  }
+  in.beg = 4 * W + (uint64_t)ESZ * o0;
+  in.end = 4 * W + (uint64_t)ESZ * (o1 > o0 ? o1 : o0);
+  in.short_read = false;
+  const uint64_t q0 = in.beg >> 4, q1 = (in.end + 15) >> 4;
+#pragma unroll
+  for (int k = 0; k < X::QPT; ++k) {
+    const uint64_t q = q0 + tid + (uint64_t)k * kBlock;
+    u32x4 d = {0u, 0u, 0u, 0u};
+    if (q < q1) {
+      const uint64_t qb = q << 4;
+      if (qb + 16 <= eff) {
+        d = *reinterpret_cast<const u32x4*>(src + qb);
+      } else {
+        for (int b = 0; b < 16; b += ESZ) {
+          if (qb + b + ESZ <= eff) vec_set<ESZ>(d, b / ESZ, load_elem<ESZ>(src + qb + b));
+          else if (qb + b >= in.beg && qb + b < in.end) in.short_read = true;
+        }
+      }
+    }
+    in.q[k] = d;
+  }
+}
+
+template <int ESZ, int V>
+struct ZvcExpandLds {
+  using S = ZvcShape<ESZ, V>;
+  uint32_t tot[S::SEG];
+  uint32_t mask[S::WPT];
+  __attribute__((aligned(16))) uint8_t stage[S::STAGE];
+};
+
+template <int ESZ, int V>
+__device__ __forceinline__ uint32_t zvc_expand_tile(ZvcExpandLds<ESZ, V>& L, const ZvcTileIn<ESZ, V>& in, uint32_t t,
+                                                    uint64_t n, uint8_t* __restrict__ dst, int tid, int wave,
+                                                    int lane) {
+  using S = ZvcShape<ESZ, V>;
+  using X = ZvcExpandShape<ESZ, V>;
+  const uint64_t W = (n + 31) / 32;
+  const uint64_t q0 = in.beg >> 4, q1 = (in.end + 15) >> 4;
+#pragma unroll
+  for (int k = 0; k < X::MPT; ++k) {
+    const int i = tid + k * kBlock;
+    if (i < S::WPT) {
+      uint32_t w = in.m[k];
+      const uint64_t g = (uint64_t)t * S::WPT + i;
+      if (g == W - 1 && (n & 31)) w &= (1u << (n & 31)) - 1;
+      L.mask[i] = w;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < X::QPT; ++k) {
+    const uint64_t q = q0 + tid + (uint64_t)k * kBlock;
+    if (q < q1 && 16 * (q - q0) + 16 <= (uint64_t)S::STAGE) *reinterpret_cast<u32x4*>(L.stage + 16 * (q - q0)) = in.q[k];
+  }
+  __syncthreads();
+  uint32_t bits[V], ex[V];
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    const uint32_t c = (uint32_t)((wave * V + j) * 64 + lane);
+    bits[j] = (L.mask[c / S::LPW] >> ((c % S::LPW) * S::EPL)) & ((1u << S::EPL) - 1);
+    const uint32_t cnt = (uint32_t)__builtin_popcount(bits[j]);
+    const uint32_t inc = wave_incl_scan(cnt);
+    ex[j] = inc - cnt;
+    if (lane == 63) L.tot[wave * V + j] = inc;
+  }
+  __syncthreads();
+  uint32_t base[V];
+  const uint32_t total = segment_bases<V>(L.tot, wave, base);
+  // values the offsets give this tile (never more than a tile holds)
+  const uint64_t span = (in.end - in.beg) / ESZ;
+  const uint32_t avail = span < (uint64_t)S::TE ? (uint32_t)span : (uint32_t)S::TE;
+  const uint32_t shift = (uint32_t)(in.beg & 15);
+  const uint64_t e_tile = (uint64_t)t * S::TE;
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    const uint32_t c = (uint32_t)((wave * V + j) * 64 + lane);
+    uint32_t r = base[j] + ex[j];
+    u32x4 o = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int k = 0; k < S::EPL; ++k) {
+      if ((bits[j] >> k) & 1u) {
+        if (r < avail) vec_set<ESZ>(o, k, load_elem<ESZ>(L.stage + shift + ESZ * r));
+        ++r;
+      }
+    }
+    store_vec<ESZ>(dst, e_tile + (uint64_t)c * S::EPL, n, o);
+  }
+  __syncthreads();
+  return total;
+}
+
+template <int ESZ, int V>
+__global__ __launch_bounds__(kBlock) void zvc_expand_kernel(
+    const uint8_t* __restrict__ src, uint64_t src_capacity, const uint64_t* __restrict__ src_bytes,
+    uint64_t n, uint8_t* __restrict__ dst, uint32_t* __restrict__ error,
+    const uint32_t* __restrict__ offsets, uint32_t num_tiles) {
+  __shared__ ZvcExpandLds<ESZ, V> L;
+  const int tid = threadIdx.x;
+  const int lane = (int)lane_id();
+  const int wave = tid >> 6;
+  const uint32_t G = gridDim.x;
+  const uint64_t W = (n + 31) / 32;
+  const uint64_t claimed = src_bytes ? *src_bytes : src_capacity;
+  const uint64_t eff = claimed < src_capacity ? claimed : src_capacity;
+  uint32_t err = 0;
+  uint32_t ta = blockIdx.x;
+  if (ta >= num_tiles) return;
+  ZvcTileIn<ESZ, V> A, B;
+  zvc_fetch_tile<ESZ, V>(A, src, eff, W, ta, offsets[ta], offsets[ta + 1], tid);
+  uint32_t tb = ta + G;
+  uint32_t ob0 = 0, ob1 = 0;
+  if (tb < num_tiles) {
+    ob0 = offsets[tb];
+    ob1 = offsets[tb + 1];
+  }
+  for (;;) {
+    // A holds tile ta; fetch tile tb into B; offsets of the tile after tb
+    uint32_t tc = tb + G, oc0 = 0, oc1 = 0;
+    if (tb < num_tiles) zvc_fetch_tile<ESZ, V>(B, src, eff, W, tb, ob0, ob1, tid);
+    if (tc < num_tiles) {
+      oc0 = offsets[tc];
+      oc1 = offsets[tc + 1];
+    }
+    if (A.short_read) err |= CDMA_E_SIZE;
+    zvc_expand_tile<ESZ, V>(L, A, ta, n, dst, tid, wave, lane);
+    if (ta == num_tiles - 1 && tid == 0 && src_bytes && A.end != *src_bytes) err |= CDMA_E_SIZE;
+    if (tb >= num_tiles) break;
+    ta = tb;
+    tb = tc;
+    ob0 = oc0;
+    ob1 = oc1;
+    // same step with the roles of A and B swapped
+    tc = tb + G;
+    if (tb < num_tiles) zvc_fetch_tile<ESZ, V>(A, src, eff, W, tb, ob0, ob1, tid);
+    if (tc < num_tiles) {
+      oc0 = offsets[tc];
+      oc1 = offsets[tc + 1];
+    }
+    if (B.short_read) err |= CDMA_E_SIZE;
+    zvc_expand_tile<ESZ, V>(L, B, ta, n, dst, tid, wave, lane);
+    if (ta == num_tiles - 1 && tid == 0 && src_bytes && B.end != *src_bytes) err |= CDMA_E_SIZE;
+    if (tb >= num_tiles) break;
+    ta = tb;
+    tb = tc;
+    ob0 = oc0;
+    ob1 = oc1;
+  }
+  if (err && error) atomicOr(error, err);
+}
+
+}  // namespace cdma

@@ -1,0 +1,126 @@
+"""The C ABI without a GPU: the library loads, exports every entry point that
+include/cdma.h declares, sizes buffers by the closed forms, and rejects bad
+arguments on the host before touching the device."""
+
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        for m in re.finditer(r"^[A-Za-z_][\w \t\*]*?\b(cdma_\w+)\s*\(", text, flags=re.M):
+            names.add(m.group(1))
+    return sorted(names)
+
+
+@pytest.fixture(scope="module")
+def cdma():
+    from sparse_activation_compression_amd.build import LIB, build_library
+    if not os.path.exists(LIB):
+        build_library()
+    import sparse_activation_compression_amd as m
+    return m
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for required in ("cdma_compress", "cdma_decompress", "cdma_offload_async", "cdma_offload_wait",
+                     "cdma_max_compressed_bytes", "cdma_workspace_bytes"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(cdma):
+    lib = ctypes.CDLL(cdma.library_path())
+    missing = [n for n in _declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+@pytest.mark.parametrize("esz", [2, 4])
+@pytest.mark.parametrize("n", [0, 1, 31, 32, 33, 4096, 1 << 30])
+def test_max_compressed_bytes_closed_forms(cdma, esz, n):
+    assert cdma.cdma_max_compressed_bytes(0, esz, n) == 4 * ((n + 31) // 32) + esz * n
+    E = 4096 // esz
+    wr = (n + E - 1) // E
+    assert cdma.cdma_max_compressed_bytes(1, esz, n) == 8 * (wr + 1) + 2 * (n + 2 * wr) + esz * n
+
+
+def test_sizes_reject_bad_algo_esz_n(cdma):
+    assert cdma.cdma_max_compressed_bytes(2, 4, 10) == 0
+    assert cdma.cdma_max_compressed_bytes(0, 3, 10) == 0
+    assert cdma.cdma_max_compressed_bytes(0, 4, (1 << 31) + 1) == 0
+    assert cdma.cdma_max_compressed_bytes(1, 4, (1 << 30) + 1) == 0
+    assert cdma.cdma_workspace_bytes(0, 8, 10) == 0
+
+
+def test_workspace_grows_with_tiles(cdma):
+    a = cdma.cdma_workspace_bytes(0, 4, 1)
+    b = cdma.cdma_workspace_bytes(0, 4, 1 << 30)
+    assert 256 < a < b and b % 8 == 0
+
+
+# Fake but aligned addresses: every call below must fail validation on the
+# host, so nothing is ever dereferenced or enqueued.
+P = 1 << 20
+
+
+@pytest.mark.parametrize("args,status", [
+    ((2, 4, P, 100, P, 10 ** 6, P, P, 10 ** 6, None), 1),          # bad algo
+    ((0, 3, P, 100, P, 10 ** 6, P, P, 10 ** 6, None), 1),          # bad element size
+    ((0, 4, None, 100, P, 10 ** 6, P, P, 10 ** 6, None), 1),       # NULL source
+    ((0, 4, P + 4, 100, P, 10 ** 6, P, P, 10 ** 6, None), 1),      # misaligned source
+    ((0, 4, P, 100, P + 8, 10 ** 6, P, P, 10 ** 6, None), 1),      # misaligned destination
+    ((0, 4, P, 100, P, 10 ** 6, None, P, 10 ** 6, None), 1),       # NULL size word
+    ((0, 4, P, 100, P, 10 ** 6, P + 4, P, 10 ** 6, None), 1),      # misaligned size word
+    ((0, 4, P, 100, P, 415, P, P, 10 ** 6, None), 2),              # destination one byte short
+    ((0, 4, P, 100, P, 10 ** 6, P, P, 263, None), 2),              # workspace too small
+    ((1, 4, P, (1 << 30) + 1, P, 1 << 40, P, P, 1 << 40, None), 1),  # RLE n limit
+])
+def test_compress_rejects_on_host(cdma, args, status):
+    assert cdma.cdma_compress(*args) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((5, 4, P, 100, None, 10, P, None, P, 10 ** 6, None), 1),
+    ((0, 4, P + 2, 100, None, 10, P, None, P, 10 ** 6, None), 1),
+    ((0, 4, P, 100, P + 4, 10, P, None, P, 10 ** 6, None), 1),     # misaligned size word
+    ((0, 4, P, 100, None, 10, P + 4, None, P, 10 ** 6, None), 1),  # misaligned destination
+    ((0, 4, P, 100, None, 10, P, P + 1, P, 10 ** 6, None), 1),     # misaligned error word
+    ((0, 4, P, 100, None, 10, P, None, P, 8, None), 2),            # workspace too small
+])
+def test_decompress_rejects_on_host(cdma, args, status):
+    assert cdma.cdma_decompress(*args) == status
+
+
+def test_offload_rejects_on_host(cdma):
+    sb = cdma.cdma_offload_scratch_bytes(0, 4, 4096, 2)
+    assert sb > 0
+    ok = dict(algo=0, esz=4, d_src=P, n=10000, chunk_elems=4096, h_dst=P, h_capacity=10 ** 6,
+              d_scratch=P, scratch_bytes=sb, slots=2, compute_stream=16, copy_stream=32)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return cdma.cdma_offload_async(*a.values())
+
+    assert call(chunk_elems=1000)[0] == 1          # not a multiple of 2048
+    assert call(slots=0)[0] == 1
+    assert call(copy_stream=16)[0] == 1            # same stream twice
+    assert call(scratch_bytes=sb - 1)[0] == 2
+    assert call(d_scratch=P + 16)[0] == 1          # scratch must be 256-byte aligned
+    assert call(esz=8)[0] == 1
+    assert call(h_dst=None)[0] == 1
+    assert cdma.cdma_offload_scratch_bytes(0, 4, 0, 2) == 0
+    assert cdma.cdma_offload_scratch_bytes(0, 4, 4096, 0) == 0
+
+
+def test_status_strings(cdma):
+    assert cdma.cdma_status_string(0) == "ok"
+    assert cdma.cdma_status_string(2) == "buffer too small"
+    assert "unknown" in cdma.cdma_status_string(99)
