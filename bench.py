@@ -1,0 +1,358 @@
+"""Benchmark of the activation-compression hot path on one MI355X.
+
+One step = every stage of the path over one resident 4 GiB fp32 activation
+buffer (2^30 elements, zero fraction 0.5, the largest single-GPU workload of
+the sparsity sweep):
+
+  ZVC compress -> ZVC decompress -> RLE compress -> RLE decompress
+  -> compressed offload of the buffer to pinned host memory (ZVC chunks of
+     2^24 elements compressed on one stream while earlier chunks are copied
+     over PCIe on another).
+
+`value` is uncompressed bytes per step over the step time, so it includes
+the PCIe-bound offload; each stage's own rate, the roofline of the dominant
+kernel (zvc_compress) and the raw PCIe copy rate are reported beside it.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--zero-frac S]
+
+`python bench.py --summarize-profile DIR --out FILE` turns rocprofv3 output
+(kernel trace with --stats, or a --pmc counter run) into a short text summary.
+"""
+
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import platform
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+N_ELEMS = 1 << 30
+CHUNK = 1 << 24
+SLOTS = 3
+CPU_SAMPLE = 1 << 28
+KERNEL_SOURCES = ("sparse_activation_compression_amd/csrc/zvc_kernels.hpp",
+                  "sparse_activation_compression_amd/csrc/device_common.hpp")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "zvc_compress_kernel_sweep4GiB_s0.5_traffic.md")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic():
+    """HBM bytes per zvc_compress launch from the committed counter summary,
+    or None if it is missing or was taken on a different kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if line.startswith("- ") and ":" in line:
+                k, v = line[2:].split(":", 1)
+                vals[k.strip()] = v.strip().strip("`")
+    if vals.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ----------------------------------------------------------------------------
+# rocprofv3 summaries
+# ----------------------------------------------------------------------------
+
+def _read_csv(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_profile(d: str, out: str, command: str, calib_bytes: float | None) -> None:
+    lines = [f"# rocprofv3 summary: {os.path.basename(out)}", "", f"Command: `{command}`", ""]
+    stats = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
+    counters = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if stats:
+        rows = _read_csv(stats[0])
+        lines += ["| kernel | calls | average (us) | min (us) | max (us) | share |", "|---|---|---|---|---|---|"]
+        for r in rows:
+            name = r.get("Name", "?")
+            short = name.split("(")[0][:90]
+            lines.append(f"| `{short}` | {r.get('Calls')} | {float(r.get('AverageNs', 0)) / 1e3:.1f} | "
+                         f"{float(r.get('MinNs', 0)) / 1e3:.1f} | {float(r.get('MaxNs', 0)) / 1e3:.1f} | "
+                         f"{float(r.get('Percentage', 0)):.1f}% |")
+    if counters:
+        rows = _read_csv(counters[0])
+        per = {}
+        for r in rows:
+            name = r.get("Kernel_Name", "?").split("(")[0]
+            cname = r.get("Counter_Name", "?")
+            per.setdefault((name, cname), []).append(float(r.get("Counter_Value", 0)))
+        lines += ["| kernel | counter | dispatches | mean per dispatch (KiB) |", "|---|---|---|---|"]
+        for (name, cname), v in sorted(per.items()):
+            lines.append(f"| `{name[:90]}` | {cname} | {len(v)} | {statistics.mean(v):.1f} |")
+        if calib_bytes:
+            lines += ["", f"Calibration copy bytes: {calib_bytes:.0f}"]
+    lines.append("")
+    with open(out, "w") as f:
+        f.write("\n".join(lines))
+    print(out)
+
+
+# ----------------------------------------------------------------------------
+# CPU baseline: the oracle on a bounded sample of the same buffer
+# ----------------------------------------------------------------------------
+
+def zsize_chunks(x, cdma) -> int:
+    """Expected host bytes of the ZVC offload: the chunk streams' closed-form sizes."""
+    import torch
+    total = 0
+    for lo in range(0, x.numel(), CHUNK):
+        part = x[lo: lo + CHUNK]
+        total += 4 * ((part.numel() + 31) // 32) + 4 * int(torch.count_nonzero(part).item())
+    return total
+
+
+def cpu_baseline(x_dev, sample: int):
+    import numpy as np
+    import oracle
+
+    bits = x_dev[:sample].cpu().numpy().view(np.uint32)
+    t0 = time.perf_counter()
+    z = oracle.zvc_compress(bits)
+    oracle.zvc_decompress(z, bits.size, 4)
+    r = oracle.rle_compress(bits)
+    oracle.rle_decompress(r, bits.size, 4)
+    dt = time.perf_counter() - t0
+    return {
+        "value": round(4 * sample / dt / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"first {sample} elements ({4 * sample / 2**20:.0f} MiB) of the same buffer; "
+                   "ZVC compress+decompress and RLE compress+decompress (the offload stage is a "
+                   "PCIe copy and has no CPU counterpart); single-threaded C oracle, gcc -O2"),
+        "seconds": round(dt, 2),
+        "host_cpu": platform.processor() or platform.machine(),
+        "host_cpus_visible": os.cpu_count(),
+    }
+
+
+# ----------------------------------------------------------------------------
+# the benchmark
+# ----------------------------------------------------------------------------
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--zero-frac", type=float, default=0.5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--rows-only", action="store_true",
+                    help="time the four codec kernels only (no offload stage); for counter runs")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain device copy of known size (counter calibration)")
+    ap.add_argument("--summarize-profile", metavar="DIR")
+    ap.add_argument("--out")
+    ap.add_argument("--command", default="")
+    ap.add_argument("--calib-bytes", type=float)
+    args = ap.parse_args()
+
+    if args.summarize_profile:
+        summarize_profile(args.summarize_profile, args.out, args.command, args.calib_bytes)
+        return 0
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by independent chunks; see DESIGN.md)", file=sys.stderr)
+        return 2
+
+    import torch
+    from sparse_activation_compression_amd.build import LIB
+    if not os.path.exists(LIB):
+        import __graft_entry__
+        __graft_entry__.build()
+    import sparse_activation_compression_amd as cdma
+    from synth import SWEEP_SEEDS, SWEEP_ZERO_FRACTIONS, sweep_bits_device
+
+    dev = torch.device("cuda:0")
+    s = args.zero_frac
+    seed = dict(zip(SWEEP_ZERO_FRACTIONS, SWEEP_SEEDS)).get(s, 52)
+    n = N_ELEMS
+    x = sweep_bits_device(n, s, seed, device=dev)
+    torch.cuda.synchronize()
+    nnz = int(torch.count_nonzero(x).item())
+    W = (n + 31) // 32
+    stream = torch.cuda.current_stream()
+
+    # buffers (all allocated once, outside the timed region)
+    zcap = cdma.cdma_max_compressed_bytes(0, 4, n)
+    rcap = cdma.cdma_max_compressed_bytes(1, 4, n)
+    zdst = torch.empty(zcap, dtype=torch.uint8, device=dev)
+    rdst = torch.empty(rcap, dtype=torch.uint8, device=dev)
+    zsz = torch.zeros(1, dtype=torch.int64, device=dev)
+    rsz = torch.zeros(1, dtype=torch.int64, device=dev)
+    ws = torch.empty(max(cdma.cdma_workspace_bytes(0, 4, n), cdma.cdma_workspace_bytes(1, 4, n)),
+                     dtype=torch.uint8, device=dev)
+    zout = torch.empty_like(x)
+    rout = torch.empty_like(x)
+    zerr = torch.zeros(1, dtype=torch.int32, device=dev)
+    rerr = torch.zeros(1, dtype=torch.int32, device=dev)
+    host = torch.empty(zcap, dtype=torch.uint8, pin_memory=True)
+    scratch = torch.empty(cdma.cdma_offload_scratch_bytes(0, 4, CHUNK, SLOTS), dtype=torch.uint8, device=dev)
+    cstream = torch.cuda.Stream(device=dev)
+    pstream = torch.cuda.Stream(device=dev)
+
+    names = ("zvc_compress", "zvc_decompress", "rle_compress", "rle_decompress")
+    ev_times = {k: [] for k in names}
+    off_times, off_totals = [], []
+
+    def step(record: bool):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+        evs[0].record(stream)
+        cdma.compress(x, "zvc", dst=zdst, out_bytes=zsz, ws=ws)
+        evs[1].record(stream)
+        cdma.decompress(zdst, n, 4, "zvc", src_bytes=zsz, out=zout, error=zerr, ws=ws)
+        evs[2].record(stream)
+        cdma.compress(x, "rle", dst=rdst, out_bytes=rsz, ws=ws)
+        evs[3].record(stream)
+        cdma.decompress(rdst, n, 4, "rle", src_bytes=rsz, out=rout, error=rerr, ws=ws)
+        evs[4].record(stream)
+        if args.rows_only:
+            if record:
+                evs[4].synchronize()
+                for k, name in enumerate(names):
+                    ev_times[name].append(evs[k].elapsed_time(evs[k + 1]) * 1e3)
+            return
+        t0 = time.perf_counter()
+        job = cdma.offload(x, host, CHUNK, "zvc", SLOTS, scratch=scratch, compute_stream=cstream,
+                           copy_stream=pstream)
+        rc, total, sizes = job.wait()
+        t1 = time.perf_counter()
+        if rc != 0:
+            raise RuntimeError(f"offload failed: {rc}")
+        if record:
+            evs[4].synchronize()
+            for k, name in enumerate(names):
+                ev_times[name].append(evs[k].elapsed_time(evs[k + 1]) * 1e3)
+            off_times.append((t1 - t0) * 1e6)
+            off_totals.append(total)
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    t_total = time.perf_counter() - t0
+
+    if args.calibrate_copy:  # a plain copy of known size, for the counter scale factor
+        a = torch.empty(1 << 28, dtype=torch.int32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    # correctness of what was timed (outside the timed region)
+    zsize, rsize = int(zsz.item()), int(rsz.item())
+    ok = (zsize == 4 * W + 4 * nnz and int(zerr.item()) == 0 and int(rerr.item()) == 0
+          and torch.equal(zout, x) and torch.equal(rout, x) and all(t == off_totals[0] for t in off_totals)
+          and (args.rows_only or off_totals[0] == zsize_chunks(x, cdma)))
+
+    # raw PCIe device-to-host copy of the dense buffer, for comparison
+    raw = []
+    for _ in range(3):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        host[: 4 * n].copy_(x.view(torch.uint8), non_blocking=True)
+        torch.cuda.synchronize()
+        raw.append(time.perf_counter() - t0)
+    raw_gbs = 4 * n / min(raw) / 1e9
+
+    in_bytes = 4 * n
+    zvc_alg = in_bytes + 4 * W + 4 * nnz
+    med = {k: statistics.median(v) for k, v in ev_times.items()}
+    rows = {}
+    for k, alg in (("zvc_compress", zvc_alg), ("zvc_decompress", zvc_alg), ("rle_compress", in_bytes + rsize),
+                   ("rle_decompress", in_bytes + rsize)):
+        us = med[k]
+        rows[k] = {"us": round(us, 1), "gbs_uncompressed": round(in_bytes / us / 1e3, 1),
+                   "gbs_algorithmic": round(alg / us / 1e3, 1), "hbm_frac": round(alg / us / 1e3 / PEAK_HBM_GBS, 4)}
+    if args.rows_only:
+        off_times.append(float("nan"))
+        off_totals.append(0)
+    off_us = statistics.median(off_times)
+    rows["offload"] = {"us": round(off_us, 1), "gbs_uncompressed": round(in_bytes / off_us / 1e3, 2),
+                       "raw_pcie_d2h_gbs": round(raw_gbs, 2), "host_bytes": off_totals[0],
+                       "speedup_vs_raw_copy": round((in_bytes / raw_gbs / 1e3) / off_us, 3)}
+
+    ms_per_step = t_total / args.steps * 1e3
+    comp_us = med["zvc_compress"]
+    result = {
+        "metric": "ZVC compress/decompress GB/s (uncompressed) and % HBM peak; compression ratio",
+        "value": round(in_bytes / (ms_per_step / 1e3) / 1e9, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"sweep_fp32_4GiB_s{s}",
+            "elements": n,
+            "element": "fp32 bit patterns",
+            "zero_fraction": s,
+            "generator": "counter-based hash, seed %d, forced all-zero/all-dense windows" % seed,
+            "step": ["zvc_compress", "zvc_decompress", "rle_compress", "rle_decompress",
+                     f"zvc_offload(chunk={CHUNK},slots={SLOTS})"],
+            "parallelism": "single GPU",
+        },
+        "compression_ratio": {"zvc": round(in_bytes / zsize, 4), "rle": round(in_bytes / rsize, 4)},
+        "rows": rows,
+        "roofline": {
+            "kernel": "zvc_compress (workspace clear + zvc_compress_kernel)",
+            "bound": "hbm",
+            "achieved": round(zvc_alg / comp_us / 1e3, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(zvc_alg / comp_us / 1e3 / PEAK_HBM_GBS, 4),
+            "traffic": stored_traffic(),
+            "algorithmic_bytes_per_launch": zvc_alg,
+            "avg_launch_us": round(statistics.mean(ev_times["zvc_compress"]), 1),
+        },
+        "ok": bool(ok),
+    }
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(x, CPU_SAMPLE)
+        rows_gpu_us = sum(med[k] for k in names)
+        result["cpu_baseline"]["gpu_same_rows_gbs"] = round(in_bytes / rows_gpu_us / 1e3, 1)
+    print(json.dumps(result), flush=True)
+    # release device and pinned memory before the interpreter exits
+    del x, zdst, rdst, zsz, rsz, ws, zout, rout, zerr, rerr, host, scratch
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return 0 if ok else 1
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -79,17 +79,13 @@ static hipError_t zvc_compress_t(const void* src, uint64_t n, void* dst, uint64_
   const uint64_t tiles = zvc_compress_tiles(ESZ, n);
   hipError_t e = clear_workspace(ws, tiles, s);
   if (e != hipSuccess) return e;
-  // co-resident persistent grid: launched cooperatively so every workgroup
-  // is running at once (the static tile order relies on it)
+  // persistent grid: about one workgroup per CU, tiles handed out by ticket
   auto kern = zvc_compress_kernel<ESZ>;
   const uint64_t res = resident_groups(reinterpret_cast<const void*>(kern), kCBlock);
   const unsigned grid = (unsigned)(tiles < res ? tiles : res);
-  const uint8_t* a_src = static_cast<const uint8_t*>(src);
-  uint8_t* a_dst = static_cast<uint8_t*>(dst);
-  uint64_t* a_status = ws_status(ws);
-  uint32_t a_tiles = (uint32_t)tiles;
-  void* args[] = {&a_src, &n, &a_dst, &out_bytes, &a_status, &a_tiles};
-  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kern), dim3(grid), dim3(kCBlock), args, 0, s);
+  kern<<<grid, kCBlock, 0, s>>>(static_cast<const uint8_t*>(src), n, static_cast<uint8_t*>(dst), out_bytes,
+                                ws_counter(ws), ws_status(ws), (uint32_t)tiles);
+  return hipGetLastError();
 }
 
 // per-tile value offsets live after the status words of the super tiles

@@ -118,30 +118,33 @@ __device__ __forceinline__ uint32_t segment_bases(const uint32_t* s_tot, int wav
 }
 
 // ---------------------------------------------------------------------------
-// compress: one 1024-thread workgroup per CU, 64 KB tiles, lag-1 pipeline
+// compress: 1024-thread workgroups, 64 KB tiles, lag-1 pipeline
 // ---------------------------------------------------------------------------
 //
-// The grid is launched cooperatively with G workgroups, all resident at once;
-// workgroup w handles tiles w, w+G, w+2G, ... in order.  Iteration i of a
-// workgroup:
-//   1. wave 0 issues the first lookback round for the previous tile p = t-G,
-//      whose aggregate (and that of every tile of its band) was published one
-//      iteration earlier;
-//   2. all waves classify tile t (prefetched into registers): window masks go
-//      straight to their fixed place in the stream, the nonzeros are compacted
-//      into LDS buffer i%2, and t's aggregate is published;
-//   3. the next tile t+G is prefetched;
-//   4. wave 0 resolves p's lookback (its reads have returned meanwhile) and
-//      publishes p's inclusive prefix;
-//   5. all waves store p's values from LDS buffer (i-1)%2, realigned to their
-//      byte position in the stream.
-// Vector-memory counters retire in order, so the lookback reads of step 1 are
-// consumed in step 4 without waiting for the prefetch of step 3.
-// Progress: the smallest unclassified tile's workgroup has classified every
-// tile before it in its own order, and a lookback only waits for unclassified
-// predecessors; with all workgroups resident it always advances.
+// A persistent grid of (about) one workgroup per CU takes tiles from a ticket
+// counter.  Iteration i of a workgroup, holding tickets a (classified in
+// iteration i-1, values in LDS buffer (i-1)%2) and b (loads in flight):
+//   1. the last wave draws the next ticket c;
+//   2. all waves classify tile b: window masks go straight to their fixed
+//      place in the stream, b's aggregate (nonzero count) is published and its
+//      nonzeros are compacted into LDS buffer i%2;
+//   3. wave 0 issues the first lookback round for tile a and tile c's loads
+//      are issued (c's classification is the next iteration);
+//   4. wave 0 resolves a's lookback (its reads have returned meanwhile) and
+//      publishes a's inclusive prefix;
+//   5. all waves store a's values, realigned to their byte position.
+// Vector-memory counters retire in order, so the lookback reads of step 3
+// are consumed in step 4 without waiting for c's loads issued after them.
+// Progress: a ticket is drawn only by a running workgroup, which classifies
+// it in its next iteration; a lookback reads tiles classified at least one
+// iteration earlier.  The holder of the smallest unclassified ticket is busy
+// with older tiles only, whose predecessors are all classified, so it always
+// reaches that ticket: no co-residency is assumed and every lookback ends.
 
-constexpr int kCBlock = 1024;
+#ifndef CDMA_CBLOCK
+#define CDMA_CBLOCK 1024
+#endif
+constexpr int kCBlock = CDMA_CBLOCK;
 constexpr int kCWaves = kCBlock / 64;
 
 template <int ESZ>
@@ -153,7 +156,7 @@ struct ZvcCShape {
   static constexpr int WPT = TE / 32;              // windows per tile
   static constexpr int SEG = kCWaves * V;          // wave segments per tile
   static constexpr int STAGE = TE * ESZ + 16;
-  static_assert(SEG == 64, "one lane per wave segment in the tile scan");
+  static_assert(SEG <= 64, "one lane per wave segment in the tile scan");
   static_assert(WPT <= kCBlock, "one mask store per thread");
 };
 
@@ -162,6 +165,7 @@ struct ZvcCLds {
   using S = ZvcCShape<ESZ>;
   uint64_t excl;         // exclusive prefix of the tile being stored
   uint32_t total[2];     // nonzeros held in stage[b]
+  uint32_t next;         // next ticket of this workgroup
   bool stuck;
   uint32_t tot[S::SEG];
   uint32_t mask[S::WPT];
@@ -225,20 +229,27 @@ __device__ __forceinline__ void zvc_c_store_values(const uint8_t* __restrict__ s
 }
 
 // One pipeline iteration: classify tile t from `cur` (if t < num_tiles),
-// prefetch t+G into `nxt`, resolve and store the previous tile t-G (if
-// have_prev).  Returns with the workgroup synchronised.
+// draw the next ticket and prefetch it into `nxt`, resolve and store the
+// previous tile tp (if tp < num_tiles) with the lookback round `lr` issued at
+// the end of the previous iteration, then issue t's first lookback round into
+// `lr`.  Returns the next ticket, with the workgroup synchronised.
 template <int ESZ>
-__device__ __forceinline__ void zvc_c_iteration(ZvcCLds<ESZ>& L, u32x4 (&cur)[ZvcCShape<ESZ>::V],
-                                                u32x4 (&nxt)[ZvcCShape<ESZ>::V], uint32_t t, bool have_prev,
-                                                int buf, uint32_t G, uint32_t full, uint64_t W,
-                                                const uint8_t* __restrict__ src, uint64_t n,
-                                                uint8_t* __restrict__ dst, uint64_t* __restrict__ out_bytes,
-                                                uint64_t* __restrict__ status, uint32_t num_tiles, int tid,
-                                                int wave, int lane) {
+__device__ __forceinline__ uint32_t zvc_c_iteration(ZvcCLds<ESZ>& L, u32x4 (&cur)[ZvcCShape<ESZ>::V],
+                                                    u32x4 (&nxt)[ZvcCShape<ESZ>::V], LookbackRound& lr,
+                                                    uint32_t t, uint32_t tp, int buf, uint32_t full, uint64_t W,
+                                                    const uint8_t* __restrict__ src, uint64_t n,
+                                                    uint8_t* __restrict__ dst, uint64_t* __restrict__ out_bytes,
+                                                    uint64_t* __restrict__ status, uint32_t* __restrict__ counter,
+                                                    uint32_t num_tiles, int tid, int wave, int lane) {
   using S = ZvcCShape<ESZ>;
   constexpr int V = S::V;
   const bool have_cur = t < num_tiles;
-  const uint32_t tp = t - G;  // tile to store (valid when have_prev)
+  const bool have_prev = tp < num_tiles;
+
+  // next ticket: drawn early, published to the workgroup at the barrier
+  uint32_t ticket = 0;
+  if (have_cur && tid == kCBlock - 64)
+    ticket = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   uint32_t bits[V], ex[V];
   if (have_cur) {
@@ -258,17 +269,13 @@ __device__ __forceinline__ void zvc_c_iteration(ZvcCLds<ESZ>& L, u32x4 (&cur)[Zv
       if (lane == 63) L.tot[wave * V + j] = inc;
     }
   }
+  if (tid == kCBlock - 64) L.next = have_cur ? ticket : num_tiles;
   __syncthreads();
-
-  // The previous tile's lookback reads go out now; its aggregate and those of
-  // its band were published an iteration ago.  They return while this tile's
-  // values are compacted and the next tile's loads are issued.
-  LookbackRound r;
-  if (wave == 0 && have_prev && tp > 0) lookback_issue(status, (int64_t)tp - 1, r);
+  const uint32_t tn = L.next;
 
   if (have_cur) {
-    // segment bases: lane l of every wave scans the 64 segment totals
-    const uint32_t x = L.tot[lane];
+    // segment bases: lane l of every wave scans the segment totals
+    const uint32_t x = lane < S::SEG ? L.tot[lane] : 0u;
     const uint32_t inc = wave_incl_scan(x);
     const uint32_t T = read_lane(inc, 63);
     if (tid == 0) {
@@ -291,11 +298,11 @@ __device__ __forceinline__ void zvc_c_iteration(ZvcCLds<ESZ>& L, u32x4 (&cur)[Zv
         }
       }
     }
-    if (t + G < full) zvc_c_load_full<ESZ>(nxt, src, t + G, wave, lane);
+    if (tn < full) zvc_c_load_full<ESZ>(nxt, src, tn, wave, lane);
   }
   if (wave == 0 && have_prev) {
     bool stuck = false;
-    const uint64_t X = tp > 0 ? lookback_resolve(status, tp, r, &stuck) : 0;
+    const uint64_t X = tp > 0 ? lookback_resolve(status, tp, lr, &stuck) : 0;
     if (lane == 0) {
       L.excl = X;
       L.stuck = stuck;
@@ -312,37 +319,46 @@ __device__ __forceinline__ void zvc_c_iteration(ZvcCLds<ESZ>& L, u32x4 (&cur)[Zv
     // tile, so if any lookback could not finish, neither could this one.
     if (tp == num_tiles - 1 && tid == 0) *out_bytes = L.stuck ? kSizeInternalError : A + (uint64_t)ESZ * T;
   }
+  // t's first lookback round goes out now: t's aggregate and those of the
+  // tiles drawn before it were published during this iteration, and the
+  // reads have the whole of the next classify phase to return.
+  if (wave == 0 && have_cur && t > 0) lookback_issue(status, (int64_t)t - 1, lr);
   __syncthreads();
+  return tn;
 }
 
 template <int ESZ>
 __global__ __launch_bounds__(kCBlock) void zvc_compress_kernel(
     const uint8_t* __restrict__ src, uint64_t n, uint8_t* __restrict__ dst,
-    uint64_t* __restrict__ out_bytes, uint64_t* __restrict__ status, uint32_t num_tiles) {
+    uint64_t* __restrict__ out_bytes, uint32_t* __restrict__ counter, uint64_t* __restrict__ status,
+    uint32_t num_tiles) {
   using S = ZvcCShape<ESZ>;
   __shared__ ZvcCLds<ESZ> L;
   const int tid = threadIdx.x;
   const int lane = (int)lane_id();
   const int wave = tid >> 6;
-  const uint32_t G = gridDim.x;
   const uint64_t W = (n + 31) / 32;
   const uint32_t full = (uint32_t)(n / S::TE);  // tiles with no element past n
-  uint32_t t = blockIdx.x;                      // < num_tiles: the grid never exceeds the tiles
+  if (tid == 0) L.next = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  uint32_t t = L.next;        // tile to classify
+  uint32_t tp = num_tiles;    // tile to store (none yet)
   u32x4 ra[S::V], rb[S::V];
+  LookbackRound lr;
   if (t < full) zvc_c_load_full<ESZ>(ra, src, t, wave, lane);
   // two iterations per trip so the register sets swap roles without copies;
-  // the iteration with no tile left to classify only stores the last one
-  bool have_prev = false;
+  // an iteration with no tile left to classify only stores the last one
   for (;;) {
-    zvc_c_iteration<ESZ>(L, ra, rb, t, have_prev, 0, G, full, W, src, n, dst, out_bytes, status, num_tiles,
-                         tid, wave, lane);
+    uint32_t tn = zvc_c_iteration<ESZ>(L, ra, rb, lr, t, tp, 0, full, W, src, n, dst, out_bytes, status, counter,
+                                       num_tiles, tid, wave, lane);
     if (t >= num_tiles) break;
-    t += G;
-    have_prev = true;
-    zvc_c_iteration<ESZ>(L, rb, ra, t, have_prev, 1, G, full, W, src, n, dst, out_bytes, status, num_tiles,
-                         tid, wave, lane);
+    tp = t;
+    t = tn;
+    tn = zvc_c_iteration<ESZ>(L, rb, ra, lr, t, tp, 1, full, W, src, n, dst, out_bytes, status, counter,
+                              num_tiles, tid, wave, lane);
     if (t >= num_tiles) break;
-    t += G;
+    tp = t;
+    t = tn;
   }
 }
 
