@@ -113,6 +113,47 @@ def summarize_profile(d: str, out: str, command: str, calib_bytes: float | None)
     print(out)
 
 
+def summarize_traffic(fetch_dir: str, write_dir: str, out: str, command: str, calib_bytes: float) -> None:
+    """HBM bytes per dispatch from a FETCH_SIZE run and a WRITE_SIZE run of
+    the same program, each scaled by what the counter reads for the plain
+    device copy of calib_bytes that the program ran (--calibrate-copy)."""
+    def load(d, counter):
+        f = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)[0]
+        by_id = {}
+        for r in _read_csv(f):
+            if r.get("Counter_Name") == counter:
+                by_id[int(r["Dispatch_Id"])] = (r["Kernel_Name"].split("(")[0], float(r["Counter_Value"]))
+        return by_id
+
+    fetch, write = load(fetch_dir, "FETCH_SIZE"), load(write_dir, "WRITE_SIZE")
+    calib_kib = calib_bytes / 1024
+    ids = [i for i, (k, v) in write.items() if "copy" in k.lower() and abs(v - calib_kib) < 1e-6 * calib_kib]
+    f_scale = calib_kib / statistics.mean(fetch[i][1] for i in ids)
+    w_scale = calib_kib / statistics.mean(write[i][1] for i in ids)
+    lines = [f"# HBM traffic per dispatch (rocprofv3 FETCH_SIZE / WRITE_SIZE): {os.path.basename(out)}", "",
+             f"Command: `{command}`", "",
+             f"Calibration: a plain device-to-device copy of {calib_bytes:.0f} bytes reads back as "
+             f"FETCH_SIZE {calib_kib / f_scale:.1f} KiB and WRITE_SIZE {calib_kib / w_scale:.1f} KiB, "
+             f"so FETCH_SIZE is scaled by {f_scale:.4f} and WRITE_SIZE by {w_scale:.4f} "
+             f"(dispatches {ids}).", "",
+             "| kernel | fetched (GB, scaled) | written (GB, scaled) | total (GB) |", "|---|---|---|---|"]
+    per = {}
+    for i, (k, v) in fetch.items():
+        if i in write and "cdma" in k:
+            per.setdefault(k, []).append((v * f_scale * 1024, write[i][1] * w_scale * 1024))
+    for k, v in sorted(per.items()):
+        fb, wb = statistics.mean(a for a, _ in v), statistics.mean(b for _, b in v)
+        lines.append(f"| `{k}` | {fb / 1e9:.4f} | {wb / 1e9:.4f} | {(fb + wb) / 1e9:.4f} |")
+    comp = [a + b for k, v in per.items() if "zvc_compress_kernel<4>" in k for a, b in v]
+    lines += ["", "Machine-readable (read by bench.py; valid only for the kernel source hashed here):", "",
+              f"- kernel: `zvc_compress_kernel<4>`",
+              f"- hbm_bytes_per_launch: `{statistics.mean(comp):.0f}`",
+              f"- kernel_source_sha256: `{kernel_source_hash()}`", ""]
+    with open(out, "w") as f:
+        f.write("\n".join(lines))
+    print(out)
+
+
 # ----------------------------------------------------------------------------
 # CPU baseline: the oracle on a bounded sample of the same buffer
 # ----------------------------------------------------------------------------
@@ -168,11 +209,15 @@ def main() -> int:
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain device copy of known size (counter calibration)")
     ap.add_argument("--summarize-profile", metavar="DIR")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--out")
     ap.add_argument("--command", default="")
     ap.add_argument("--calib-bytes", type=float)
     args = ap.parse_args()
 
+    if args.summarize_traffic:
+        summarize_traffic(*args.summarize_traffic, args.out, args.command, args.calib_bytes or float(1 << 30))
+        return 0
     if args.summarize_profile:
         summarize_profile(args.summarize_profile, args.out, args.command, args.calib_bytes)
         return 0
