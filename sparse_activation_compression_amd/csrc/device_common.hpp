@@ -23,6 +23,28 @@ constexpr int kWaves = kBlock / 64;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// Streaming accesses.  The activation map is read once and the stream
+// written once, so the bulk loads and stores carry the non-temporal hint:
+// on gfx950 it lifts a pure streaming read from about 6.3 to 7.1 TB/s.
+#ifndef CDMA_NT_LOAD
+#define CDMA_NT_LOAD 1
+#endif
+#ifndef CDMA_NT_STORE
+#define CDMA_NT_STORE 1
+#endif
+
+template <typename T>
+__device__ __forceinline__ T ld_stream(const T* p) {
+  if constexpr (CDMA_NT_LOAD) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+
+template <typename T>
+__device__ __forceinline__ void st_stream(T* p, T v) {
+  if constexpr (CDMA_NT_STORE) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
+
 // ---- lane helpers ----------------------------------------------------------
 
 __device__ __forceinline__ uint32_t lane_id() {

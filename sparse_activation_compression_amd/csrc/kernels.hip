@@ -88,29 +88,26 @@ static hipError_t zvc_compress_t(const void* src, uint64_t n, void* dst, uint64_
   return hipGetLastError();
 }
 
-// per-tile value offsets live after the status words of the super tiles
-static uint32_t* ws_offsets(void* ws, uint64_t tiles) {
-  return reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + kWsHeader + 8 * tiles);
-}
-
+// decompress workspace: local[tiles] then sup[supers + 1]
 template <int ESZ>
 static hipError_t zvc_decompress_t(const void* src, uint64_t cap, const uint64_t* src_bytes, uint64_t n,
                                    void* dst, uint32_t* error, void* ws, hipStream_t s) {
   using C = ZvcScanShape<ESZ, kZvcV>;
   const uint64_t tiles = zvc_tiles(ESZ, n);
   const uint64_t supers = (tiles + C::SUPER - 1) / C::SUPER;
-  hipError_t e = clear_workspace(ws, supers, s);
-  if (e != hipSuccess) return e;
-  uint32_t* offsets = ws_offsets(ws, tiles);
-  zvc_offsets_kernel<ESZ, kZvcV><<<(unsigned)supers, kBlock, 0, s>>>(
-      static_cast<const uint8_t*>(src), cap, src_bytes, n, offsets, error, ws_counter(ws), ws_status(ws),
-      (uint32_t)tiles, (uint32_t)supers);
+  uint32_t* local = static_cast<uint32_t*>(ws);
+  uint32_t* sup = local + tiles;
+  hipError_t e;
+  zvc_count_kernel<ESZ, kZvcV><<<(unsigned)supers, kBlock, 0, s>>>(static_cast<const uint8_t*>(src), cap, src_bytes,
+                                                                  n, local, sup, error, (uint32_t)tiles);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  zvc_scan_kernel<<<1, kScanBlock, 0, s>>>(sup, (uint32_t)supers);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   auto kern = zvc_expand_kernel<ESZ, kZvcV>;
   const uint64_t res = resident_groups(reinterpret_cast<const void*>(kern));
   const unsigned grid = (unsigned)(tiles < res ? tiles : res);
   kern<<<grid, kBlock, 0, s>>>(static_cast<const uint8_t*>(src), cap, src_bytes, n, static_cast<uint8_t*>(dst),
-                               error, offsets, (uint32_t)tiles);
+                               error, local, sup, (uint32_t)tiles);
   return hipGetLastError();
 }
 

@@ -219,7 +219,7 @@ __global__ __launch_bounds__(kBlock) void rle_compress_kernel(
     const uint64_t qb = q << 4;
     const uint32_t lo = (uint32_t)(qb - (q0 << 4));
     if (qb >= beg && qb + 16 <= end) {
-      *reinterpret_cast<u32x4*>(dst + qb) = *reinterpret_cast<const u32x4*>(s_stage + lo);
+      st_stream(reinterpret_cast<u32x4*>(dst + qb), *reinterpret_cast<const u32x4*>(s_stage + lo));
     } else {
       for (int k = 0; k < 16; k += 2) {
         const uint64_t b = qb + k;
@@ -308,7 +308,7 @@ __global__ __launch_bounds__(kBlock) void rle_decompress_kernel(
       const uint64_t qb = q << 4;
       const uint32_t lo = (uint32_t)(qb - (q0 << 4));
       if (qb + 16 <= eff) {
-        *reinterpret_cast<u32x4*>(blk + lo) = *reinterpret_cast<const u32x4*>(src + qb);
+        *reinterpret_cast<u32x4*>(blk + lo) = ld_stream(reinterpret_cast<const u32x4*>(src + qb));
       } else {
         for (int k = 0; k < 16; k += 2) {
           const uint64_t b = qb + k;

@@ -83,7 +83,7 @@ __device__ __forceinline__ void store_elem(uint8_t* p, uint32_t e) {
 template <int ESZ>
 __device__ __forceinline__ u32x4 load_vec(const uint8_t* __restrict__ src, uint64_t e0, uint64_t n) {
   constexpr int EPL = 16 / ESZ;
-  if (e0 + EPL <= n) return *reinterpret_cast<const u32x4*>(src + e0 * ESZ);
+  if (e0 + EPL <= n) return ld_stream(reinterpret_cast<const u32x4*>(src + e0 * ESZ));
   u32x4 v = {0u, 0u, 0u, 0u};
   for (int k = 0; k < EPL; ++k)
     if (e0 + k < n) vec_set<ESZ>(v, k, load_elem<ESZ>(src + (e0 + k) * ESZ));
@@ -95,7 +95,7 @@ template <int ESZ>
 __device__ __forceinline__ void store_vec(uint8_t* __restrict__ dst, uint64_t e0, uint64_t n, u32x4 v) {
   constexpr int EPL = 16 / ESZ;
   if (e0 + EPL <= n) {
-    *reinterpret_cast<u32x4*>(dst + e0 * ESZ) = v;
+    st_stream(reinterpret_cast<u32x4*>(dst + e0 * ESZ), v);
     return;
   }
   for (int k = 0; k < EPL; ++k)
@@ -178,7 +178,7 @@ __device__ __forceinline__ void zvc_c_load_full(u32x4 (&v)[ZvcCShape<ESZ>::V], c
   using S = ZvcCShape<ESZ>;
   const uint8_t* p = src + (uint64_t)t * (S::TE * ESZ) + (uint64_t)(wave * S::V * 64 + lane) * 16;
 #pragma unroll
-  for (int j = 0; j < S::V; ++j) v[j] = *reinterpret_cast<const u32x4*>(p + j * 1024);
+  for (int j = 0; j < S::V; ++j) v[j] = ld_stream(reinterpret_cast<const u32x4*>(p + j * 1024));
 }
 
 template <int ESZ>
@@ -218,7 +218,7 @@ __device__ __forceinline__ void zvc_c_store_values(const uint8_t* __restrict__ s
         out = u32x4{__builtin_amdgcn_alignbyte(w1, w0, 2), __builtin_amdgcn_alignbyte(w2, w1, 2),
                     __builtin_amdgcn_alignbyte(w3, w2, 2), __builtin_amdgcn_alignbyte(w4, w3, 2)};
       }
-      *reinterpret_cast<u32x4*>(dst + qb) = out;
+      st_stream(reinterpret_cast<u32x4*>(dst + qb), out);
     } else {
       for (int k = 0; k < 16; k += ESZ) {
         const uint64_t b = qb + k;
@@ -363,14 +363,18 @@ __global__ __launch_bounds__(kCBlock) void zvc_compress_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// decompress, pass 1: value offset of every tile from the masks alone
+// decompress, passes 1 and 2: value offset of every tile from the masks alone
 // ---------------------------------------------------------------------------
 //
-// A super tile is SUPER consecutive ZVC tiles (32 KB of masks).  Each
-// workgroup popcounts its masks, scans the per-tile counts and joins a
-// decoupled lookback over super tiles; it writes offsets[t] = number of
-// nonzeros before tile t (offsets[num_tiles] = total).  Mask bytes at or past
-// the readable size count as 0; mask bits for indices >= n are not counted.
+// Pass 1 (zvc_count_kernel): a super tile is SUPER consecutive ZVC tiles
+// (32 KB of masks).  Each workgroup popcounts its masks and writes, for every
+// tile, the number of nonzeros before it inside the super tile (local[t]),
+// and the super tile's total (sup[u]).  Mask bytes at or past the readable
+// size count as 0; mask bits for indices >= n are not counted but reported.
+// Pass 2 (zvc_scan_kernel): one workgroup turns sup[] into exclusive prefixes
+// in place, with the grand total in sup[num_super].  The value offset of tile
+// t is then sup[t / SUPER] + local[t].  Neither pass waits on another
+// workgroup.
 
 template <int ESZ, int V>
 struct ZvcScanShape {
@@ -383,45 +387,46 @@ struct ZvcScanShape {
 };
 
 template <int ESZ, int V>
-__global__ __launch_bounds__(kBlock) void zvc_offsets_kernel(
+__global__ __launch_bounds__(kBlock) void zvc_count_kernel(
     const uint8_t* __restrict__ src, uint64_t src_capacity, const uint64_t* __restrict__ src_bytes,
-    uint64_t n, uint32_t* __restrict__ offsets, uint32_t* __restrict__ error,
-    uint32_t* __restrict__ counter, uint64_t* __restrict__ status, uint32_t num_tiles,
-    uint32_t num_super) {
+    uint64_t n, uint32_t* __restrict__ local, uint32_t* __restrict__ sup, uint32_t* __restrict__ error,
+    uint32_t num_tiles) {
   using C = ZvcScanShape<ESZ, V>;
-  __shared__ uint32_t s_ticket;
   __shared__ uint32_t s_cnt[C::SUPER];
   const int tid = threadIdx.x;
   const int lane = (int)lane_id();
   const int wave = tid >> 6;
-  if (tid == 0) s_ticket = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint32_t u = blockIdx.x;
   for (int i = tid; i < C::SUPER; i += kBlock) s_cnt[i] = 0;
-  __syncthreads();
-  const uint32_t u = s_ticket;
   const uint64_t W = (n + 31) / 32;
   const uint64_t claimed = src_bytes ? *src_bytes : src_capacity;
   const uint64_t eff = claimed < src_capacity ? claimed : src_capacity;
   const uint64_t g0 = (uint64_t)u * C::WORDS + (uint64_t)tid * C::WPTH;  // first mask word of this thread
-  uint32_t cnt = 0, err = 0;
+  u32x4 m[C::WPTH / 4];
 #pragma unroll
-  for (int k = 0; k < C::WPTH; k += 4) {
-    const uint64_t g = g0 + k;
-    u32x4 m = {0u, 0u, 0u, 0u};
+  for (int k = 0; k < C::WPTH / 4; ++k) {
+    const uint64_t g = g0 + 4 * k;
     if (g + 4 <= W && 4 * (g + 4) <= eff) {
-      m = *reinterpret_cast<const u32x4*>(src + 4 * g);
+      m[k] = ld_stream(reinterpret_cast<const u32x4*>(src + 4 * g));
     } else {
+      m[k] = u32x4{0u, 0u, 0u, 0u};
       for (int i = 0; i < 4; ++i) {
         if (g + i >= W) break;
         uint32_t w = 0;
         for (int b = 0; b < 4; ++b)
           if (4 * (g + i) + b < eff) w |= (uint32_t)src[4 * (g + i) + b] << (8 * b);
-        m[i] = w;
+        m[k][i] = w;
       }
     }
+  }
+  __syncthreads();
+  uint32_t cnt = 0, err = 0;
+#pragma unroll
+  for (int k = 0; k < C::WPTH / 4; ++k) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      uint32_t w = m[i];
-      if (g + i == W - 1 && (n & 31)) {
+      uint32_t w = m[k][i];
+      if (g0 + 4 * k + i == W - 1 && (n & 31)) {
         const uint32_t valid = (1u << (n & 31)) - 1;
         if (w & ~valid) err |= CDMA_E_MASK_PAST_N;
         w &= valid;
@@ -431,19 +436,45 @@ __global__ __launch_bounds__(kBlock) void zvc_offsets_kernel(
   }
   if (cnt) atomicAdd(&s_cnt[tid / C::TPT], cnt);
   __syncthreads();
-  uint32_t c = 0, inc = 0, total = 0;
   if (wave == 0) {
-    c = lane < C::SUPER ? s_cnt[lane] : 0u;
-    inc = wave_incl_scan(c);
-    total = read_lane(inc, 63);
-    bool stuck;
-    const uint64_t x = lookback_exclusive(status, u, total, &stuck);
-    if (stuck) err |= CDMA_E_INTERNAL;
+    const uint32_t c = lane < C::SUPER ? s_cnt[lane] : 0u;
+    const uint32_t inc = wave_incl_scan(c);
     const uint64_t t = (uint64_t)u * C::SUPER + lane;
-    if (lane < C::SUPER && t < num_tiles) offsets[t] = (uint32_t)(x + inc - c);
-    if (u == num_super - 1 && lane == 0) offsets[num_tiles] = (uint32_t)(x + total);
+    if (lane < C::SUPER && t < num_tiles) local[t] = inc - c;
+    if (lane == 63) sup[u] = inc;
   }
   if (err && error) atomicOr(error, err);
+}
+
+// Exclusive prefix sums of sup[0..count) in place, total in sup[count]; one
+// workgroup of kScanBlock threads.
+constexpr int kScanBlock = 1024;
+
+__global__ __launch_bounds__(kScanBlock) void zvc_scan_kernel(uint32_t* __restrict__ sup, uint32_t count) {
+  __shared__ uint32_t s_wave[kScanBlock / 64];
+  __shared__ uint32_t s_carry;
+  const int tid = threadIdx.x;
+  const int lane = (int)lane_id();
+  const int wave = tid >> 6;
+  if (tid == 0) s_carry = 0;
+  __syncthreads();
+  for (uint32_t base = 0; base < count; base += kScanBlock) {
+    const uint32_t i = base + tid;
+    const uint32_t v = i < count ? sup[i] : 0u;
+    const uint32_t inc = wave_incl_scan(v);
+    if (lane == 63) s_wave[wave] = inc;
+    __syncthreads();
+    uint32_t before = s_carry, all = 0;
+    for (int w = 0; w < kScanBlock / 64; ++w) {
+      if (w < wave) before += s_wave[w];
+      all += s_wave[w];
+    }
+    if (i < count) sup[i] = before + inc - v;
+    __syncthreads();
+    if (tid == 0) s_carry += all;
+    __syncthreads();
+  }
+  if (tid == 0) sup[count] = s_carry;
 }
 
 // ---------------------------------------------------------------------------
@@ -502,7 +533,7 @@ __device__ __forceinline__ void zvc_fetch_tile(ZvcTileIn<ESZ, V>& in, const uint
     if (q < q1) {
       const uint64_t qb = q << 4;
       if (qb + 16 <= eff) {
-        d = *reinterpret_cast<const u32x4*>(src + qb);
+        d = ld_stream(reinterpret_cast<const u32x4*>(src + qb));
       } else {
         for (int b = 0; b < 16; b += ESZ) {
           if (qb + b + ESZ <= eff) vec_set<ESZ>(d, b / ESZ, load_elem<ESZ>(src + qb + b));
@@ -582,11 +613,21 @@ __device__ __forceinline__ uint32_t zvc_expand_tile(ZvcExpandLds<ESZ, V>& L, con
   return total;
 }
 
+// Value offset of tile t (t <= num_tiles) from the two count passes.
+template <int ESZ, int V>
+__device__ __forceinline__ uint32_t zvc_tile_offset(const uint32_t* __restrict__ local,
+                                                    const uint32_t* __restrict__ sup, uint32_t t,
+                                                    uint32_t num_tiles) {
+  using C = ZvcScanShape<ESZ, V>;
+  if (t >= num_tiles) return sup[(num_tiles + C::SUPER - 1) / C::SUPER];  // the grand total
+  return sup[t / C::SUPER] + local[t];
+}
+
 template <int ESZ, int V>
 __global__ __launch_bounds__(kBlock) void zvc_expand_kernel(
     const uint8_t* __restrict__ src, uint64_t src_capacity, const uint64_t* __restrict__ src_bytes,
     uint64_t n, uint8_t* __restrict__ dst, uint32_t* __restrict__ error,
-    const uint32_t* __restrict__ offsets, uint32_t num_tiles) {
+    const uint32_t* __restrict__ local, const uint32_t* __restrict__ sup, uint32_t num_tiles) {
   __shared__ ZvcExpandLds<ESZ, V> L;
   const int tid = threadIdx.x;
   const int lane = (int)lane_id();
@@ -599,20 +640,21 @@ __global__ __launch_bounds__(kBlock) void zvc_expand_kernel(
   uint32_t ta = blockIdx.x;
   if (ta >= num_tiles) return;
   ZvcTileIn<ESZ, V> A, B;
-  zvc_fetch_tile<ESZ, V>(A, src, eff, W, ta, offsets[ta], offsets[ta + 1], tid);
+  zvc_fetch_tile<ESZ, V>(A, src, eff, W, ta, zvc_tile_offset<ESZ, V>(local, sup, ta, num_tiles),
+                         zvc_tile_offset<ESZ, V>(local, sup, ta + 1, num_tiles), tid);
   uint32_t tb = ta + G;
   uint32_t ob0 = 0, ob1 = 0;
   if (tb < num_tiles) {
-    ob0 = offsets[tb];
-    ob1 = offsets[tb + 1];
+    ob0 = zvc_tile_offset<ESZ, V>(local, sup, tb, num_tiles);
+    ob1 = zvc_tile_offset<ESZ, V>(local, sup, tb + 1, num_tiles);
   }
   for (;;) {
     // A holds tile ta; fetch tile tb into B; offsets of the tile after tb
     uint32_t tc = tb + G, oc0 = 0, oc1 = 0;
     if (tb < num_tiles) zvc_fetch_tile<ESZ, V>(B, src, eff, W, tb, ob0, ob1, tid);
     if (tc < num_tiles) {
-      oc0 = offsets[tc];
-      oc1 = offsets[tc + 1];
+      oc0 = zvc_tile_offset<ESZ, V>(local, sup, tc, num_tiles);
+      oc1 = zvc_tile_offset<ESZ, V>(local, sup, tc + 1, num_tiles);
     }
     if (A.short_read) err |= CDMA_E_SIZE;
     zvc_expand_tile<ESZ, V>(L, A, ta, n, dst, tid, wave, lane);
@@ -626,8 +668,8 @@ __global__ __launch_bounds__(kBlock) void zvc_expand_kernel(
     tc = tb + G;
     if (tb < num_tiles) zvc_fetch_tile<ESZ, V>(A, src, eff, W, tb, ob0, ob1, tid);
     if (tc < num_tiles) {
-      oc0 = offsets[tc];
-      oc1 = offsets[tc + 1];
+      oc0 = zvc_tile_offset<ESZ, V>(local, sup, tc, num_tiles);
+      oc1 = zvc_tile_offset<ESZ, V>(local, sup, tc + 1, num_tiles);
     }
     if (B.short_read) err |= CDMA_E_SIZE;
     zvc_expand_tile<ESZ, V>(L, B, ta, n, dst, tid, wave, lane);
