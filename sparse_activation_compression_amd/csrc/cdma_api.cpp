@@ -17,7 +17,7 @@ uint64_t max_n(int algo) { return algo == CDMA_ALGO_ZVC ? CDMA_ZVC_MAX_N : CDMA_
 uint64_t rle_window(int esz) { return 4096u / (unsigned)esz; }
 
 uint64_t tiles(int algo, int esz, uint64_t n) {
-  return algo == CDMA_ALGO_ZVC ? cdma::zvc_tiles(esz, n) : cdma::rle_tiles(esz, n);
+  return algo == CDMA_ALGO_ZVC ? cdma::zvc_tiles(esz, n) : cdma::rle_compress_tiles(esz, n);
 }
 
 }  // namespace
@@ -33,7 +33,8 @@ uint64_t cdma_max_compressed_bytes(int algo, int esz, uint64_t n) {
 
 uint64_t cdma_workspace_bytes(int algo, int esz, uint64_t n) {
   if (!algo_ok(algo) || !esz_ok(esz) || n > max_n(algo)) return 0;
-  // counter, one scan status word per tile, and (ZVC) one value offset per tile
+  // counter and one scan status word per compress tile; ZVC decompress keeps a
+  // value offset per (smaller) decompress tile in the same space
   const uint64_t t = tiles(algo, esz, n);
   return algo == CDMA_ALGO_ZVC ? cdma::kWsHeader + 12 * t + 16 : cdma::kWsHeader + 8 * t;
 }

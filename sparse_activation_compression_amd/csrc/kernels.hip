@@ -154,15 +154,23 @@ uint64_t rle_tiles(int esz, uint64_t n) {
   return (n + te - 1) / te;
 }
 
+uint64_t rle_compress_tiles(int esz, uint64_t n) {
+  const uint64_t te = esz == 4 ? RleCShape<4>::TE : RleCShape<2>::TE;
+  return (n + te - 1) / te;
+}
+
 template <int ESZ>
 static hipError_t rle_compress_t(const void* src, uint64_t n, void* dst, uint64_t* out_bytes, void* ws,
                                  hipStream_t s) {
-  const uint64_t tiles = rle_tiles(ESZ, n);
+  constexpr int block = RleCShape<ESZ>::BLOCK;
+  const uint64_t tiles = rle_compress_tiles(ESZ, n);
   hipError_t e = clear_workspace(ws, tiles, s);
   if (e != hipSuccess) return e;
-  rle_compress_kernel<ESZ><<<(unsigned)tiles, kBlock, 0, s>>>(
-      static_cast<const uint8_t*>(src), n, static_cast<uint8_t*>(dst), out_bytes, ws_counter(ws),
-      ws_status(ws), (uint32_t)tiles);
+  auto kern = rle_compress_kernel<ESZ>;
+  const uint64_t res = resident_groups(reinterpret_cast<const void*>(kern), block);
+  const unsigned grid = (unsigned)(tiles < res ? tiles : res);
+  kern<<<grid, block, 0, s>>>(static_cast<const uint8_t*>(src), n, static_cast<uint8_t*>(dst), out_bytes,
+                              ws_counter(ws), ws_status(ws), (uint32_t)tiles);
   return hipGetLastError();
 }
 

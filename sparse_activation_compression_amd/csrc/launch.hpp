@@ -12,7 +12,8 @@ constexpr uint64_t kWsHeader = 256;  // tile-ticket counter, padded
 
 uint64_t zvc_tiles(int esz, uint64_t n);           // decompress tiles
 uint64_t zvc_compress_tiles(int esz, uint64_t n);  // compress tiles (fewer, larger)
-uint64_t rle_tiles(int esz, uint64_t n);
+uint64_t rle_tiles(int esz, uint64_t n);           // decompress tiles
+uint64_t rle_compress_tiles(int esz, uint64_t n);  // compress tiles (fewer, larger)
 
 hipError_t zvc_compress_launch(int esz, const void* src, uint64_t n, void* dst, uint64_t* out_bytes,
                                void* ws, hipStream_t s);

@@ -12,14 +12,16 @@
 //
 // One wavefront owns one window: 4 vectors of 16 bytes per lane cover exactly
 // E elements, so each window's bitmap (E/32 mask words), runs and values are
-// produced by one wave, and a workgroup of 4 waves handles 4 windows.
+// produced by one wave.
 //
-// compress:   load -> nonzero bits -> window masks in LDS (DPP OR) -> run
-//             boundaries = mask XOR (mask shifted by one element) -> per-wave
-//             counts of boundaries and nonzeros -> one decoupled lookback over
-//             the packed pair (entries, nonzeros) gives the tile's byte offset
-//             -> run lengths (gaps between boundaries) and values compacted
-//             into LDS at their final alignment -> aligned 16-byte stores.
+// compress:   persistent workgroups of NW waves take tiles of NW windows from a
+//             ticket counter: load -> nonzero bits -> window masks in LDS (DPP
+//             OR) -> run boundaries = mask XOR (mask shifted by one element) ->
+//             per-window entry and nonzero counts -> run lengths (gaps between
+//             boundaries) and values staged in LDS -> one decoupled lookback
+//             over the packed pair (entries, nonzeros), overlapped with the
+//             next tile, gives the tile's byte offset -> realigned 16-byte
+//             stores of the staged blocks and the tile's index entries.
 // decompress: the index gives each window's block offset directly (no scan)
 //             -> block read into LDS -> run starts by a wave prefix sum ->
 //             boundary bitmap (LDS XOR) -> prefix-XOR turns boundaries back
@@ -40,7 +42,6 @@ struct RleShape {
   static constexpr int WPW = E / 32;               // mask words per window (32 or 64)
   static constexpr int MAXENT = E + 2;             // run entries incl. padding, upper bound
   static constexpr int BLK = 2 * MAXENT + ESZ * E;  // largest block in bytes
-  static constexpr int STAGE = kWaves * BLK + 32;  // compress: the tile's blocks + alignment
   static constexpr int WSTAGE = BLK + 32;          // decompress: one window's block + alignment
   static_assert(V * 64 * EPL == E, "a wavefront must cover one window");
 };
@@ -62,172 +63,258 @@ __device__ __forceinline__ void lds_u16(uint8_t* base, uint32_t byte, uint32_t v
 }
 
 // ---------------------------------------------------------------------------
-// compress
+// compress: persistent workgroups, one wavefront per window, lag-1 pipeline
 // ---------------------------------------------------------------------------
+//
+// The same pipeline as the ZVC compressor: a tile is NW windows (one per
+// wavefront), tiles come from a ticket counter, and iteration i of a
+// workgroup classifies tile t (runs and values staged in LDS buffer i%2, its
+// aggregate published), prefetches the next ticket, resolves the lookback of
+// the previous tile tp (issued at the end of iteration i-1) and stores tp's
+// blocks and index entries.  The aggregate of a tile packs its run-entry count
+// and nonzero count as (entries << 31) | nonzeros; the stream limit keeps both
+// sums below 2^31, so packed sums never carry between the fields.  The
+// progress argument of the ZVC compressor applies unchanged.
+//
+// A window of L elements with v nonzeros has k <= min(v, L - v + 1) nonzero
+// runs and at most 2k + 1 runs, so its block is at most 4L + 8 bytes for
+// 32-bit and 3L + 6 bytes for 16-bit elements; BLKMAX bounds the staging.
 
 template <int ESZ>
-__global__ __launch_bounds__(kBlock) void rle_compress_kernel(
+struct RleCShape {
+  static constexpr int BLOCK = ESZ == 4 ? 1024 : 512;  // threads (16-bit blocks stage up to 1.5x)
+  static constexpr int NW = BLOCK / 64;                 // windows per tile
+  static constexpr int V = 4;
+  static constexpr int EPL = 16 / ESZ;
+  static constexpr int LPW = 32 / EPL;
+  static constexpr int E = 4096 / ESZ;
+  static constexpr int TE = NW * E;
+  static constexpr int WPW = E / 32;
+  static constexpr int BLKMAX = ESZ == 4 ? 4 * E + 8 : 3 * E + 6;
+  static constexpr int STAGE = NW * BLKMAX + 16;
+  static_assert(V * 64 * EPL == E, "a wavefront must cover one window");
+};
+
+template <int ESZ>
+struct RleCLds {
+  using S = RleCShape<ESZ>;
+  uint64_t excl;                        // packed exclusive prefix of the tile being stored
+  uint64_t agg[2];                      // packed aggregate of the tile in stage[b]
+  uint32_t pw[2][S::NW], vw[2][S::NW];  // per-window entries and nonzeros of that tile
+  uint32_t next;
+  bool stuck;
+  uint32_t mask[S::NW * S::WPW];
+  __attribute__((aligned(16))) uint8_t stage[2][S::STAGE];
+};
+
+template <int ESZ>
+__device__ __forceinline__ void rle_c_load_full(u32x4 (&v)[RleCShape<ESZ>::V], const uint8_t* __restrict__ src,
+                                                uint32_t t, int wave, int lane) {
+  using S = RleCShape<ESZ>;
+  // uniform 64-bit tile base (SGPRs) plus a 32-bit per-lane offset; the empty
+  // asm keeps the compiler from hoisting base + offset into a 64-bit VGPR
+  // pair that would outlive the loop and spill
+  const uint8_t* p = src + (uint64_t)t * (S::NW * 4096);
+  uint32_t o = (uint32_t)(wave * 4096 + lane * 16);
+  asm volatile("" : "+v"(o));
+#pragma unroll
+  for (int j = 0; j < S::V; ++j) v[j] = ld_stream(reinterpret_cast<const u32x4*>(p + o + j * 1024));
+}
+
+template <int ESZ>
+__device__ __forceinline__ uint32_t rle_c_iteration(RleCLds<ESZ>& L, u32x4 (&cur)[RleCShape<ESZ>::V],
+                                                    u32x4 (&nxt)[RleCShape<ESZ>::V], LookbackRound& lr,
+                                                    uint32_t t, uint32_t tp, int buf, uint32_t full, uint64_t Wr,
+                                                    const uint8_t* __restrict__ src, uint64_t n,
+                                                    uint8_t* __restrict__ dst, uint64_t* __restrict__ out_bytes,
+                                                    uint64_t* __restrict__ status, uint32_t* __restrict__ counter,
+                                                    uint32_t num_tiles, int tid, int wave, int lane) {
+  using S = RleCShape<ESZ>;
+  constexpr int V = S::V;
+  const bool have_cur = t < num_tiles;
+  const bool have_prev = tp < num_tiles;
+  const uint64_t H = 8 * (Wr + 1);
+
+  uint32_t ticket = 0;
+  if (have_cur && tid == S::BLOCK - 64)
+    ticket = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+  // classify this wave's window
+  const uint64_t gw = (uint64_t)t * S::NW + wave;
+  const uint64_t e_win = gw * S::E;
+  const uint32_t Lw = have_cur && gw < Wr ? (uint32_t)(n - e_win < (uint64_t)S::E ? n - e_win : S::E) : 0u;
+  uint32_t ex[V], v_w = 0;  // ex[j]: nonzeros of the window before lane's vector j
+  if (have_cur) {
+    if (t >= full) {  // the one partial tile: load bounded, drain so nothing stays pending on cur
+      uint32_t el = (uint32_t)lane * S::EPL;
+      asm volatile("" : "+v"(el));
+      for (int j = 0; j < V; ++j) cur[j] = load_vec<ESZ>(src, e_win + (el + (uint32_t)(j * 64 * S::EPL)), n);
+      __builtin_amdgcn_s_waitcnt(0);
+    }
+    uint32_t* wmask = L.mask + wave * S::WPW + lane / S::LPW;
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      const uint32_t bits = vec_nz_bits<ESZ>(cur[j]);
+      const uint32_t m = group_or<S::LPW>(bits << ((lane % S::LPW) * S::EPL));
+      if (lane % S::LPW == 0) wmask[j * (64 / S::LPW)] = m;
+      const uint32_t cnt = (uint32_t)__builtin_popcount(bits);
+      const uint32_t inc = wave_incl_scan(cnt);
+      ex[j] = v_w + inc - cnt;
+      v_w += read_lane(inc, 63);
+    }
+  }
+  if (tid == S::BLOCK - 64) L.next = have_cur ? ticket : num_tiles;
+  __syncthreads();
+  const uint32_t tn = __builtin_amdgcn_readfirstlane(L.next);  // uniform: keeps tile bases in SGPRs
+
+  // run boundaries: lane g holds mask word g of the window
+  const uint32_t g = (uint32_t)lane;
+  uint32_t T = 0, texcl = 0, r_w = 0, p_w = 0;
+  if (have_cur) {
+    if (g < (uint32_t)S::WPW && 32 * g < Lw) {
+      const uint32_t m = L.mask[wave * S::WPW + g];
+      const uint32_t prev = g ? L.mask[wave * S::WPW + g - 1] : 0u;
+      T = m ^ ((m << 1) | (prev >> 31));  // the element before the window counts as zero
+      const uint32_t rem = Lw - 32 * g;
+      if (rem < 32) T &= (1u << rem) - 1;
+    }
+    const uint32_t tc = (uint32_t)__builtin_popcount(T);
+    const uint32_t tinc = wave_incl_scan(tc);
+    texcl = tinc - tc;
+    r_w = Lw ? 1 + read_lane(tinc, 63) : 0u;
+    p_w = ESZ == 4 ? r_w + (r_w & 1) : r_w;
+    if (lane == 0) {
+      L.pw[buf][wave] = p_w;
+      L.vw[buf][wave] = v_w;
+    }
+  }
+  __syncthreads();
+
+  if (have_cur) {
+    uint32_t P = 0, Vs = 0, blk = 0;
+#pragma unroll
+    for (int w = 0; w < S::NW; ++w) {
+      if (w == wave) blk = 2 * P + ESZ * Vs;
+      P += L.pw[buf][w];
+      Vs += L.vw[buf][w];
+    }
+    const uint64_t agg = ((uint64_t)P << 31) | Vs;
+    if (tid == 0) {
+      L.agg[buf] = agg;
+      status_store(&status[t], (t == 0 ? kFlagPrefix : kFlagAggregate) | agg);
+    }
+    uint8_t* st = L.stage[buf] + blk;
+    if (Lw) {
+      // run lengths: the gap from the previous boundary (0 at the window start)
+      const uint32_t lastpos = T ? 32 * g + 31 - (uint32_t)__builtin_clz(T) : 0u;
+      const uint32_t imax = wave_incl_max(lastpos);
+      const uint32_t before = __shfl_up(imax, 1, 64);
+      uint32_t prev = lane ? before : 0u;
+      const uint32_t tau_last = read_lane(imax, 63);
+      uint32_t x = T, k = texcl;
+      while (x) {
+        const uint32_t b = (uint32_t)__builtin_ctz(x);
+        x &= x - 1;
+        const uint32_t pos = 32 * g + b;
+        lds_u16(st, 2 * k, pos - prev);
+        prev = pos;
+        ++k;
+      }
+      if (lane == 0) {
+        lds_u16(st, 2 * (r_w - 1), Lw - tau_last);
+        if (p_w > r_w) lds_u16(st, 2 * r_w, 0);
+      }
+      // values follow the runs
+#pragma unroll
+      for (int j = 0; j < V; ++j) {
+        const uint32_t bits = vec_nz_bits<ESZ>(cur[j]);
+        uint32_t pos = 2 * p_w + ESZ * ex[j];
+#pragma unroll
+        for (int k2 = 0; k2 < S::EPL; ++k2) {
+          if ((bits >> k2) & 1u) {
+            store_elem<ESZ>(st + pos, vec_elem<ESZ>(cur[j], k2));
+            pos += ESZ;
+          }
+        }
+      }
+    }
+    if (tn < full) rle_c_load_full<ESZ>(nxt, src, tn, wave, lane);
+  }
+  if (wave == 0 && have_prev) {
+    bool stuck = false;
+    const uint64_t X = tp > 0 ? lookback_resolve(status, tp, lr, &stuck) : 0;
+    if (lane == 0) {
+      L.excl = X;
+      L.stuck = stuck;
+      if (tp > 0) status_store(&status[tp], kFlagPrefix | (X + L.agg[buf ^ 1]));
+    }
+  }
+  __syncthreads();
+
+  if (have_prev) {
+    const int pb = buf ^ 1;
+    const uint64_t agg = L.agg[pb];
+    const uint32_t P = (uint32_t)(agg >> 31), Vs = (uint32_t)(agg & kLow31);
+    const uint64_t RX = L.excl >> 31, VX = L.excl & kLow31;
+    const uint64_t O = H + 2 * RX + (uint64_t)ESZ * VX;  // first byte of the tile's blocks
+    const uint32_t span = 2 * P + ESZ * Vs;
+    store_staged<2, S::BLOCK>(L.stage[pb], span, O, dst, tid);
+    if (tid < S::NW) {
+      const uint64_t w = (uint64_t)tp * S::NW + tid;
+      if (w < Wr) {
+        uint32_t pr = 0, vr = 0;
+        for (int k = 0; k < tid; ++k) {
+          pr += L.pw[pb][k];
+          vr += L.vw[pb][k];
+        }
+        reinterpret_cast<uint32_t*>(dst)[w] = (uint32_t)(RX + pr);
+        reinterpret_cast<uint32_t*>(dst + 4 * (Wr + 1))[w] = (uint32_t)(VX + vr);
+      }
+    }
+    // Only the last tile reports the size; its lookback passes over every
+    // tile, so if any lookback could not finish, neither could this one.
+    if (tp == num_tiles - 1 && tid == 0) {
+      reinterpret_cast<uint32_t*>(dst)[Wr] = (uint32_t)(RX + P);
+      reinterpret_cast<uint32_t*>(dst + 4 * (Wr + 1))[Wr] = (uint32_t)(VX + Vs);
+      *out_bytes = L.stuck ? kSizeInternalError : O + span;
+    }
+  }
+  if (wave == 0 && have_cur && t > 0) lookback_issue(status, (int64_t)t - 1, lr);
+  __syncthreads();
+  return tn;
+}
+
+template <int ESZ>
+__global__ __launch_bounds__(RleCShape<ESZ>::BLOCK) void rle_compress_kernel(
     const uint8_t* __restrict__ src, uint64_t n, uint8_t* __restrict__ dst,
     uint64_t* __restrict__ out_bytes, uint32_t* __restrict__ counter,
     uint64_t* __restrict__ status, uint32_t num_tiles) {
-  using S = RleShape<ESZ>;
-  constexpr int V = S::V;
-  __shared__ uint32_t s_ticket;
-  __shared__ uint64_t s_excl;
-  __shared__ bool s_stuck;
-  __shared__ uint32_t s_tot[kWaves * V];
-  __shared__ uint32_t s_mask[kWaves * S::WPW];
-  __shared__ uint32_t s_p[kWaves], s_v[kWaves];
-  __shared__ __attribute__((aligned(16))) uint8_t s_stage[S::STAGE];
-
+  using S = RleCShape<ESZ>;
+  __shared__ RleCLds<ESZ> L;
   const int tid = threadIdx.x;
   const int lane = (int)lane_id();
   const int wave = tid >> 6;
-  if (tid == 0) s_ticket = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  const uint32_t t = s_ticket;
   const uint64_t Wr = (n + S::E - 1) / S::E;
-  const uint64_t H = 8 * (Wr + 1);
-  const uint64_t gw = (uint64_t)t * kWaves + wave;  // this wave's window
-  const uint64_t e_win = gw * S::E;
-  const uint32_t Lw = gw < Wr ? (uint32_t)(n - e_win < (uint64_t)S::E ? n - e_win : S::E) : 0;
-
-  u32x4 v[V];
-#pragma unroll
-  for (int j = 0; j < V; ++j) v[j] = load_vec<ESZ>(src, e_win + (uint64_t)(j * 64 + lane) * S::EPL, n);
-
-  uint32_t bits[V], ex[V];
-#pragma unroll
-  for (int j = 0; j < V; ++j) {
-    const uint32_t c = (uint32_t)(j * 64 + lane);  // vector index inside the window
-    bits[j] = vec_nz_bits<ESZ>(v[j]);
-    const uint32_t m = group_or<S::LPW>(bits[j] << ((lane % S::LPW) * S::EPL));
-    if (lane % S::LPW == 0) s_mask[wave * S::WPW + c / S::LPW] = m;
-    const uint32_t cnt = (uint32_t)__builtin_popcount(bits[j]);
-    const uint32_t inc = wave_incl_scan(cnt);
-    ex[j] = inc - cnt;
-    if (lane == 63) s_tot[wave * V + j] = inc;
-  }
+  const uint32_t full = (uint32_t)(n / S::TE);  // tiles with no element past n
+  if (tid == 0) L.next = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
-
-  uint32_t vbase[V], v_w = 0;
-#pragma unroll
-  for (int j = 0; j < V; ++j) {
-    vbase[j] = v_w;
-    v_w += s_tot[wave * V + j];
+  uint32_t t = __builtin_amdgcn_readfirstlane(L.next);
+  uint32_t tp = num_tiles;
+  u32x4 ra[S::V], rb[S::V];
+  LookbackRound lr;
+  if (t < full) rle_c_load_full<ESZ>(ra, src, t, wave, lane);
+  for (;;) {
+    uint32_t tn = rle_c_iteration<ESZ>(L, ra, rb, lr, t, tp, 0, full, Wr, src, n, dst, out_bytes, status, counter,
+                                       num_tiles, tid, wave, lane);
+    if (t >= num_tiles) break;
+    tp = t;
+    t = tn;
+    tn = rle_c_iteration<ESZ>(L, rb, ra, lr, t, tp, 1, full, Wr, src, n, dst, out_bytes, status, counter,
+                              num_tiles, tid, wave, lane);
+    if (t >= num_tiles) break;
+    tp = t;
+    t = tn;
   }
-
-  // run boundaries of this wave's window: lane g holds mask word g
-  const uint32_t g = (uint32_t)lane;
-  uint32_t T = 0;
-  if (g < (uint32_t)S::WPW && 32 * g < Lw) {
-    const uint32_t m = s_mask[wave * S::WPW + g];
-    const uint32_t prev = g ? s_mask[wave * S::WPW + g - 1] : 0u;
-    T = m ^ ((m << 1) | (prev >> 31));  // element before the window counts as zero
-    const uint32_t rem = Lw - 32 * g;
-    if (rem < 32) T &= (1u << rem) - 1;
-  }
-  const uint32_t tc = (uint32_t)__builtin_popcount(T);
-  const uint32_t tinc = wave_incl_scan(tc);
-  const uint32_t texcl = tinc - tc;
-  const uint32_t r_w = Lw ? 1 + read_lane(tinc, 63) : 0;
-  const uint32_t p_w = ESZ == 4 ? r_w + (r_w & 1) : r_w;
-  if (lane == 0) {
-    s_p[wave] = p_w;
-    s_v[wave] = v_w;
-  }
-  __syncthreads();
-
-  uint32_t P = 0, Vs = 0, blk = 0;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    if (w == wave) blk = 2 * P + ESZ * Vs;
-    P += s_p[w];
-    Vs += s_v[w];
-  }
-  const uint32_t span = 2 * P + ESZ * Vs;
-  if (wave == 0) {
-    bool stuck;
-    const uint64_t x = lookback_exclusive(status, t, ((uint64_t)P << 31) | Vs, &stuck);
-    if (lane == 0) {
-      s_excl = x;
-      s_stuck = stuck;
-    }
-  }
-  __syncthreads();
-  const uint64_t RX = s_excl >> 31, VX = s_excl & kLow31;
-  const uint64_t O = H + 2 * RX + (uint64_t)ESZ * VX;  // first byte of this tile's blocks
-  const uint32_t shift = (uint32_t)(O & 15);
-
-  // index entries of this tile's windows (fixed offsets)
-  if (tid < kWaves) {
-    const uint64_t w = (uint64_t)t * kWaves + tid;
-    if (w < Wr) {
-      uint32_t pr = 0, vr = 0;
-      for (int k = 0; k < tid; ++k) {
-        pr += s_p[k];
-        vr += s_v[k];
-      }
-      reinterpret_cast<uint32_t*>(dst)[w] = (uint32_t)(RX + pr);
-      reinterpret_cast<uint32_t*>(dst + 4 * (Wr + 1))[w] = (uint32_t)(VX + vr);
-    }
-  }
-  if (t == num_tiles - 1 && tid == 0) {
-    reinterpret_cast<uint32_t*>(dst)[Wr] = (uint32_t)(RX + P);
-    reinterpret_cast<uint32_t*>(dst + 4 * (Wr + 1))[Wr] = (uint32_t)(VX + Vs);
-  }
-
-  // run lengths: the gap from the previous boundary (0 at the window start)
-  const uint32_t bw = shift + blk;
-  if (Lw) {
-    const uint32_t lastpos = T ? 32 * g + 31 - (uint32_t)__builtin_clz(T) : 0u;
-    const uint32_t imax = wave_incl_max(lastpos);
-    const uint32_t before = __shfl_up(imax, 1, 64);
-    uint32_t prev = lane ? before : 0u;
-    const uint32_t tau_last = read_lane(imax, 63);
-    uint32_t x = T, k = 1 + texcl;
-    while (x) {
-      const uint32_t b = (uint32_t)__builtin_ctz(x);
-      x &= x - 1;
-      const uint32_t pos = 32 * g + b;
-      lds_u16(s_stage, bw + 2 * (k - 1), pos - prev);
-      prev = pos;
-      ++k;
-    }
-    if (lane == 0) {
-      lds_u16(s_stage, bw + 2 * (r_w - 1), Lw - tau_last);
-      if (p_w > r_w) lds_u16(s_stage, bw + 2 * r_w, 0);
-    }
-  }
-  // values follow the runs
-#pragma unroll
-  for (int j = 0; j < V; ++j) {
-    uint32_t pos = bw + 2 * p_w + ESZ * (vbase[j] + ex[j]);
-#pragma unroll
-    for (int k = 0; k < S::EPL; ++k) {
-      if ((bits[j] >> k) & 1u) {
-        store_elem<ESZ>(s_stage + pos, vec_elem<ESZ>(v[j], k));
-        pos += ESZ;
-      }
-    }
-  }
-  __syncthreads();
-
-  const uint64_t beg = O, end = O + span;
-  const uint64_t q0 = beg >> 4, q1 = (end + 15) >> 4;
-  for (uint64_t q = q0 + tid; q < q1; q += kBlock) {
-    const uint64_t qb = q << 4;
-    const uint32_t lo = (uint32_t)(qb - (q0 << 4));
-    if (qb >= beg && qb + 16 <= end) {
-      st_stream(reinterpret_cast<u32x4*>(dst + qb), *reinterpret_cast<const u32x4*>(s_stage + lo));
-    } else {
-      for (int k = 0; k < 16; k += 2) {
-        const uint64_t b = qb + k;
-        if (b >= beg && b < end) *reinterpret_cast<uint16_t*>(dst + b) = *reinterpret_cast<const uint16_t*>(s_stage + lo + k);
-      }
-    }
-  }
-  if (t == num_tiles - 1 && tid == 0) *out_bytes = s_stuck ? kSizeInternalError : end;
 }
 
 // ---------------------------------------------------------------------------

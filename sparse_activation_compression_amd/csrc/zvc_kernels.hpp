@@ -193,26 +193,30 @@ __device__ __forceinline__ void zvc_c_load_bounded(u32x4 (&v)[ZvcCShape<ESZ>::V]
   }
 }
 
-// Store the T staged values of a tile to stream bytes [A, A + ESZ*T): aligned
-// 16-byte stores, the staged bytes shifted into place on the way.
-template <int ESZ>
-__device__ __forceinline__ void zvc_c_store_values(const uint8_t* __restrict__ st, uint32_t T, uint64_t A,
-                                                   uint8_t* __restrict__ dst, int tid) {
-  const uint64_t end = A + (uint64_t)ESZ * T;
+// Store `bytes` staged bytes (staged from offset 0) to stream bytes
+// [A, A + bytes) with NT threads: aligned 16-byte stores, the staged bytes
+// shifted into place on the way.  A and bytes are multiples of G (2 or 4);
+// the two partial quads at the ends are written G bytes at a time.  Reads up
+// to 4 bytes past the staged span, which the stage buffer must hold.
+template <int G, int NT>
+__device__ __forceinline__ void store_staged(const uint8_t* __restrict__ st, uint32_t bytes, uint64_t A,
+                                             uint8_t* __restrict__ dst, int tid) {
+  static_assert(G == 2 || G == 4, "store granularity");
+  const uint64_t end = A + bytes;
   const uint64_t q0 = A >> 4, q1 = (end + 15) >> 4;
   const uint32_t d = (uint32_t)(A & 15);
   const uint32_t* sw = reinterpret_cast<const uint32_t*>(st);
-  for (uint64_t q = q0 + tid; q < q1; q += kCBlock) {
+  for (uint64_t q = q0 + tid; q < q1; q += NT) {
     const uint64_t qb = q << 4;
     if (qb >= A && qb + 16 <= end) {
       const uint32_t o = (uint32_t)(qb - A);  // staged byte of the quad's first byte
       u32x4 out;
       if (d == 0) {
         out = *reinterpret_cast<const u32x4*>(st + o);
-      } else if ((d & 3) == 0) {
+      } else if (G == 4 || (d & 3) == 0) {
         const uint32_t i = o >> 2;
         out = u32x4{sw[i], sw[i + 1], sw[i + 2], sw[i + 3]};
-      } else {  // 16-bit elements, 2 bytes off a word boundary
+      } else {  // 2 bytes off a word boundary
         const uint32_t i = o >> 2;
         const uint32_t w0 = sw[i], w1 = sw[i + 1], w2 = sw[i + 2], w3 = sw[i + 3], w4 = sw[i + 4];
         out = u32x4{__builtin_amdgcn_alignbyte(w1, w0, 2), __builtin_amdgcn_alignbyte(w2, w1, 2),
@@ -220,9 +224,9 @@ __device__ __forceinline__ void zvc_c_store_values(const uint8_t* __restrict__ s
       }
       st_stream(reinterpret_cast<u32x4*>(dst + qb), out);
     } else {
-      for (int k = 0; k < 16; k += ESZ) {
+      for (int k = 0; k < 16; k += G) {
         const uint64_t b = qb + k;
-        if (b >= A && b < end) store_elem<ESZ>(dst + b, load_elem<ESZ>(st + (b - A)));
+        if (b >= A && b < end) store_elem<G>(dst + b, load_elem<G>(st + (b - A)));
       }
     }
   }
@@ -271,7 +275,7 @@ __device__ __forceinline__ uint32_t zvc_c_iteration(ZvcCLds<ESZ>& L, u32x4 (&cur
   }
   if (tid == kCBlock - 64) L.next = have_cur ? ticket : num_tiles;
   __syncthreads();
-  const uint32_t tn = L.next;
+  const uint32_t tn = __builtin_amdgcn_readfirstlane(L.next);  // uniform: keeps tile bases in SGPRs
 
   if (have_cur) {
     // segment bases: lane l of every wave scans the segment totals
@@ -314,7 +318,7 @@ __device__ __forceinline__ uint32_t zvc_c_iteration(ZvcCLds<ESZ>& L, u32x4 (&cur
   if (have_prev) {
     const uint32_t T = L.total[buf ^ 1];
     const uint64_t A = 4 * W + (uint64_t)ESZ * L.excl;
-    zvc_c_store_values<ESZ>(L.stage[buf ^ 1], T, A, dst, tid);
+    store_staged<ESZ, kCBlock>(L.stage[buf ^ 1], ESZ * T, A, dst, tid);
     // Only the last tile reports the size; its lookback passes over every
     // tile, so if any lookback could not finish, neither could this one.
     if (tp == num_tiles - 1 && tid == 0) *out_bytes = L.stuck ? kSizeInternalError : A + (uint64_t)ESZ * T;
@@ -341,7 +345,7 @@ __global__ __launch_bounds__(kCBlock) void zvc_compress_kernel(
   const uint32_t full = (uint32_t)(n / S::TE);  // tiles with no element past n
   if (tid == 0) L.next = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
-  uint32_t t = L.next;        // tile to classify
+  uint32_t t = __builtin_amdgcn_readfirstlane(L.next);        // tile to classify
   uint32_t tp = num_tiles;    // tile to store (none yet)
   u32x4 ra[S::V], rb[S::V];
   LookbackRound lr;
