@@ -97,175 +97,87 @@ __device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
 
 // ---- decoupled lookback ----------------------------------------------------
 //
-// status[t] holds flag (2 bits) | value (62 bits) in one 64-bit word that is
-// written and read with single-copy-atomic agent-scope accesses, so no fence
-// is needed: the value travels inside the word that carries the flag.  The
-// "value" is a sum that composes by 64-bit addition (a count, or two packed
-// 31-bit counts).
-
-constexpr uint64_t kFlagAggregate = 1ull << 62;  // tile's own total is known
-constexpr uint64_t kFlagPrefix = 2ull << 62;     // inclusive prefix is known
-constexpr uint64_t kValueMask = (1ull << 62) - 1;
 constexpr uint64_t kSizeInternalError = CDMA_SIZE_INTERNAL_ERROR;
 
-__device__ __forceinline__ void status_store(uint64_t* p, uint64_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// ---- tile offsets: per-workgroup chaining over published aggregates --------
+//
+// A persistent workgroup takes its tiles in increasing order, so the exclusive
+// prefix of its tile t is the inclusive prefix of its own previous tile tp plus
+// the aggregates of the tiles strictly between tp and t (of all tiles before t,
+// for its first tile).  A tile therefore publishes only its aggregate, and no
+// workgroup ever waits for another one's prefix, only for aggregates, which
+// every tile publishes as soon as it is classified.  agg[t] holds the
+// aggregate plus one (0 = not yet published), written and read with
+// single-copy-atomic agent-scope 32-bit accesses; the workspace is cleared
+// before each launch.
+
+__device__ __forceinline__ void agg_publish(uint32_t* agg, uint32_t t, uint32_t v) {
+  __hip_atomic_store(&agg[t], v + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ uint64_t status_load(const uint64_t* p) {
-  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ uint32_t agg_load(const uint32_t* agg, uint64_t i) {
+  return __hip_atomic_load(const_cast<uint32_t*>(agg) + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Upper bound on polling rounds of one lookback.  A predecessor publishes its
-// aggregate a few microseconds after it starts, so a healthy wait is a few
+// Upper bound on polling rounds of one chain sum.  A tile's aggregate appears
+// a few microseconds after its ticket is drawn, so a healthy wait is a few
 // rounds; the bound only turns an impossible wait into a reported error
 // instead of a wave that never finishes.
-constexpr uint32_t kLookbackSpinLimit = 1u << 21;
+constexpr uint32_t kChainSpinLimit = 1u << 21;
 
-// Predecessors examined per lookback round: kLookbackK status words per lane.
-// One round covers 64*kLookbackK tiles, so tiles can enter the pipeline at up
-// to 64*kLookbackK per round-trip latency of a status read.
-#ifndef CDMA_LOOKBACK_K
-#define CDMA_LOOKBACK_K 4
+// Aggregate words read per lane per round: one round covers 64*kChainK tiles.
+#ifndef CDMA_CHAIN_K
+#define CDMA_CHAIN_K 4
 #endif
-constexpr int kLookbackK = CDMA_LOOKBACK_K;
+constexpr int kChainK = CDMA_CHAIN_K;
 
-// Called by all 64 lanes of one wavefront of tile t with the tile's own
-// aggregate.  Publishes the aggregate, looks back over predecessors
-// 64*kLookbackK at a time until one with a known inclusive prefix closes the
-// window, publishes this tile's inclusive prefix and returns the exclusive
-// prefix (uniform).  Every predecessor belongs to a workgroup that is resident
-// and publishes its aggregate without waiting, so the loop ends; *stuck is
-// set if the spin bound was hit anyway (the result is then meaningless).
-//
-// `after_issue` runs once, right after the first round's status loads are
-// issued.  Vector-memory counters retire in order on this GPU, so loads the
-// caller issues there (e.g. a prefetch) do not delay that first round.
-struct NoOp {
-  __device__ void operator()() const {}
+struct ChainRound {
+  uint32_t w[kChainK];
 };
 
-template <typename F = NoOp>
-__device__ __forceinline__ uint64_t lookback_exclusive(uint64_t* status, uint32_t t, uint64_t agg,
-                                                       bool* stuck, F after_issue = F()) {
-  const uint32_t lane = lane_id();
-  *stuck = false;
-  if (t == 0) {
-    if (lane == 0) status_store(&status[0], kFlagPrefix | agg);
-    after_issue();
-    return 0;
-  }
-  if (lane == 0) status_store(&status[t], kFlagAggregate | agg);
-  uint64_t excl = 0;
-  int64_t base = (int64_t)t - 1;
-  uint32_t spins = 0;
-  bool first = true;
-  for (;;) {
-    // slot k*64 + lane looks at tile base - (k*64 + lane): nearest first
-    uint64_t s[kLookbackK];
-#pragma unroll
-    for (int k = 0; k < kLookbackK; ++k) {
-      const int64_t idx = base - (int64_t)(k * 64 + lane);
-      s[k] = idx >= 0 ? status_load(&status[idx]) : kFlagPrefix;
-    }
-    if (first) {
-      after_issue();
-      first = false;
-    }
-    bool wait = false, closed = false;
-    uint64_t sum = 0;
-#pragma unroll
-    for (int k = 0; k < kLookbackK; ++k) {
-      if (wait || closed) break;
-      const uint32_t flag = (uint32_t)(s[k] >> 62);
-      const uint64_t pmask = __ballot(flag == 2);
-      const uint64_t zmask = __ballot(flag == 0);
-      const int p = pmask ? __ffsll((unsigned long long)pmask) - 1 : 64;  // nearest prefix
-      const uint64_t need = p >= 63 ? ~0ull : ((2ull << p) - 1);          // lanes 0..p
-      if (zmask & need) {
-        wait = true;
-      } else {
-        sum += (int)lane <= p ? (s[k] & kValueMask) : 0;
-        closed = p < 64;
-      }
-    }
-    if (wait && !closed) {
-      // partial progress is discarded: the next round re-reads the same window
-      if (++spins > kLookbackSpinLimit) {
-        *stuck = true;
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
-      continue;
-    }
-    excl += wave_sum_u64(sum);
-    if (closed) break;
-    base -= 64 * kLookbackK;
-  }
-  if (lane == 0) status_store(&status[t], kFlagPrefix | (excl + agg));
-  return excl;
-}
-
-// ---- split lookback: issue a round early, resolve later ---------------------
-//
-// The pipelined compressor issues the first round for a tile before doing
-// other work and resolves it afterwards, so the round trip of the status
-// reads overlaps that work.  Publishing the tile's own flags is left to the
-// caller.
-
-struct LookbackRound {
-  uint64_t s[kLookbackK];
-};
-
-// Issue the status reads of predecessors base, base-1, ..., base-64K+1.
-__device__ __forceinline__ void lookback_issue(const uint64_t* status, int64_t base, LookbackRound& r) {
+// Issue the reads of agg[lo + k*64 + lane] for the round starting at lo;
+// slots at or past hi read as a published zero.
+__device__ __forceinline__ void chain_issue(const uint32_t* agg, uint64_t lo, uint64_t hi, ChainRound& r) {
   const uint32_t lane = lane_id();
 #pragma unroll
-  for (int k = 0; k < kLookbackK; ++k) {
-    const int64_t idx = base - (int64_t)(k * 64 + lane);
-    r.s[k] = idx >= 0 ? status_load(&status[idx]) : kFlagPrefix;
+  for (int k = 0; k < kChainK; ++k) {
+    const uint64_t i = lo + (uint64_t)(k * 64) + lane;
+    r.w[k] = i < hi ? agg_load(agg, i) : 1u;
   }
 }
 
-// Exclusive prefix of tile t >= 1 whose first round (base t-1) is already in
-// r; further rounds are issued as needed.  Uniform result; *stuck as above.
-__device__ __forceinline__ uint64_t lookback_resolve(const uint64_t* status, uint32_t t, LookbackRound& r,
-                                                     bool* stuck) {
+// Sum over tiles [lo, hi) of dec(aggregate), where r holds the first round
+// (issued from lo).  Unpublished words are read again until they appear;
+// further rounds are issued as needed.  Uniform result; *stuck is set (and the
+// result meaningless) if the spin bound was hit.  Called by a whole wave.
+template <typename Dec>
+__device__ __forceinline__ uint64_t chain_sum(const uint32_t* agg, uint64_t lo, uint64_t hi, ChainRound& r,
+                                              bool* stuck, Dec dec) {
   const uint32_t lane = lane_id();
   *stuck = false;
-  uint64_t excl = 0;
-  int64_t base = (int64_t)t - 1;
+  uint64_t sum = 0, base = lo;
   uint32_t spins = 0;
   for (;;) {
-    bool wait = false, closed = false;
-    uint64_t sum = 0;
+    bool missing = false;
 #pragma unroll
-    for (int k = 0; k < kLookbackK; ++k) {
-      if (wait || closed) break;
-      const uint32_t flag = (uint32_t)(r.s[k] >> 62);
-      const uint64_t pmask = __ballot(flag == 2);
-      const uint64_t zmask = __ballot(flag == 0);
-      const int p = pmask ? __ffsll((unsigned long long)pmask) - 1 : 64;
-      const uint64_t need = p >= 63 ? ~0ull : ((2ull << p) - 1);
-      if (zmask & need) {
-        wait = true;
-      } else {
-        sum += (int)lane <= p ? (r.s[k] & kValueMask) : 0;
-        closed = p < 64;
-      }
-    }
-    if (wait && !closed) {
-      if (++spins > kLookbackSpinLimit) {
+    for (int k = 0; k < kChainK; ++k) missing |= r.w[k] == 0;
+    if (__ballot(missing)) {
+      if (++spins > kChainSpinLimit) {
         *stuck = true;
-        return excl;
+        return 0;
       }
       __builtin_amdgcn_s_sleep(1);
-      lookback_issue(status, base, r);
+#pragma unroll
+      for (int k = 0; k < kChainK; ++k)
+        if (r.w[k] == 0) r.w[k] = agg_load(agg, base + (uint64_t)(k * 64) + lane);
       continue;
     }
-    excl += wave_sum_u64(sum);
-    if (closed) return excl;
-    base -= 64 * kLookbackK;
-    lookback_issue(status, base, r);
+    uint64_t part = 0;
+#pragma unroll
+    for (int k = 0; k < kChainK; ++k) part += dec(r.w[k] - 1);
+    sum += wave_sum_u64(part);
+    base += 64 * kChainK;
+    if (base >= hi) return sum;
+    chain_issue(agg, base, hi, r);
   }
 }
 

@@ -23,10 +23,10 @@ __global__ void store_u64_kernel(uint64_t* p, uint64_t v) {
   if (threadIdx.x == 0 && blockIdx.x == 0) *p = v;
 }
 
-// Clear the ticket counter and the per-tile status words with a kernel (not a
-// memset node), so the sequence stays correct if a caller captures it.
+// Clear the ticket counter and the per-tile aggregate words with a kernel (not
+// a memset node), so the sequence stays correct if a caller captures it.
 static hipError_t clear_workspace(void* ws, uint64_t tiles, hipStream_t s) {
-  const uint64_t words = (kWsHeader + 8 * tiles) / 8;
+  const uint64_t words = (kWsHeader + 4 * tiles + 7) / 8;
   uint64_t blocks = (words + 255) / 256;
   if (blocks > 2048) blocks = 2048;
   fill_zero_u64_kernel<<<(unsigned)blocks, 256, 0, s>>>(static_cast<uint64_t*>(ws), words);
@@ -34,8 +34,8 @@ static hipError_t clear_workspace(void* ws, uint64_t tiles, hipStream_t s) {
 }
 
 static uint32_t* ws_counter(void* ws) { return static_cast<uint32_t*>(ws); }
-static uint64_t* ws_status(void* ws) {
-  return reinterpret_cast<uint64_t*>(static_cast<uint8_t*>(ws) + kWsHeader);
+static uint32_t* ws_agg(void* ws) {
+  return reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + kWsHeader);
 }
 
 uint64_t zvc_tiles(int esz, uint64_t n) {
@@ -84,7 +84,7 @@ static hipError_t zvc_compress_t(const void* src, uint64_t n, void* dst, uint64_
   const uint64_t res = resident_groups(reinterpret_cast<const void*>(kern), kCBlock);
   const unsigned grid = (unsigned)(tiles < res ? tiles : res);
   kern<<<grid, kCBlock, 0, s>>>(static_cast<const uint8_t*>(src), n, static_cast<uint8_t*>(dst), out_bytes,
-                                ws_counter(ws), ws_status(ws), (uint32_t)tiles);
+                                ws_counter(ws), ws_agg(ws), (uint32_t)tiles);
   return hipGetLastError();
 }
 
@@ -170,7 +170,7 @@ static hipError_t rle_compress_t(const void* src, uint64_t n, void* dst, uint64_
   const uint64_t res = resident_groups(reinterpret_cast<const void*>(kern), block);
   const unsigned grid = (unsigned)(tiles < res ? tiles : res);
   kern<<<grid, block, 0, s>>>(static_cast<const uint8_t*>(src), n, static_cast<uint8_t*>(dst), out_bytes,
-                              ws_counter(ws), ws_status(ws), (uint32_t)tiles);
+                              ws_counter(ws), ws_agg(ws), (uint32_t)tiles);
   return hipGetLastError();
 }
 

@@ -18,9 +18,10 @@
 //             ticket counter: load -> nonzero bits -> window masks in LDS (DPP
 //             OR) -> run boundaries = mask XOR (mask shifted by one element) ->
 //             per-window entry and nonzero counts -> run lengths (gaps between
-//             boundaries) and values staged in LDS -> one decoupled lookback
-//             over the packed pair (entries, nonzeros), overlapped with the
-//             next tile, gives the tile's byte offset -> realigned 16-byte
+//             boundaries) and values staged in LDS -> a chain sum over the
+//             packed (entries, nonzeros) aggregates of the tiles since the
+//             workgroup's previous tile, overlapped with the next tile, gives
+//             the tile's byte offset -> realigned 16-byte
 //             stores of the staged blocks and the tile's index entries.
 // decompress: the index gives each window's block offset directly (no scan)
 //             -> block read into LDS -> run starts by a wave prefix sum ->
@@ -66,15 +67,18 @@ __device__ __forceinline__ void lds_u16(uint8_t* base, uint32_t byte, uint32_t v
 // compress: persistent workgroups, one wavefront per window, lag-1 pipeline
 // ---------------------------------------------------------------------------
 //
-// The same pipeline as the ZVC compressor: a tile is NW windows (one per
-// wavefront), tiles come from a ticket counter, and iteration i of a
+// The same pipeline as the ZVC compressor, with wave 0 doing the offset chain
+// sums between its data work: a tile is NW windows (one per wavefront), tiles
+// come from a ticket counter (drawn one iteration ahead), and iteration i of a
 // workgroup classifies tile t (runs and values staged in LDS buffer i%2, its
-// aggregate published), prefetches the next ticket, resolves the lookback of
-// the previous tile tp (issued at the end of iteration i-1) and stores tp's
-// blocks and index entries.  The aggregate of a tile packs its run-entry count
-// and nonzero count as (entries << 31) | nonzeros; the stream limit keeps both
-// sums below 2^31, so packed sums never carry between the fields.  The
-// progress argument of the ZVC compressor applies unchanged.
+// aggregate published), prefetches the next tile, finishes the chain sum of
+// the previous tile tp (its first round issued at the end of iteration i-1)
+// and stores tp's blocks and index entries.  A published aggregate packs the
+// tile's run-entry and nonzero counts (each below 2^15) as
+// (entries << 15) | nonzeros; offsets are summed as (entries << 31) |
+// nonzeros, and the stream limit keeps both sums below 2^31, so the packed
+// sums never carry between the fields.  The progress argument of the ZVC
+// compressor applies unchanged.
 //
 // A window of L elements with v nonzeros has k <= min(v, L - v + 1) nonzero
 // runs and at most 2k + 1 runs, so its block is at most 4L + 8 bytes for
@@ -101,7 +105,7 @@ struct RleCLds {
   uint64_t excl;                        // packed exclusive prefix of the tile being stored
   uint64_t agg[2];                      // packed aggregate of the tile in stage[b]
   uint32_t pw[2][S::NW], vw[2][S::NW];  // per-window entries and nonzeros of that tile
-  uint32_t next;
+  uint32_t next[2];  // tickets handed between iterations (and the first two)
   bool stuck;
   uint32_t mask[S::NW * S::WPW];
   __attribute__((aligned(16))) uint8_t stage[2][S::STAGE];
@@ -123,11 +127,13 @@ __device__ __forceinline__ void rle_c_load_full(u32x4 (&v)[RleCShape<ESZ>::V], c
 
 template <int ESZ>
 __device__ __forceinline__ uint32_t rle_c_iteration(RleCLds<ESZ>& L, u32x4 (&cur)[RleCShape<ESZ>::V],
-                                                    u32x4 (&nxt)[RleCShape<ESZ>::V], LookbackRound& lr,
-                                                    uint32_t t, uint32_t tp, int buf, uint32_t full, uint64_t Wr,
+                                                    u32x4 (&nxt)[RleCShape<ESZ>::V], ChainRound& cr,
+                                                    uint64_t& chain_lo, uint64_t& pfx, uint32_t t, uint32_t tn,
+                                                    uint32_t tp, int buf, uint32_t full,
+                                                    uint64_t Wr,
                                                     const uint8_t* __restrict__ src, uint64_t n,
                                                     uint8_t* __restrict__ dst, uint64_t* __restrict__ out_bytes,
-                                                    uint64_t* __restrict__ status, uint32_t* __restrict__ counter,
+                                                    uint32_t* __restrict__ aggw, uint32_t* __restrict__ counter,
                                                     uint32_t num_tiles, int tid, int wave, int lane) {
   using S = RleCShape<ESZ>;
   constexpr int V = S::V;
@@ -135,7 +141,7 @@ __device__ __forceinline__ uint32_t rle_c_iteration(RleCLds<ESZ>& L, u32x4 (&cur
   const bool have_prev = tp < num_tiles;
   const uint64_t H = 8 * (Wr + 1);
 
-  uint32_t ticket = 0;
+  uint32_t ticket = 0;  // the ticket after tn, consumed at the end of the iteration
   if (have_cur && tid == S::BLOCK - 64)
     ticket = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
@@ -143,7 +149,7 @@ __device__ __forceinline__ uint32_t rle_c_iteration(RleCLds<ESZ>& L, u32x4 (&cur
   const uint64_t gw = (uint64_t)t * S::NW + wave;
   const uint64_t e_win = gw * S::E;
   const uint32_t Lw = have_cur && gw < Wr ? (uint32_t)(n - e_win < (uint64_t)S::E ? n - e_win : S::E) : 0u;
-  uint32_t ex[V], v_w = 0;  // ex[j]: nonzeros of the window before lane's vector j
+  uint32_t v_w = 0;  // nonzeros of this wave's window
   if (have_cur) {
     if (t >= full) {  // the one partial tile: load bounded, drain so nothing stays pending on cur
       uint32_t el = (uint32_t)lane * S::EPL;
@@ -157,15 +163,10 @@ __device__ __forceinline__ uint32_t rle_c_iteration(RleCLds<ESZ>& L, u32x4 (&cur
       const uint32_t bits = vec_nz_bits<ESZ>(cur[j]);
       const uint32_t m = group_or<S::LPW>(bits << ((lane % S::LPW) * S::EPL));
       if (lane % S::LPW == 0) wmask[j * (64 / S::LPW)] = m;
-      const uint32_t cnt = (uint32_t)__builtin_popcount(bits);
-      const uint32_t inc = wave_incl_scan(cnt);
-      ex[j] = v_w + inc - cnt;
-      v_w += read_lane(inc, 63);
+      v_w += read_lane(wave_incl_scan((uint32_t)__builtin_popcount(bits)), 63);
     }
   }
-  if (tid == S::BLOCK - 64) L.next = have_cur ? ticket : num_tiles;
   __syncthreads();
-  const uint32_t tn = __builtin_amdgcn_readfirstlane(L.next);  // uniform: keeps tile bases in SGPRs
 
   // run boundaries: lane g holds mask word g of the window
   const uint32_t g = (uint32_t)lane;
@@ -198,10 +199,9 @@ __device__ __forceinline__ uint32_t rle_c_iteration(RleCLds<ESZ>& L, u32x4 (&cur
       P += L.pw[buf][w];
       Vs += L.vw[buf][w];
     }
-    const uint64_t agg = ((uint64_t)P << 31) | Vs;
     if (tid == 0) {
-      L.agg[buf] = agg;
-      status_store(&status[t], (t == 0 ? kFlagPrefix : kFlagAggregate) | agg);
+      L.agg[buf] = ((uint64_t)P << 31) | Vs;
+      agg_publish(aggw, t, (P << 15) | Vs);
     }
     uint8_t* st = L.stage[buf] + blk;
     if (Lw) {
@@ -224,11 +224,16 @@ __device__ __forceinline__ uint32_t rle_c_iteration(RleCLds<ESZ>& L, u32x4 (&cur
         lds_u16(st, 2 * (r_w - 1), Lw - tau_last);
         if (p_w > r_w) lds_u16(st, 2 * r_w, 0);
       }
-      // values follow the runs
+      // values follow the runs; the counts are scanned again here rather
+      // than held in registers across the barriers
+      uint32_t vb = 0;
 #pragma unroll
       for (int j = 0; j < V; ++j) {
         const uint32_t bits = vec_nz_bits<ESZ>(cur[j]);
-        uint32_t pos = 2 * p_w + ESZ * ex[j];
+        const uint32_t cnt = (uint32_t)__builtin_popcount(bits);
+        const uint32_t inc = wave_incl_scan(cnt);
+        uint32_t pos = 2 * p_w + ESZ * (vb + inc - cnt);
+        vb += read_lane(inc, 63);
 #pragma unroll
         for (int k2 = 0; k2 < S::EPL; ++k2) {
           if ((bits >> k2) & 1u) {
@@ -242,12 +247,14 @@ __device__ __forceinline__ uint32_t rle_c_iteration(RleCLds<ESZ>& L, u32x4 (&cur
   }
   if (wave == 0 && have_prev) {
     bool stuck = false;
-    const uint64_t X = tp > 0 ? lookback_resolve(status, tp, lr, &stuck) : 0;
+    const uint64_t X = pfx + chain_sum(aggw, chain_lo, tp, cr, &stuck, [](uint32_t v) {
+                         return ((uint64_t)(v >> 15) << 31) | (v & 0x7FFFu);
+                       });
     if (lane == 0) {
       L.excl = X;
       L.stuck = stuck;
-      if (tp > 0) status_store(&status[tp], kFlagPrefix | (X + L.agg[buf ^ 1]));
     }
+    pfx = X + L.agg[buf ^ 1];  // tp's inclusive prefix
   }
   __syncthreads();
 
@@ -271,24 +278,29 @@ __device__ __forceinline__ uint32_t rle_c_iteration(RleCLds<ESZ>& L, u32x4 (&cur
         reinterpret_cast<uint32_t*>(dst + 4 * (Wr + 1))[w] = (uint32_t)(VX + vr);
       }
     }
-    // Only the last tile reports the size; its lookback passes over every
-    // tile, so if any lookback could not finish, neither could this one.
+    // Only the last tile reports the size.  A chain sum that hit the spin
+    // bound leaves every later offset of its workgroup wrong, and the last
+    // tile's workgroup waits on every tile, so it reports such a failure.
     if (tp == num_tiles - 1 && tid == 0) {
       reinterpret_cast<uint32_t*>(dst)[Wr] = (uint32_t)(RX + P);
       reinterpret_cast<uint32_t*>(dst + 4 * (Wr + 1))[Wr] = (uint32_t)(VX + Vs);
       *out_bytes = L.stuck ? kSizeInternalError : O + span;
     }
   }
-  if (wave == 0 && have_cur && t > 0) lookback_issue(status, (int64_t)t - 1, lr);
+  if (wave == 0 && have_cur) {
+    chain_lo = have_prev ? (uint64_t)tp + 1 : 0;
+    chain_issue(aggw, chain_lo, t, cr);
+  }
+  if (tid == S::BLOCK - 64) L.next[0] = have_cur ? ticket : num_tiles;
   __syncthreads();
-  return tn;
+  return __builtin_amdgcn_readfirstlane(L.next[0]);  // uniform: keeps tile bases in SGPRs
 }
 
 template <int ESZ>
 __global__ __launch_bounds__(RleCShape<ESZ>::BLOCK) void rle_compress_kernel(
     const uint8_t* __restrict__ src, uint64_t n, uint8_t* __restrict__ dst,
     uint64_t* __restrict__ out_bytes, uint32_t* __restrict__ counter,
-    uint64_t* __restrict__ status, uint32_t num_tiles) {
+    uint32_t* __restrict__ aggw, uint32_t num_tiles) {
   using S = RleCShape<ESZ>;
   __shared__ RleCLds<ESZ> L;
   const int tid = threadIdx.x;
@@ -296,24 +308,35 @@ __global__ __launch_bounds__(RleCShape<ESZ>::BLOCK) void rle_compress_kernel(
   const int wave = tid >> 6;
   const uint64_t Wr = (n + S::E - 1) / S::E;
   const uint32_t full = (uint32_t)(n / S::TE);  // tiles with no element past n
-  if (tid == 0) L.next = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0 || tid == S::BLOCK - 64)
+    L.next[tid == 0 ? 0 : 1] = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
-  uint32_t t = __builtin_amdgcn_readfirstlane(L.next);
+  uint32_t t = __builtin_amdgcn_readfirstlane(L.next[0]);
+  uint32_t tn = __builtin_amdgcn_readfirstlane(L.next[1]);
+  if (tn < t) {  // classify the smaller ticket first
+    const uint32_t x = t;
+    t = tn;
+    tn = x;
+  }
   uint32_t tp = num_tiles;
   u32x4 ra[S::V], rb[S::V];
-  LookbackRound lr;
+  ChainRound cr;          // wave 0: chain sum in flight
+  uint64_t chain_lo = 0;  // wave 0: first tile of that sum
+  uint64_t pfx = 0;       // wave 0: packed inclusive prefix of the last resolved tile
   if (t < full) rle_c_load_full<ESZ>(ra, src, t, wave, lane);
   for (;;) {
-    uint32_t tn = rle_c_iteration<ESZ>(L, ra, rb, lr, t, tp, 0, full, Wr, src, n, dst, out_bytes, status, counter,
-                                       num_tiles, tid, wave, lane);
+    uint32_t tnn = rle_c_iteration<ESZ>(L, ra, rb, cr, chain_lo, pfx, t, tn, tp, 0, full, Wr, src, n, dst, out_bytes,
+                                        aggw, counter, num_tiles, tid, wave, lane);
     if (t >= num_tiles) break;
     tp = t;
     t = tn;
-    tn = rle_c_iteration<ESZ>(L, rb, ra, lr, t, tp, 1, full, Wr, src, n, dst, out_bytes, status, counter,
-                              num_tiles, tid, wave, lane);
+    tn = tnn;
+    tnn = rle_c_iteration<ESZ>(L, rb, ra, cr, chain_lo, pfx, t, tn, tp, 1, full, Wr, src, n, dst, out_bytes, aggw,
+                               counter, num_tiles, tid, wave, lane);
     if (t >= num_tiles) break;
     tp = t;
     t = tn;
+    tn = tnn;
   }
 }
 
