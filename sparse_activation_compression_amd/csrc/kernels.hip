@@ -13,10 +13,10 @@ namespace cdma {
 #endif
 constexpr int kZvcV = CDMA_ZVC_V;
 
-__global__ void fill_zero_u64_kernel(uint64_t* __restrict__ p, uint64_t count) {
-  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count;
-       i += (uint64_t)gridDim.x * blockDim.x)
-    p[i] = 0;
+__global__ void fill_zero_u64_kernel(uint64_t* __restrict__ p, uint64_t count, uint64_t* __restrict__ extra) {
+  const uint64_t i0 = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i0 == 0 && extra) *extra = 0;
+  for (uint64_t i = i0; i < count; i += (uint64_t)gridDim.x * blockDim.x) p[i] = 0;
 }
 
 __global__ void store_u64_kernel(uint64_t* p, uint64_t v) {
@@ -25,11 +25,13 @@ __global__ void store_u64_kernel(uint64_t* p, uint64_t v) {
 
 // Clear the ticket counter and the per-tile aggregate words with a kernel (not
 // a memset node), so the sequence stays correct if a caller captures it.
-static hipError_t clear_workspace(void* ws, uint64_t tiles, hipStream_t s) {
+// The compressors report the stream size with atomic max, so *out_bytes is
+// cleared here too.
+static hipError_t clear_workspace(void* ws, uint64_t tiles, uint64_t* out_bytes, hipStream_t s) {
   const uint64_t words = (kWsHeader + 4 * tiles + 7) / 8;
   uint64_t blocks = (words + 255) / 256;
   if (blocks > 2048) blocks = 2048;
-  fill_zero_u64_kernel<<<(unsigned)blocks, 256, 0, s>>>(static_cast<uint64_t*>(ws), words);
+  fill_zero_u64_kernel<<<(unsigned)blocks, 256, 0, s>>>(static_cast<uint64_t*>(ws), words, out_bytes);
   return hipGetLastError();
 }
 
@@ -77,7 +79,7 @@ template <int ESZ>
 static hipError_t zvc_compress_t(const void* src, uint64_t n, void* dst, uint64_t* out_bytes, void* ws,
                                  hipStream_t s) {
   const uint64_t tiles = zvc_compress_tiles(ESZ, n);
-  hipError_t e = clear_workspace(ws, tiles, s);
+  hipError_t e = clear_workspace(ws, tiles, out_bytes, s);
   if (e != hipSuccess) return e;
   // persistent grid: about one workgroup per CU, tiles handed out by ticket
   auto kern = zvc_compress_kernel<ESZ>;
@@ -164,7 +166,7 @@ static hipError_t rle_compress_t(const void* src, uint64_t n, void* dst, uint64_
                                  hipStream_t s) {
   constexpr int block = RleCShape<ESZ>::BLOCK;
   const uint64_t tiles = rle_compress_tiles(ESZ, n);
-  hipError_t e = clear_workspace(ws, tiles, s);
+  hipError_t e = clear_workspace(ws, tiles, out_bytes, s);
   if (e != hipSuccess) return e;
   auto kern = rle_compress_kernel<ESZ>;
   const uint64_t res = resident_groups(reinterpret_cast<const void*>(kern), block);

@@ -64,21 +64,15 @@ __device__ __forceinline__ void lds_u16(uint8_t* base, uint32_t byte, uint32_t v
 }
 
 // ---------------------------------------------------------------------------
-// compress: persistent workgroups, one wavefront per window, lag-1 pipeline
+// compress: persistent workgroups, one data wavefront per window
 // ---------------------------------------------------------------------------
 //
-// The same pipeline as the ZVC compressor, with wave 0 doing the offset chain
-// sums between its data work: a tile is NW windows (one per wavefront), tiles
-// come from a ticket counter (drawn one iteration ahead), and iteration i of a
-// workgroup classifies tile t (runs and values staged in LDS buffer i%2, its
-// aggregate published), prefetches the next tile, finishes the chain sum of
-// the previous tile tp (its first round issued at the end of iteration i-1)
-// and stores tp's blocks and index entries.  A published aggregate packs the
-// tile's run-entry and nonzero counts (each below 2^15) as
-// (entries << 15) | nonzeros; offsets are summed as (entries << 31) |
-// nonzeros, and the stream limit keeps both sums below 2^31, so the packed
-// sums never carry between the fields.  The progress argument of the ZVC
-// compressor applies unchanged.
+// The same pipeline as the ZVC compressor: a tile is NW windows, one per data
+// wavefront, and the last wavefront is the control wave (tickets and offset
+// chain sums).  A published aggregate packs the tile's run-entry and nonzero
+// counts (each below 2^15) as (entries << 15) | nonzeros; offsets are summed
+// as (entries << 31) | nonzeros, and the stream limit keeps both sums below
+// 2^31, so the packed sums never carry between the fields.
 //
 // A window of L elements with v nonzeros has k <= min(v, L - v + 1) nonzero
 // runs and at most 2k + 1 runs, so its block is at most 4L + 8 bytes for
@@ -87,7 +81,7 @@ __device__ __forceinline__ void lds_u16(uint8_t* base, uint32_t byte, uint32_t v
 template <int ESZ>
 struct RleCShape {
   static constexpr int BLOCK = ESZ == 4 ? 1024 : 512;  // threads (16-bit blocks stage up to 1.5x)
-  static constexpr int NW = BLOCK / 64;                 // windows per tile
+  static constexpr int NW = BLOCK / 64 - 1;             // windows per tile: one per data wave
   static constexpr int V = 4;
   static constexpr int EPL = 16 / ESZ;
   static constexpr int LPW = 32 / EPL;
@@ -104,9 +98,10 @@ struct RleCLds {
   using S = RleCShape<ESZ>;
   uint64_t excl;                        // packed exclusive prefix of the tile being stored
   uint64_t agg[2];                      // packed aggregate of the tile in stage[b]
-  uint32_t pw[2][S::NW], vw[2][S::NW];  // per-window entries and nonzeros of that tile
-  uint32_t next[2];  // tickets handed between iterations (and the first two)
-  bool stuck;
+  uint32_t pw[S::NW], vw[S::NW];        // per-window entries and nonzeros (read between B1 and B2)
+  uint32_t ipw[2][S::NW], ivw[2][S::NW];  // their exclusive in-tile prefixes, for the tile in stage[b]
+  uint32_t next;                        // ticket handed from the control wave to the data waves
+  uint32_t init[3];                     // the first three tickets
   uint32_t mask[S::NW * S::WPW];
   __attribute__((aligned(16))) uint8_t stage[2][S::STAGE];
 };
@@ -125,12 +120,18 @@ __device__ __forceinline__ void rle_c_load_full(u32x4 (&v)[RleCShape<ESZ>::V], c
   for (int j = 0; j < S::V; ++j) v[j] = ld_stream(reinterpret_cast<const u32x4*>(p + o + j * 1024));
 }
 
+// Packed (entries << 15 | nonzeros) aggregate word -> (entries << 31 | nonzeros).
+struct RleAggDec {
+  __device__ uint64_t operator()(uint32_t v) const { return ((uint64_t)(v >> 15) << 31) | (v & 0x7FFFu); }
+};
+
+// One pipeline iteration (the structure of the ZVC compressor's).  Returns
+// the ticket the data waves prefetch in the next iteration.
 template <int ESZ>
 __device__ __forceinline__ uint32_t rle_c_iteration(RleCLds<ESZ>& L, u32x4 (&cur)[RleCShape<ESZ>::V],
                                                     u32x4 (&nxt)[RleCShape<ESZ>::V], ChainRound& cr,
-                                                    uint64_t& chain_lo, uint64_t& pfx, uint32_t t, uint32_t tn,
-                                                    uint32_t tp, int buf, uint32_t full,
-                                                    uint64_t Wr,
+                                                    uint64_t& chain_lo, uint64_t& pfx, uint32_t& pend, uint32_t t,
+                                                    uint32_t tn, uint32_t tp, int buf, uint32_t full, uint64_t Wr,
                                                     const uint8_t* __restrict__ src, uint64_t n,
                                                     uint8_t* __restrict__ dst, uint64_t* __restrict__ out_bytes,
                                                     uint32_t* __restrict__ aggw, uint32_t* __restrict__ counter,
@@ -139,18 +140,18 @@ __device__ __forceinline__ uint32_t rle_c_iteration(RleCLds<ESZ>& L, u32x4 (&cur
   constexpr int V = S::V;
   const bool have_cur = t < num_tiles;
   const bool have_prev = tp < num_tiles;
+  const bool data = wave < S::NW;
   const uint64_t H = 8 * (Wr + 1);
 
-  uint32_t ticket = 0;  // the ticket after tn, consumed at the end of the iteration
-  if (have_cur && tid == S::BLOCK - 64)
-    ticket = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-
-  // classify this wave's window
+  // data waves: classify this wave's window and count its runs.  The window's
+  // mask words are written and read by this wave only, so a wave-level fence
+  // orders them.
   const uint64_t gw = (uint64_t)t * S::NW + wave;
   const uint64_t e_win = gw * S::E;
-  const uint32_t Lw = have_cur && gw < Wr ? (uint32_t)(n - e_win < (uint64_t)S::E ? n - e_win : S::E) : 0u;
-  uint32_t v_w = 0;  // nonzeros of this wave's window
-  if (have_cur) {
+  const uint32_t Lw = data && have_cur && gw < Wr ? (uint32_t)(n - e_win < (uint64_t)S::E ? n - e_win : S::E) : 0u;
+  const uint32_t g = (uint32_t)lane;  // lane g holds mask word g of the window
+  uint32_t T = 0, texcl = 0, r_w = 0, p_w = 0;
+  if (data && have_cur) {
     if (t >= full) {  // the one partial tile: load bounded, drain so nothing stays pending on cur
       uint32_t el = (uint32_t)lane * S::EPL;
       asm volatile("" : "+v"(el));
@@ -158,6 +159,7 @@ __device__ __forceinline__ uint32_t rle_c_iteration(RleCLds<ESZ>& L, u32x4 (&cur
       __builtin_amdgcn_s_waitcnt(0);
     }
     uint32_t* wmask = L.mask + wave * S::WPW + lane / S::LPW;
+    uint32_t v_w = 0;
 #pragma unroll
     for (int j = 0; j < V; ++j) {
       const uint32_t bits = vec_nz_bits<ESZ>(cur[j]);
@@ -165,13 +167,9 @@ __device__ __forceinline__ uint32_t rle_c_iteration(RleCLds<ESZ>& L, u32x4 (&cur
       if (lane % S::LPW == 0) wmask[j * (64 / S::LPW)] = m;
       v_w += read_lane(wave_incl_scan((uint32_t)__builtin_popcount(bits)), 63);
     }
-  }
-  __syncthreads();
-
-  // run boundaries: lane g holds mask word g of the window
-  const uint32_t g = (uint32_t)lane;
-  uint32_t T = 0, texcl = 0, r_w = 0, p_w = 0;
-  if (have_cur) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     if (g < (uint32_t)S::WPW && 32 * g < Lw) {
       const uint32_t m = L.mask[wave * S::WPW + g];
       const uint32_t prev = g ? L.mask[wave * S::WPW + g - 1] : 0u;
@@ -185,115 +183,117 @@ __device__ __forceinline__ uint32_t rle_c_iteration(RleCLds<ESZ>& L, u32x4 (&cur
     r_w = Lw ? 1 + read_lane(tinc, 63) : 0u;
     p_w = ESZ == 4 ? r_w + (r_w & 1) : r_w;
     if (lane == 0) {
-      L.pw[buf][wave] = p_w;
-      L.vw[buf][wave] = v_w;
+      L.pw[wave] = p_w;
+      L.vw[wave] = v_w;
     }
   }
   __syncthreads();
 
-  if (have_cur) {
-    uint32_t P = 0, Vs = 0, blk = 0;
-#pragma unroll
-    for (int w = 0; w < S::NW; ++w) {
-      if (w == wave) blk = 2 * P + ESZ * Vs;
-      P += L.pw[buf][w];
-      Vs += L.vw[buf][w];
-    }
-    if (tid == 0) {
-      L.agg[buf] = ((uint64_t)P << 31) | Vs;
-      agg_publish(aggw, t, (P << 15) | Vs);
-    }
-    uint8_t* st = L.stage[buf] + blk;
-    if (Lw) {
-      // run lengths: the gap from the previous boundary (0 at the window start)
-      const uint32_t lastpos = T ? 32 * g + 31 - (uint32_t)__builtin_clz(T) : 0u;
-      const uint32_t imax = wave_incl_max(lastpos);
-      const uint32_t before = __shfl_up(imax, 1, 64);
-      uint32_t prev = lane ? before : 0u;
-      const uint32_t tau_last = read_lane(imax, 63);
-      uint32_t x = T, k = texcl;
-      while (x) {
-        const uint32_t b = (uint32_t)__builtin_ctz(x);
-        x &= x - 1;
-        const uint32_t pos = 32 * g + b;
-        lds_u16(st, 2 * k, pos - prev);
-        prev = pos;
-        ++k;
+  if (data) {
+    if (have_cur) {
+      uint32_t P = 0, Vs = 0;  // entries and nonzeros of the windows before this one
+      for (int w = 0; w < wave; ++w) {
+        P += L.pw[w];
+        Vs += L.vw[w];
       }
       if (lane == 0) {
-        lds_u16(st, 2 * (r_w - 1), Lw - tau_last);
-        if (p_w > r_w) lds_u16(st, 2 * r_w, 0);
+        L.ipw[buf][wave] = P;
+        L.ivw[buf][wave] = Vs;
       }
-      // values follow the runs; the counts are scanned again here rather
-      // than held in registers across the barriers
-      uint32_t vb = 0;
+      uint8_t* st = L.stage[buf] + 2 * P + ESZ * Vs;
+      if (Lw) {
+        // run lengths: the gap from the previous boundary (0 at the window start)
+        const uint32_t lastpos = T ? 32 * g + 31 - (uint32_t)__builtin_clz(T) : 0u;
+        const uint32_t imax = wave_incl_max(lastpos);
+        const uint32_t before = __shfl_up(imax, 1, 64);
+        uint32_t prev = lane ? before : 0u;
+        const uint32_t tau_last = read_lane(imax, 63);
+        uint32_t x = T, k = texcl;
+        while (x) {
+          const uint32_t b = (uint32_t)__builtin_ctz(x);
+          x &= x - 1;
+          const uint32_t pos = 32 * g + b;
+          lds_u16(st, 2 * k, pos - prev);
+          prev = pos;
+          ++k;
+        }
+        if (lane == 0) {
+          lds_u16(st, 2 * (r_w - 1), Lw - tau_last);
+          if (p_w > r_w) lds_u16(st, 2 * r_w, 0);
+        }
+        // values follow the runs; the counts are scanned again here rather
+        // than held in registers across the barrier
+        uint32_t vb = 0;
 #pragma unroll
-      for (int j = 0; j < V; ++j) {
-        const uint32_t bits = vec_nz_bits<ESZ>(cur[j]);
-        const uint32_t cnt = (uint32_t)__builtin_popcount(bits);
-        const uint32_t inc = wave_incl_scan(cnt);
-        uint32_t pos = 2 * p_w + ESZ * (vb + inc - cnt);
-        vb += read_lane(inc, 63);
+        for (int j = 0; j < V; ++j) {
+          const uint32_t bits = vec_nz_bits<ESZ>(cur[j]);
+          const uint32_t cnt = (uint32_t)__builtin_popcount(bits);
+          const uint32_t inc = wave_incl_scan(cnt);
+          uint32_t pos = 2 * p_w + ESZ * (vb + inc - cnt);
+          vb += read_lane(inc, 63);
 #pragma unroll
-        for (int k2 = 0; k2 < S::EPL; ++k2) {
-          if ((bits >> k2) & 1u) {
-            store_elem<ESZ>(st + pos, vec_elem<ESZ>(cur[j], k2));
-            pos += ESZ;
+          for (int k2 = 0; k2 < S::EPL; ++k2) {
+            if ((bits >> k2) & 1u) {
+              store_elem<ESZ>(st + pos, vec_elem<ESZ>(cur[j], k2));
+              pos += ESZ;
+            }
           }
         }
       }
+      if (tn < full) rle_c_load_full<ESZ>(nxt, src, tn, wave, lane);
     }
-    if (tn < full) rle_c_load_full<ESZ>(nxt, src, tn, wave, lane);
-  }
-  if (wave == 0 && have_prev) {
-    bool stuck = false;
-    const uint64_t X = pfx + chain_sum(aggw, chain_lo, tp, cr, &stuck, [](uint32_t v) {
-                         return ((uint64_t)(v >> 15) << 31) | (v & 0x7FFFu);
-                       });
-    if (lane == 0) {
-      L.excl = X;
-      L.stuck = stuck;
+  } else {
+    // control wave (see the ZVC compressor)
+    if (lane == 0) L.next = pend;
+    if (have_cur) {
+      const uint32_t pl = lane < S::NW ? L.pw[lane] : 0u;
+      const uint32_t vl = lane < S::NW ? L.vw[lane] : 0u;
+      const uint32_t P = read_lane(wave_incl_scan(pl), 63), Vs = read_lane(wave_incl_scan(vl), 63);
+      if (lane == 0) {
+        L.agg[buf] = ((uint64_t)P << 31) | Vs;
+        agg_publish(aggw, t, (P << 15) | Vs);
+      }
     }
-    pfx = X + L.agg[buf ^ 1];  // tp's inclusive prefix
+    if (have_prev) {
+      bool stuck = false;
+      const uint64_t X = pfx + chain_sum(aggw, chain_lo, tp, cr, &stuck, RleAggDec());
+      if (lane == 0) {
+        L.excl = X;
+        if (stuck) atomicMax(reinterpret_cast<unsigned long long*>(out_bytes), kSizeInternalError);
+      }
+      pfx = X + L.agg[buf ^ 1];  // tp's inclusive prefix
+    }
   }
   __syncthreads();
 
-  if (have_prev) {
-    const int pb = buf ^ 1;
-    const uint64_t agg = L.agg[pb];
-    const uint32_t P = (uint32_t)(agg >> 31), Vs = (uint32_t)(agg & kLow31);
-    const uint64_t RX = L.excl >> 31, VX = L.excl & kLow31;
-    const uint64_t O = H + 2 * RX + (uint64_t)ESZ * VX;  // first byte of the tile's blocks
-    const uint32_t span = 2 * P + ESZ * Vs;
-    store_staged<2, S::BLOCK>(L.stage[pb], span, O, dst, tid);
-    if (tid < S::NW) {
-      const uint64_t w = (uint64_t)tp * S::NW + tid;
-      if (w < Wr) {
-        uint32_t pr = 0, vr = 0;
-        for (int k = 0; k < tid; ++k) {
-          pr += L.pw[pb][k];
-          vr += L.vw[pb][k];
+  if (data) {
+    if (have_prev) {
+      const int pb = buf ^ 1;
+      const uint64_t agg = L.agg[pb];
+      const uint32_t P = (uint32_t)(agg >> 31), Vs = (uint32_t)(agg & kLow31);
+      const uint64_t RX = L.excl >> 31, VX = L.excl & kLow31;
+      const uint64_t O = H + 2 * RX + (uint64_t)ESZ * VX;  // first byte of the tile's blocks
+      const uint32_t span = 2 * P + ESZ * Vs;
+      store_staged<2, S::NW * 64>(L.stage[pb], span, O, dst, tid);
+      if (tid < S::NW) {
+        const uint64_t w = (uint64_t)tp * S::NW + tid;
+        if (w < Wr) {
+          reinterpret_cast<uint32_t*>(dst)[w] = (uint32_t)(RX + L.ipw[pb][tid]);
+          reinterpret_cast<uint32_t*>(dst + 4 * (Wr + 1))[w] = (uint32_t)(VX + L.ivw[pb][tid]);
         }
-        reinterpret_cast<uint32_t*>(dst)[w] = (uint32_t)(RX + pr);
-        reinterpret_cast<uint32_t*>(dst + 4 * (Wr + 1))[w] = (uint32_t)(VX + vr);
+      }
+      if (tp == num_tiles - 1 && tid == 0) {
+        reinterpret_cast<uint32_t*>(dst)[Wr] = (uint32_t)(RX + P);
+        reinterpret_cast<uint32_t*>(dst + 4 * (Wr + 1))[Wr] = (uint32_t)(VX + Vs);
+        atomicMax(reinterpret_cast<unsigned long long*>(out_bytes), O + span);
       }
     }
-    // Only the last tile reports the size.  A chain sum that hit the spin
-    // bound leaves every later offset of its workgroup wrong, and the last
-    // tile's workgroup waits on every tile, so it reports such a failure.
-    if (tp == num_tiles - 1 && tid == 0) {
-      reinterpret_cast<uint32_t*>(dst)[Wr] = (uint32_t)(RX + P);
-      reinterpret_cast<uint32_t*>(dst + 4 * (Wr + 1))[Wr] = (uint32_t)(VX + Vs);
-      *out_bytes = L.stuck ? kSizeInternalError : O + span;
-    }
-  }
-  if (wave == 0 && have_cur) {
+  } else if (have_cur) {
     chain_lo = have_prev ? (uint64_t)tp + 1 : 0;
     chain_issue(aggw, chain_lo, t, cr);
+    if (lane == 0) pend = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  if (tid == S::BLOCK - 64) L.next[0] = have_cur ? ticket : num_tiles;
-  __syncthreads();
-  return __builtin_amdgcn_readfirstlane(L.next[0]);  // uniform: keeps tile bases in SGPRs
+  return __builtin_amdgcn_readfirstlane(L.next);  // uniform: keeps tile bases in SGPRs
 }
 
 template <int ESZ>
@@ -308,31 +308,31 @@ __global__ __launch_bounds__(RleCShape<ESZ>::BLOCK) void rle_compress_kernel(
   const int wave = tid >> 6;
   const uint64_t Wr = (n + S::E - 1) / S::E;
   const uint32_t full = (uint32_t)(n / S::TE);  // tiles with no element past n
-  if (tid == 0 || tid == S::BLOCK - 64)
-    L.next[tid == 0 ? 0 : 1] = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid < 3 * 64 && lane == 0)
+    L.init[wave] = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
-  uint32_t t = __builtin_amdgcn_readfirstlane(L.next[0]);
-  uint32_t tn = __builtin_amdgcn_readfirstlane(L.next[1]);
-  if (tn < t) {  // classify the smaller ticket first
-    const uint32_t x = t;
-    t = tn;
-    tn = x;
-  }
+  const uint32_t a = __builtin_amdgcn_readfirstlane(L.init[0]);
+  const uint32_t b = __builtin_amdgcn_readfirstlane(L.init[1]);
+  const uint32_t c = __builtin_amdgcn_readfirstlane(L.init[2]);
+  const uint32_t lo = min(a, min(b, c)), hi = max(a, max(b, c));
+  uint32_t t = lo;
+  uint32_t tn = a + b + c - lo - hi;
+  uint32_t pend = hi;     // control wave: ticket to hand over next
   uint32_t tp = num_tiles;
   u32x4 ra[S::V], rb[S::V];
-  ChainRound cr;          // wave 0: chain sum in flight
-  uint64_t chain_lo = 0;  // wave 0: first tile of that sum
-  uint64_t pfx = 0;       // wave 0: packed inclusive prefix of the last resolved tile
-  if (t < full) rle_c_load_full<ESZ>(ra, src, t, wave, lane);
+  ChainRound cr;          // control wave: chain sum in flight
+  uint64_t chain_lo = 0;  // control wave: first tile of that sum
+  uint64_t pfx = 0;       // control wave: packed inclusive prefix of the last resolved tile
+  if (wave < S::NW && t < full) rle_c_load_full<ESZ>(ra, src, t, wave, lane);
   for (;;) {
-    uint32_t tnn = rle_c_iteration<ESZ>(L, ra, rb, cr, chain_lo, pfx, t, tn, tp, 0, full, Wr, src, n, dst, out_bytes,
-                                        aggw, counter, num_tiles, tid, wave, lane);
+    uint32_t tnn = rle_c_iteration<ESZ>(L, ra, rb, cr, chain_lo, pfx, pend, t, tn, tp, 0, full, Wr, src, n, dst,
+                                        out_bytes, aggw, counter, num_tiles, tid, wave, lane);
     if (t >= num_tiles) break;
     tp = t;
     t = tn;
     tn = tnn;
-    tnn = rle_c_iteration<ESZ>(L, rb, ra, cr, chain_lo, pfx, t, tn, tp, 1, full, Wr, src, n, dst, out_bytes, aggw,
-                               counter, num_tiles, tid, wave, lane);
+    tnn = rle_c_iteration<ESZ>(L, rb, ra, cr, chain_lo, pfx, pend, t, tn, tp, 1, full, Wr, src, n, dst, out_bytes,
+                               aggw, counter, num_tiles, tid, wave, lane);
     if (t >= num_tiles) break;
     tp = t;
     t = tn;

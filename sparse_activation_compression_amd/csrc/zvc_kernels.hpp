@@ -139,6 +139,11 @@ __device__ __forceinline__ uint32_t segment_bases(const uint32_t* s_tot, int wav
 //                 (aggregates of the tiles between this workgroup's previous
 //                 tile and tp, read one iteration earlier) -> B2 -> issue the
 //                 first round of t's chain sum and draw a ticket.
+// The size is reported with 64-bit atomic max operations on a word cleared
+// before the launch: the last tile writes the stream size and a control wave
+// whose chain sum hit the spin bound writes the all-ones error value, which
+// wins whatever the order.  (Such a sum returns an under-estimate, so every
+// store still lands inside the stream's bounds.)
 // Progress: a ticket is drawn only by a running workgroup, which classifies
 // its tickets in increasing order, and a tile's aggregate is published in the
 // iteration that classifies it, before that iteration waits for anything.
@@ -174,7 +179,6 @@ struct ZvcCLds {
   uint32_t total[2];     // nonzeros held in stage[b]
   uint32_t next;         // ticket handed from the control wave to the data waves
   uint32_t init[3];      // the first three tickets
-  bool stuck;
   uint32_t tot[S::SEG];
   uint32_t mask[S::WPT];
   __attribute__((aligned(16))) uint8_t stage[2][S::STAGE];
@@ -321,7 +325,7 @@ __device__ __forceinline__ uint32_t zvc_c_iteration(ZvcCLds<ESZ>& L, u32x4 (&cur
       const uint64_t X = P + chain_sum(agg, chain_lo, tp, cr, &stuck, [](uint32_t v) { return (uint64_t)v; });
       if (lane == 0) {
         L.excl = X;
-        L.stuck = stuck;
+        if (stuck) atomicMax(reinterpret_cast<unsigned long long*>(out_bytes), kSizeInternalError);
       }
       P = X + L.total[buf ^ 1];  // tp's inclusive prefix
     }
@@ -333,9 +337,8 @@ __device__ __forceinline__ uint32_t zvc_c_iteration(ZvcCLds<ESZ>& L, u32x4 (&cur
       const uint32_t T = L.total[buf ^ 1];
       const uint64_t A = 4 * W + (uint64_t)ESZ * L.excl;
       store_staged<ESZ, kDThreads>(L.stage[buf ^ 1], ESZ * T, A, dst, tid);
-      // Only the last tile reports the size; its lookback passes over every
-      // tile, so if any lookback could not finish, neither could this one.
-      if (tp == num_tiles - 1 && tid == 0) *out_bytes = L.stuck ? kSizeInternalError : A + (uint64_t)ESZ * T;
+      if (tp == num_tiles - 1 && tid == 0)
+        atomicMax(reinterpret_cast<unsigned long long*>(out_bytes), A + (uint64_t)ESZ * T);
     }
   } else if (have_cur) {
     // the first round of t's chain sum goes out while the data waves store,
