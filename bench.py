@@ -40,7 +40,8 @@ N_ELEMS = 1 << 30
 CHUNK = 1 << 24
 SLOTS = 3
 CPU_SAMPLE = 1 << 28
-KERNEL_SOURCES = ("sparse_activation_compression_amd/csrc/zvc_kernels.hpp",
+KERNEL_SOURCES = ("sparse_activation_compression_amd/csrc/zvc_compress.hpp",
+                  "sparse_activation_compression_amd/csrc/zvc_common.hpp",
                   "sparse_activation_compression_amd/csrc/device_common.hpp")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "zvc_compress_kernel_sweep4GiB_s0.5_traffic.md")
 

@@ -2,7 +2,8 @@
 #include <mutex>
 
 #include "launch.hpp"
-#include "zvc_kernels.hpp"
+#include "zvc_compress.hpp"
+#include "zvc_decompress.hpp"
 #include "rle_kernels.hpp"
 
 namespace cdma {

@@ -29,7 +29,7 @@
 //             into the nonzero bitmap -> the same expansion as ZVC.
 #pragma once
 
-#include "zvc_kernels.hpp"
+#include "zvc_common.hpp"
 
 namespace cdma {
 

@@ -1,0 +1,347 @@
+// zvc_decompress.hpp -- ZVC decompression for gfx950 (stream format in
+// zvc_common.hpp): per-tile value offsets from the masks alone (a count pass
+// and a one-workgroup scan), then an expand pass in which each tile's value
+// span is read into LDS with aligned 16-byte loads and each lane expands its
+// vector from LDS -> aligned 16-byte stores.
+#pragma once
+
+#include "zvc_common.hpp"
+
+namespace cdma {
+
+// ---------------------------------------------------------------------------
+// decompress, passes 1 and 2: value offset of every tile from the masks alone
+// ---------------------------------------------------------------------------
+//
+// Pass 1 (zvc_count_kernel): a super tile is SUPER consecutive ZVC tiles
+// (32 KB of masks).  Each workgroup popcounts its masks and writes, for every
+// tile, the number of nonzeros before it inside the super tile (local[t]),
+// and the super tile's total (sup[u]).  Mask bytes at or past the readable
+// size count as 0; mask bits for indices >= n are not counted but reported.
+// Pass 2 (zvc_scan_kernel): one workgroup turns sup[] into exclusive prefixes
+// in place, with the grand total in sup[num_super].  The value offset of tile
+// t is then sup[t / SUPER] + local[t].  Neither pass waits on another
+// workgroup.
+
+template <int ESZ, int V>
+struct ZvcScanShape {
+  using S = ZvcShape<ESZ, V>;
+  static constexpr int WORDS = 8192;                 // mask words per super tile
+  static constexpr int SUPER = WORDS / S::WPT;       // ZVC tiles per super tile
+  static_assert(SUPER <= 64 && WORDS % S::WPT == 0, "super tile shape");
+};
+
+template <int ESZ, int V>
+__global__ __launch_bounds__(kBlock) void zvc_count_kernel(
+    const uint8_t* __restrict__ src, uint64_t src_capacity, const uint64_t* __restrict__ src_bytes,
+    uint64_t n, uint32_t* __restrict__ local, uint32_t* __restrict__ sup, uint32_t* __restrict__ error,
+    uint32_t num_tiles) {
+  using C = ZvcScanShape<ESZ, V>;
+  // Mask quad i of the super tile (16 bytes) is read by thread i % kBlock in
+  // step i / kBlock, so each load instruction covers 1 KB of contiguous masks.
+  // A ZVC tile's quads are then one half-wave or one whole wave of one step.
+  constexpr int QT = C::S::WPT / 4;            // mask quads per ZVC tile
+  constexpr int KQ = C::WORDS / 4 / kBlock;    // steps (quads per thread)
+  static_assert(QT == 32 || QT == 64, "a ZVC tile's masks are one half-wave or one wave of quads");
+  static_assert(KQ * kBlock * 4 == C::WORDS, "super tile shape");
+  __shared__ uint32_t s_cnt[C::SUPER];
+  const int tid = threadIdx.x;
+  const int lane = (int)lane_id();
+  const int wave = tid >> 6;
+  const uint32_t u = blockIdx.x;
+  const uint64_t W = (n + 31) / 32;
+  const uint64_t claimed = src_bytes ? *src_bytes : src_capacity;
+  const uint64_t eff = claimed < src_capacity ? claimed : src_capacity;
+  const uint64_t w0 = (uint64_t)u * C::WORDS;  // first mask word of the super tile
+  u32x4 m[KQ];
+  if (w0 + C::WORDS <= W && 4 * (w0 + C::WORDS) <= eff) {
+#pragma unroll
+    for (int k = 0; k < KQ; ++k)
+      m[k] = ld_stream(reinterpret_cast<const u32x4*>(src + 4 * (w0 + 4 * (uint64_t)(k * kBlock + tid))));
+  } else {  // the last super tile: words past W count as 0, bytes past the readable size read as 0
+    for (int k = 0; k < KQ; ++k) {
+      const uint64_t g = w0 + 4 * (uint64_t)(k * kBlock + tid);
+      m[k] = u32x4{0u, 0u, 0u, 0u};
+      for (int i = 0; i < 4; ++i) {
+        if (g + i >= W) break;
+        uint32_t w = 0;
+        for (int b = 0; b < 4; ++b)
+          if (4 * (g + i) + b < eff) w |= (uint32_t)src[4 * (g + i) + b] << (8 * b);
+        m[k][i] = w;
+      }
+    }
+  }
+  uint32_t err = 0;
+#pragma unroll
+  for (int k = 0; k < KQ; ++k) {
+    const uint32_t qi = (uint32_t)(k * kBlock + tid);
+    const uint64_t g = w0 + 4 * (uint64_t)qi;
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t w = m[k][i];
+      if (g + i == W - 1 && (n & 31)) {
+        const uint32_t valid = (1u << (n & 31)) - 1;
+        if (w & ~valid) err |= CDMA_E_MASK_PAST_N;
+        w &= valid;
+      }
+      cnt += (uint32_t)__builtin_popcount(w);
+    }
+    const uint32_t inc = wave_incl_scan(cnt);
+    if constexpr (QT == 64) {
+      if (lane == 63) s_cnt[qi / 64] = inc;
+    } else {
+      const uint32_t lo = read_lane(inc, 31);
+      if (lane == 31) s_cnt[qi / 32] = lo;
+      if (lane == 63) s_cnt[qi / 32] = inc - lo;
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const uint32_t c = lane < C::SUPER ? s_cnt[lane] : 0u;
+    const uint32_t inc = wave_incl_scan(c);
+    const uint64_t t = (uint64_t)u * C::SUPER + lane;
+    if (lane < C::SUPER && t < num_tiles) local[t] = inc - c;
+    if (lane == 63) sup[u] = inc;
+  }
+  if (err && error) atomicOr(error, err);
+}
+
+// Exclusive prefix sums of sup[0..count) in place, total in sup[count]; one
+// workgroup of kScanBlock threads.
+constexpr int kScanBlock = 1024;
+
+__global__ __launch_bounds__(kScanBlock) void zvc_scan_kernel(uint32_t* __restrict__ sup, uint32_t count) {
+  __shared__ uint32_t s_wave[kScanBlock / 64];
+  __shared__ uint32_t s_carry;
+  const int tid = threadIdx.x;
+  const int lane = (int)lane_id();
+  const int wave = tid >> 6;
+  if (tid == 0) s_carry = 0;
+  __syncthreads();
+  for (uint32_t base = 0; base < count; base += kScanBlock) {
+    const uint32_t i = base + tid;
+    const uint32_t v = i < count ? sup[i] : 0u;
+    const uint32_t inc = wave_incl_scan(v);
+    if (lane == 63) s_wave[wave] = inc;
+    __syncthreads();
+    uint32_t before = s_carry, all = 0;
+    for (int w = 0; w < kScanBlock / 64; ++w) {
+      if (w < wave) before += s_wave[w];
+      all += s_wave[w];
+    }
+    if (i < count) sup[i] = before + inc - v;
+    __syncthreads();
+    if (tid == 0) s_carry += all;
+    __syncthreads();
+  }
+  if (tid == 0) sup[count] = s_carry;
+}
+
+// ---------------------------------------------------------------------------
+// decompress, pass 2: expand, persistent grid-stride with prefetch
+// ---------------------------------------------------------------------------
+//
+// With the offsets known, tiles are independent.  Each workgroup walks tiles
+// t, t+G, t+2G, ...; while it expands tile a from LDS it already has the
+// masks and value quads of tile b = a+G in flight in registers, and the
+// offsets of tile b+G on their way.
+
+template <int ESZ, int V>
+struct ZvcExpandShape {
+  using S = ZvcShape<ESZ, V>;
+  static constexpr int QPT = (S::TE * ESZ / 16 + 2 + kBlock - 1) / kBlock;  // value quads per thread
+  static constexpr int MPT = (S::WPT + kBlock - 1) / kBlock;                // mask words per thread
+};
+
+template <int ESZ, int V>
+struct ZvcTileIn {
+  using X = ZvcExpandShape<ESZ, V>;
+  u32x4 q[X::QPT];
+  uint32_t m[X::MPT];
+  uint64_t beg, end;  // value span in the stream
+  bool short_read;
+};
+
+template <int ESZ, int V>
+__device__ __forceinline__ void zvc_fetch_tile(ZvcTileIn<ESZ, V>& in, const uint8_t* __restrict__ src, uint64_t eff,
+                                               uint64_t W, uint32_t t, uint32_t o0, uint32_t o1, int tid) {
+  using S = ZvcShape<ESZ, V>;
+  using X = ZvcExpandShape<ESZ, V>;
+#pragma unroll
+  for (int k = 0; k < X::MPT; ++k) {
+    const int i = tid + k * kBlock;
+    const uint64_t g = (uint64_t)t * S::WPT + i;
+    uint32_t w = 0;
+    if (i < S::WPT && g < W) {
+      if (4 * g + 4 <= eff) {
+        w = reinterpret_cast<const uint32_t*>(src)[g];
+      } else {
+        for (int b = 0; b < 4; ++b)
+          if (4 * g + b < eff) w |= (uint32_t)src[4 * g + b] << (8 * b);
+      }
+    }
+    in.m[k] = w;
+  }
+  in.beg = 4 * W + (uint64_t)ESZ * o0;
+  in.end = 4 * W + (uint64_t)ESZ * (o1 > o0 ? o1 : o0);
+  in.short_read = false;
+  const uint64_t q0 = in.beg >> 4, q1 = (in.end + 15) >> 4;
+#pragma unroll
+  for (int k = 0; k < X::QPT; ++k) {
+    const uint64_t q = q0 + tid + (uint64_t)k * kBlock;
+    u32x4 d = {0u, 0u, 0u, 0u};
+    if (q < q1) {
+      const uint64_t qb = q << 4;
+      if (qb + 16 <= eff) {
+        d = ld_stream(reinterpret_cast<const u32x4*>(src + qb));
+      } else {
+        for (int b = 0; b < 16; b += ESZ) {
+          if (qb + b + ESZ <= eff) vec_set<ESZ>(d, b / ESZ, load_elem<ESZ>(src + qb + b));
+          else if (qb + b >= in.beg && qb + b < in.end) in.short_read = true;
+        }
+      }
+    }
+    in.q[k] = d;
+  }
+}
+
+template <int ESZ, int V>
+struct ZvcExpandLds {
+  using S = ZvcShape<ESZ, V>;
+  uint32_t tot[S::SEG];
+  uint32_t mask[S::WPT];
+  __attribute__((aligned(16))) uint8_t stage[S::STAGE];
+};
+
+template <int ESZ, int V>
+__device__ __forceinline__ uint32_t zvc_expand_tile(ZvcExpandLds<ESZ, V>& L, const ZvcTileIn<ESZ, V>& in, uint32_t t,
+                                                    uint64_t n, uint8_t* __restrict__ dst, int tid, int wave,
+                                                    int lane) {
+  using S = ZvcShape<ESZ, V>;
+  using X = ZvcExpandShape<ESZ, V>;
+  const uint64_t W = (n + 31) / 32;
+  const uint64_t q0 = in.beg >> 4, q1 = (in.end + 15) >> 4;
+#pragma unroll
+  for (int k = 0; k < X::MPT; ++k) {
+    const int i = tid + k * kBlock;
+    if (i < S::WPT) {
+      uint32_t w = in.m[k];
+      const uint64_t g = (uint64_t)t * S::WPT + i;
+      if (g == W - 1 && (n & 31)) w &= (1u << (n & 31)) - 1;
+      L.mask[i] = w;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < X::QPT; ++k) {
+    const uint64_t q = q0 + tid + (uint64_t)k * kBlock;
+    if (q < q1 && 16 * (q - q0) + 16 <= (uint64_t)S::STAGE) *reinterpret_cast<u32x4*>(L.stage + 16 * (q - q0)) = in.q[k];
+  }
+  __syncthreads();
+  uint32_t bits[V], ex[V];
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    const uint32_t c = (uint32_t)((wave * V + j) * 64 + lane);
+    bits[j] = (L.mask[c / S::LPW] >> ((c % S::LPW) * S::EPL)) & ((1u << S::EPL) - 1);
+    const uint32_t cnt = (uint32_t)__builtin_popcount(bits[j]);
+    const uint32_t inc = wave_incl_scan(cnt);
+    ex[j] = inc - cnt;
+    if (lane == 63) L.tot[wave * V + j] = inc;
+  }
+  __syncthreads();
+  uint32_t base[V];
+  const uint32_t total = segment_bases<V>(L.tot, wave, base);
+  // values the offsets give this tile (never more than a tile holds)
+  const uint64_t span = (in.end - in.beg) / ESZ;
+  const uint32_t avail = span < (uint64_t)S::TE ? (uint32_t)span : (uint32_t)S::TE;
+  const uint32_t shift = (uint32_t)(in.beg & 15);
+  const uint64_t e_tile = (uint64_t)t * S::TE;
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    const uint32_t c = (uint32_t)((wave * V + j) * 64 + lane);
+    uint32_t r = base[j] + ex[j];
+    u32x4 o = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int k = 0; k < S::EPL; ++k) {
+      if ((bits[j] >> k) & 1u) {
+        if (r < avail) vec_set<ESZ>(o, k, load_elem<ESZ>(L.stage + shift + ESZ * r));
+        ++r;
+      }
+    }
+    store_vec<ESZ>(dst, e_tile + (uint64_t)c * S::EPL, n, o);
+  }
+  __syncthreads();
+  return total;
+}
+
+// Value offset of tile t (t <= num_tiles) from the two count passes.
+template <int ESZ, int V>
+__device__ __forceinline__ uint32_t zvc_tile_offset(const uint32_t* __restrict__ local,
+                                                    const uint32_t* __restrict__ sup, uint32_t t,
+                                                    uint32_t num_tiles) {
+  using C = ZvcScanShape<ESZ, V>;
+  if (t >= num_tiles) return sup[(num_tiles + C::SUPER - 1) / C::SUPER];  // the grand total
+  return sup[t / C::SUPER] + local[t];
+}
+
+template <int ESZ, int V>
+__global__ __launch_bounds__(kBlock) void zvc_expand_kernel(
+    const uint8_t* __restrict__ src, uint64_t src_capacity, const uint64_t* __restrict__ src_bytes,
+    uint64_t n, uint8_t* __restrict__ dst, uint32_t* __restrict__ error,
+    const uint32_t* __restrict__ local, const uint32_t* __restrict__ sup, uint32_t num_tiles) {
+  __shared__ ZvcExpandLds<ESZ, V> L;
+  const int tid = threadIdx.x;
+  const int lane = (int)lane_id();
+  const int wave = tid >> 6;
+  const uint32_t G = gridDim.x;
+  const uint64_t W = (n + 31) / 32;
+  const uint64_t claimed = src_bytes ? *src_bytes : src_capacity;
+  const uint64_t eff = claimed < src_capacity ? claimed : src_capacity;
+  uint32_t err = 0;
+  uint32_t ta = blockIdx.x;
+  if (ta >= num_tiles) return;
+  ZvcTileIn<ESZ, V> A, B;
+  zvc_fetch_tile<ESZ, V>(A, src, eff, W, ta, zvc_tile_offset<ESZ, V>(local, sup, ta, num_tiles),
+                         zvc_tile_offset<ESZ, V>(local, sup, ta + 1, num_tiles), tid);
+  uint32_t tb = ta + G;
+  uint32_t ob0 = 0, ob1 = 0;
+  if (tb < num_tiles) {
+    ob0 = zvc_tile_offset<ESZ, V>(local, sup, tb, num_tiles);
+    ob1 = zvc_tile_offset<ESZ, V>(local, sup, tb + 1, num_tiles);
+  }
+  for (;;) {
+    // A holds tile ta; fetch tile tb into B; offsets of the tile after tb
+    uint32_t tc = tb + G, oc0 = 0, oc1 = 0;
+    if (tb < num_tiles) zvc_fetch_tile<ESZ, V>(B, src, eff, W, tb, ob0, ob1, tid);
+    if (tc < num_tiles) {
+      oc0 = zvc_tile_offset<ESZ, V>(local, sup, tc, num_tiles);
+      oc1 = zvc_tile_offset<ESZ, V>(local, sup, tc + 1, num_tiles);
+    }
+    if (A.short_read) err |= CDMA_E_SIZE;
+    zvc_expand_tile<ESZ, V>(L, A, ta, n, dst, tid, wave, lane);
+    if (ta == num_tiles - 1 && tid == 0 && src_bytes && A.end != *src_bytes) err |= CDMA_E_SIZE;
+    if (tb >= num_tiles) break;
+    ta = tb;
+    tb = tc;
+    ob0 = oc0;
+    ob1 = oc1;
+    // same step with the roles of A and B swapped
+    tc = tb + G;
+    if (tb < num_tiles) zvc_fetch_tile<ESZ, V>(A, src, eff, W, tb, ob0, ob1, tid);
+    if (tc < num_tiles) {
+      oc0 = zvc_tile_offset<ESZ, V>(local, sup, tc, num_tiles);
+      oc1 = zvc_tile_offset<ESZ, V>(local, sup, tc + 1, num_tiles);
+    }
+    if (B.short_read) err |= CDMA_E_SIZE;
+    zvc_expand_tile<ESZ, V>(L, B, ta, n, dst, tid, wave, lane);
+    if (ta == num_tiles - 1 && tid == 0 && src_bytes && B.end != *src_bytes) err |= CDMA_E_SIZE;
+    if (tb >= num_tiles) break;
+    ta = tb;
+    tb = tc;
+    ob0 = oc0;
+    ob1 = oc1;
+  }
+  if (err && error) atomicOr(error, err);
+}
+
+}  // namespace cdma
