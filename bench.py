@@ -40,6 +40,7 @@ N_ELEMS = 1 << 30
 CHUNK = 1 << 24
 SLOTS = 3
 CPU_SAMPLE = 1 << 28
+SPIN_CYCLES = 400_000  # ~0.2 ms of device-side spin ahead of each step's first event
 KERNEL_SOURCES = ("sparse_activation_compression_amd/csrc/zvc_compress.hpp",
                   "sparse_activation_compression_amd/csrc/zvc_common.hpp",
                   "sparse_activation_compression_amd/csrc/device_common.hpp")
@@ -269,6 +270,9 @@ def main() -> int:
 
     def step(record: bool):
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+        # a short device-side spin keeps the stream busy while the host
+        # enqueues the rows, so the events time GPU work, not launch latency
+        torch.cuda._sleep(SPIN_CYCLES)
         evs[0].record(stream)
         cdma.compress(x, "zvc", dst=zdst, out_bytes=zsz, ws=ws)
         evs[1].record(stream)
@@ -284,6 +288,9 @@ def main() -> int:
                 for k, name in enumerate(names):
                     ev_times[name].append(evs[k].elapsed_time(evs[k + 1]) * 1e3)
             return
+        # the offload row times the offload alone: the codec kernels queued
+        # above must have finished before its clock starts
+        evs[4].synchronize()
         t0 = time.perf_counter()
         job = cdma.offload(x, host, CHUNK, "zvc", SLOTS, scratch=scratch, compute_stream=cstream,
                            copy_stream=pstream)
