@@ -229,10 +229,8 @@ def main() -> int:
         return 2
 
     import torch
-    from sparse_activation_compression_amd.build import LIB
-    if not os.path.exists(LIB):
-        import __graft_entry__
-        __graft_entry__.build()
+    import __graft_entry__
+    __graft_entry__.ensure_built()
     import sparse_activation_compression_amd as cdma
     from synth import SWEEP_SEEDS, SWEEP_ZERO_FRACTIONS, sweep_bits_device
 

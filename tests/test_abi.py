@@ -23,9 +23,8 @@ def _declared_functions():
 
 @pytest.fixture(scope="module")
 def cdma():
-    from sparse_activation_compression_amd.build import LIB, build_library
-    if not os.path.exists(LIB):
-        build_library()
+    import __graft_entry__
+    __graft_entry__.ensure_built()
     import sparse_activation_compression_amd as m
     return m
 
