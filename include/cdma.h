@@ -12,7 +12,7 @@
  *     the RLE window);
  *   - §V.D Software Interface: a compressed memory-copy call that reports the
  *     compressed size, and offload of every layer's activations to host
- *     memory with asynchronous copies.
+ *     memory with asynchronous copies (and their prefetch back, §II.B).
  *
  * Everything here is plain C: device and host pointers, sizes and status
  * codes.  A "stream" argument is a hipStream_t passed as void* (NULL = the
@@ -42,7 +42,8 @@
  * alive until the enqueued work has finished.  cdma_compress and
  * cdma_decompress allocate nothing.  cdma_offload_async allocates its handle,
  * a few events, a small pinned size array and one worker thread, all
- * released by cdma_offload_destroy.
+ * released by cdma_offload_destroy; cdma_prefetch_async the same without the
+ * thread, released by cdma_prefetch_destroy.
  *
  * Errors.  Argument and capacity problems are found on the host before
  * anything is enqueued and are returned as a status.  A failing HIP call
@@ -63,7 +64,7 @@ extern "C" {
 #define CDMA_OK              0
 #define CDMA_ERR_INVALID_ARG 1  /* bad algo/esz, NULL or misaligned pointer, n too large */
 #define CDMA_ERR_CAPACITY    2  /* destination, workspace or host buffer too small */
-#define CDMA_ERR_CORRUPT     3  /* reserved for host-side decode checks */
+#define CDMA_ERR_CORRUPT     3  /* host-side decode check: a prefetch chunk size no stream can have */
 #define CDMA_ERR_HIP         4  /* a HIP runtime call failed */
 
 /* algorithms */
@@ -181,6 +182,53 @@ int cdma_offload_wait(cdma_offload_t h, uint64_t *total_bytes, uint64_t *chunk_b
 
 /* Release a handle (waits for it first if cdma_offload_wait was not called). */
 void cdma_offload_destroy(cdma_offload_t h);
+
+/*
+ * Compressed prefetch (§II.B: offloaded activations are brought back to the
+ * GPU before the backward pass reuses them; §V.D: offload and prefetch use
+ * asynchronous copies; §V.B: the decompression engine expands the data on
+ * its way into GPU memory).  The inverse of cdma_offload_async: h_src holds
+ * the chunk streams back to back, chunk k's stream (chunk_bytes[k] bytes) is
+ * copied host-to-device with hipMemcpyAsync on copy_stream into staging slot
+ * k % slots and decompressed on compute_stream into elements
+ * [k*chunk_elems, min(n, (k+1)*chunk_elems)) of d_dst, while later chunks are
+ * copied.  Every chunk size is known at the call, so the whole pipeline is
+ * enqueued before it returns; no host thread is used.
+ *   h_src         pinned host memory (hipHostMalloc), h_src_bytes readable;
+ *                 the sum of chunk_bytes must fit, else CDMA_ERR_CAPACITY.
+ *   chunk_bytes   host array of n_chunks = ceil(n/chunk_elems) stream sizes,
+ *                 as cdma_offload_wait reported them; read during the call
+ *                 only.  A size larger than its chunk's
+ *                 cdma_max_compressed_bytes is rejected with CDMA_ERR_CORRUPT
+ *                 before anything is enqueued (it could not fit a slot).
+ *   chunk_elems   multiple of 2048, the value the offload used.
+ *   d_dst         device, 16-byte aligned, n*esz bytes, fully written.
+ *   d_error       device u32 or NULL; every chunk's CDMA_E_* bits (as
+ *                 cdma_decompress reports them) are OR-ed into it.
+ *   d_scratch     device, 256-byte aligned, scratch_bytes >=
+ *                 cdma_prefetch_scratch_bytes(algo, esz, n, chunk_elems, slots):
+ *                 the chunk sizes, one decompress workspace and the slots.
+ *   compute_stream, copy_stream  distinct streams; as for the offload.
+ * On success *out receives a handle; on any error nothing is left running
+ * and *out is NULL.  h_src, d_dst and d_scratch must stay valid until
+ * cdma_prefetch_wait returns.
+ */
+typedef struct cdma_prefetch_s *cdma_prefetch_t;
+
+uint64_t cdma_prefetch_scratch_bytes(int algo, int esz, uint64_t n, uint64_t chunk_elems, int slots);
+
+int cdma_prefetch_async(int algo, int esz, const void *h_src, uint64_t h_src_bytes,
+                        const uint64_t *chunk_bytes, uint64_t n_chunks, uint64_t n,
+                        uint64_t chunk_elems, void *d_dst, uint32_t *d_error,
+                        void *d_scratch, uint64_t scratch_bytes, int slots,
+                        void *compute_stream, void *copy_stream, cdma_prefetch_t *out);
+
+/* Wait until every chunk is decompressed.  Returns CDMA_OK or CDMA_ERR_HIP;
+   decode problems are in *d_error.  May be called more than once. */
+int cdma_prefetch_wait(cdma_prefetch_t h);
+
+/* Release a handle (waits for it first). */
+void cdma_prefetch_destroy(cdma_prefetch_t h);
 
 /* Static description of a status code. */
 const char *cdma_status_string(int status);

@@ -163,3 +163,22 @@ def offload_stream(x, chunk_elems: int, algo: str = "zvc", lib=None):
     parts = [comp(b[lo: lo + chunk_elems], lib) for lo in range(0, b.size, chunk_elems)]
     sizes = [p.size for p in parts]
     return (np.concatenate(parts) if parts else np.zeros(0, np.uint8)), sizes
+
+
+def restore(image, chunk_bytes, n: int, esz: int, chunk_elems: int, algo: str = "zvc", lib=None):
+    """Inverse of :func:`offload_stream`: chunk k of ``chunk_elems`` elements
+    (the last one partial) is decoded on its own from the next
+    ``chunk_bytes[k]`` bytes of ``image``.  Returns (patterns, OR of every
+    chunk's error bits)."""
+    img = np.ascontiguousarray(np.asarray(image, dtype=np.uint8))
+    dec = zvc_decompress if algo == "zvc" else rle_decompress
+    out = np.zeros(n, dtype=np.uint32 if esz == 4 else np.uint16)
+    err, off = 0, 0
+    for k, size in enumerate(chunk_bytes):
+        lo = k * chunk_elems
+        m = min(chunk_elems, n - lo)
+        part, e = dec(img[off: off + size], m, esz, lib)
+        out[lo: lo + m] = part
+        err |= e
+        off += size
+    return out, err

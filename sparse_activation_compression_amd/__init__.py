@@ -23,6 +23,7 @@ from .binding import (  # noqa: F401
     CDMA_E_VAL_COUNT,
     CdmaError,
     Offload,
+    Prefetch,
     cdma_compress,
     cdma_decompress,
     cdma_max_compressed_bytes,
@@ -30,6 +31,10 @@ from .binding import (  # noqa: F401
     cdma_offload_destroy,
     cdma_offload_scratch_bytes,
     cdma_offload_wait,
+    cdma_prefetch_async,
+    cdma_prefetch_destroy,
+    cdma_prefetch_scratch_bytes,
+    cdma_prefetch_wait,
     cdma_status_string,
     cdma_version,
     cdma_workspace_bytes,
@@ -37,4 +42,5 @@ from .binding import (  # noqa: F401
     decompress,
     library_path,
     offload,
+    prefetch,
 )

@@ -56,6 +56,11 @@ def _load():
         "cdma_offload_wait": (i32, [vp, ctypes.POINTER(u64), ctypes.POINTER(u64), u64,
                                     ctypes.POINTER(u64)]),
         "cdma_offload_destroy": (None, [vp]),
+        "cdma_prefetch_scratch_bytes": (u64, [i32, i32, u64, u64, i32]),
+        "cdma_prefetch_async": (i32, [i32, i32, vp, u64, ctypes.POINTER(u64), u64, u64, u64, vp, vp, vp, u64,
+                                      i32, vp, vp, ctypes.POINTER(vp)]),
+        "cdma_prefetch_wait": (i32, [vp]),
+        "cdma_prefetch_destroy": (None, [vp]),
         "cdma_status_string": (ctypes.c_char_p, [i32]),
         "cdma_version": (i32, []),
     }
@@ -113,6 +118,29 @@ def cdma_offload_wait(handle, max_chunks: int):
 
 def cdma_offload_destroy(handle) -> None:
     _lib.cdma_offload_destroy(handle)
+
+
+def cdma_prefetch_scratch_bytes(algo: int, esz: int, n: int, chunk_elems: int, slots: int) -> int:
+    return int(_lib.cdma_prefetch_scratch_bytes(algo, esz, n, chunk_elems, slots))
+
+
+def cdma_prefetch_async(algo, esz, h_src, h_src_bytes, chunk_bytes, n_chunks, n, chunk_elems, d_dst,
+                        d_error, d_scratch, scratch_bytes, slots, compute_stream, copy_stream):
+    """Returns (status, handle); ``chunk_bytes`` is a sequence of ints."""
+    h = ctypes.c_void_p(0)
+    arr = (ctypes.c_uint64 * max(1, len(chunk_bytes)))(*chunk_bytes)
+    rc = int(_lib.cdma_prefetch_async(algo, esz, h_src, h_src_bytes, arr, n_chunks, n, chunk_elems, d_dst,
+                                      d_error, d_scratch, scratch_bytes, slots, compute_stream, copy_stream,
+                                      ctypes.byref(h)))
+    return rc, h.value
+
+
+def cdma_prefetch_wait(handle) -> int:
+    return int(_lib.cdma_prefetch_wait(handle))
+
+
+def cdma_prefetch_destroy(handle) -> None:
+    _lib.cdma_prefetch_destroy(handle)
 
 
 def cdma_status_string(status: int) -> str:
@@ -242,3 +270,60 @@ def offload(x, h_dst, chunk_elems: int = 1 << 24, algo="zvc", slots: int = 3, sc
     _check("cdma_offload_async", rc)
     k = (n + chunk_elems - 1) // chunk_elems
     return Offload(h, (x, h_dst, scratch, comp, copy), max(1, k))
+
+
+class Prefetch:
+    """A running compressed prefetch; wait() returns (status, out, error)."""
+
+    def __init__(self, handle, out, error, keep):
+        self._h = handle
+        self._out = out
+        self._err = error
+        self._keep = keep
+        self._result = None
+
+    def wait(self):
+        if self._result is None:
+            rc = cdma_prefetch_wait(self._h)
+            cdma_prefetch_destroy(self._h)
+            self._h = None
+            self._keep = None
+            self._result = (rc, self._out, self._err)
+        return self._result
+
+    def __del__(self):
+        if self._h is not None:
+            cdma_prefetch_destroy(self._h)
+
+
+def prefetch(h_src, chunk_bytes, n: int, esz: int, chunk_elems: int = 1 << 24, algo="zvc", slots: int = 3,
+             out=None, error=None, scratch=None, compute_stream=None, copy_stream=None, device=None) -> Prefetch:
+    """Start a compressed prefetch of the host image ``h_src`` (pinned uint8
+    tensor holding the chunk streams back to back, as :func:`offload` wrote
+    them, with their sizes ``chunk_bytes``) into a device tensor of n
+    elements of esz bytes.  Ordered after the work already enqueued on the
+    current stream.  Returns a :class:`Prefetch`."""
+    import torch
+    a = _ALGOS[algo]
+    dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+    if out is None:
+        out = torch.empty(max(1, n), dtype=torch.int32 if esz == 4 else torch.int16, device=dev)[:n]
+    if error is None:
+        error = torch.zeros(1, dtype=torch.int32, device=dev)
+    if scratch is None:
+        scratch = torch.empty(max(256, cdma_prefetch_scratch_bytes(a, esz, n, chunk_elems, slots)),
+                              dtype=torch.uint8, device=dev)
+    comp = compute_stream or torch.cuda.Stream(device=dev)
+    copy = copy_stream or torch.cuda.Stream(device=dev)
+    ready = torch.cuda.Event()
+    ready.record(torch.cuda.current_stream(dev))
+    comp.wait_event(ready)
+    copy.wait_event(ready)
+    sizes = [int(v) for v in chunk_bytes]
+    rc, h = cdma_prefetch_async(a, esz, h_src.data_ptr(), h_src.numel(), sizes, len(sizes), n, chunk_elems,
+                                out.data_ptr(), error.data_ptr(), scratch.data_ptr(), scratch.numel(), slots,
+                                comp.cuda_stream, copy.cuda_stream)
+    _check("cdma_prefetch_async", rc)
+    # the caller's stream sees the result once the compute stream is done
+    torch.cuda.current_stream(dev).wait_stream(comp)
+    return Prefetch(h, out, error, (h_src, scratch, comp, copy))

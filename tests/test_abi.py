@@ -123,3 +123,34 @@ def test_status_strings(cdma):
     assert cdma.cdma_status_string(0) == "ok"
     assert cdma.cdma_status_string(2) == "buffer too small"
     assert "unknown" in cdma.cdma_status_string(99)
+
+
+def test_prefetch_rejects_on_host(cdma):
+    n, chunk = 10000, 4096
+    sb = cdma.cdma_prefetch_scratch_bytes(0, 4, n, chunk, 2)
+    assert sb > 0
+    mx = [cdma.cdma_max_compressed_bytes(0, 4, m) for m in (4096, 4096, 10000 - 8192)]
+    ok = dict(algo=0, esz=4, h_src=P, h_src_bytes=sum(mx), chunk_bytes=list(mx), n_chunks=3, n=n,
+              chunk_elems=chunk, d_dst=P, d_error=None, d_scratch=P, scratch_bytes=sb, slots=2,
+              compute_stream=16, copy_stream=32)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return cdma.cdma_prefetch_async(*a.values())[0]
+
+    assert call(algo=2) == 1
+    assert call(chunk_elems=1000) == 1                  # not a multiple of 2048
+    assert call(n_chunks=2) == 1                         # must be ceil(n / chunk_elems)
+    assert call(copy_stream=16) == 1                     # same stream twice
+    assert call(d_dst=P + 4) == 1
+    assert call(d_scratch=P + 16) == 1
+    assert call(d_error=P + 2) == 1
+    assert call(scratch_bytes=sb - 1) == 2
+    assert call(h_src_bytes=sum(mx) - 1) == 2            # the image does not hold every chunk
+    bad = list(mx)
+    bad[2] += 1                                          # larger than any stream of the last chunk
+    assert call(chunk_bytes=bad) == 3                    # CDMA_ERR_CORRUPT
+    assert cdma.cdma_prefetch_scratch_bytes(0, 4, n, 1000, 2) == 0
+    assert cdma.cdma_prefetch_scratch_bytes(0, 4, n, chunk, 0) == 0
+    # one slot holds the largest chunk's stream, and the layout grows with the slots
+    assert cdma.cdma_prefetch_scratch_bytes(0, 4, n, chunk, 3) - sb >= mx[0]

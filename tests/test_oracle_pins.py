@@ -347,3 +347,36 @@ def test_offload_stream_is_chunk_concatenation():
         out, err = oracle.zvc_decompress(part, min(4096, b.size - 4096 * k), 4)
         assert err == 0 and np.array_equal(out, b[4096 * k: 4096 * (k + 1)])
         lo += sz
+
+
+# --------------------------------------------------------------------------
+# restore (prefetch) = every chunk decoded on its own, in order
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("algo", ["zvc", "rle"])
+@pytest.mark.parametrize("esz", [4, 2])
+def test_restore_inverts_the_offload_image(algo, esz):
+    """The input itself is the expected value: restore(offload(x)) == x."""
+    x = np.random.default_rng(esz).integers(1, 2 ** (8 * esz), size=3 * 4096 + 77, dtype=np.uint64)
+    x = x.astype(np.uint32 if esz == 4 else np.uint16)
+    x[np.random.default_rng(1).random(x.size) < 0.55] = 0
+    x[100:3000] = 0  # a long zero run across a window edge
+    img, sizes = oracle.offload_stream(x, 4096, algo)
+    out, err = oracle.restore(img, sizes, x.size, esz, 4096, algo)
+    assert err == 0 and np.array_equal(out, x)
+
+
+def test_restore_reports_a_bad_chunk():
+    """A mask bit added to chunk 1 claims a value the stream does not hold:
+    the stream size no longer matches its masks (§V.A: the nonzero count is
+    the mask's popcount), so the size error bit must be set."""
+    x = np.zeros(3 * 4096, dtype=np.uint32)
+    x[::7] = 5
+    img, sizes = oracle.offload_stream(x, 4096)
+    bad = img.copy()
+    first_mask_of_chunk1 = sizes[0]
+    assert bad[first_mask_of_chunk1] & 0x2 == 0  # element 4097 of x is zero
+    bad[first_mask_of_chunk1] |= 0x2
+    out, err = oracle.restore(bad, sizes, x.size, 4, 4096)
+    assert err & oracle.E_SIZE
+    assert np.array_equal(out[:4096], x[:4096]) and np.array_equal(out[8192:], x[8192:])
