@@ -344,11 +344,49 @@ def main() -> int:
         pre_ok = pre_ok and int(perr.item()) == 0 and torch.equal(pout, x)
         del pout, pscratch
 
+    # fused producer epilogue: ReLU of pre-activations coded straight into the
+    # ZVC stream (plus the dense ReLU output), against a separate ReLU pass
+    # followed by the plain compressor.  Pre-activations are the map with -1.0
+    # where it is zero, so ReLU(pre) is the map and the stream must equal zdst.
+    fused = {}
+    if not args.rows_only:
+        pre = torch.where(x == 0, torch.tensor(-0x40800000, dtype=torch.int32, device=dev), x).view(torch.float32)
+        act = torch.empty_like(pre)
+        fdst = torch.empty_like(zdst)
+        fsz = torch.zeros(1, dtype=torch.int64, device=dev)
+        tf, tu = [], []
+        for r in range(max(1, args.warmup) + 5):
+            torch.cuda._sleep(SPIN_CYCLES)
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            e[0].record(stream)
+            cdma.relu_compress(pre, "zvc", act=act, dst=fdst, out_bytes=fsz, ws=ws)
+            e[1].record(stream)
+            torch.cuda._sleep(SPIN_CYCLES)
+            e[2].record(stream)
+            torch.clamp_min(pre, 0.0, out=act)
+            cdma.compress(act.view(torch.int32), "zvc", dst=zdst, out_bytes=zsz, ws=ws)
+            e[3].record(stream)
+            e[3].synchronize()
+            if r >= max(1, args.warmup):
+                tf.append(e[0].elapsed_time(e[1]) * 1e3)
+                tu.append(e[2].elapsed_time(e[3]) * 1e3)
+        fsize = int(fsz.item())
+        fused_ok = (fsize == int(zsz.item()) and torch.equal(fdst[:fsize], zdst[:fsize])
+                    and torch.equal(act.view(torch.int32), x))
+        f_us, u_us = statistics.mean(tf), statistics.mean(tu)
+        f_alg = 8 * n + 4 * W + 4 * nnz  # read x, write ReLU(x) densely, write the stream
+        fused = {"us": round(f_us, 1), "gbs_algorithmic": round(f_alg / f_us / 1e3, 1),
+                 "hbm_frac": round(f_alg / f_us / 1e3 / PEAK_HBM_GBS, 4),
+                 "unfused_us": round(u_us, 1), "speedup_vs_unfused": round(u_us / f_us, 3),
+                 "unfused": "torch.clamp_min then zvc compress", "ok": bool(fused_ok)}
+        del pre, act, fdst
+
     # correctness of what was timed (outside the timed region)
     zsize, rsize = int(zsz.item()), int(rsz.item())
     ok = (zsize == 4 * W + 4 * nnz and int(zerr.item()) == 0 and int(rerr.item()) == 0
           and torch.equal(zout, x) and torch.equal(rout, x) and all(t == off_totals[0] for t in off_totals)
-          and (args.rows_only or off_totals[0] == zsize_chunks(x, cdma)) and pre_ok)
+          and (args.rows_only or off_totals[0] == zsize_chunks(x, cdma)) and pre_ok
+          and fused.get("ok", True))
 
     # raw PCIe device-to-host copy of the dense buffer, for comparison
     raw = []
@@ -391,6 +429,9 @@ def main() -> int:
                             "raw_pcie_h2d_gbs": round(raw_h2d_gbs, 2), "host_bytes": sum(last_sizes),
                             "speedup_vs_raw_copy": round((in_bytes / raw_h2d_gbs / 1e3) / pre_us, 3),
                             "timed": "separately, after the steps (not part of ms_per_step)"}
+
+    if fused:
+        rows["relu_zvc_compress"] = dict(fused, timed="separately, after the steps (not part of ms_per_step)")
 
     ms_per_step = t_total / args.steps * 1e3
     comp_us = statistics.mean(ev_times["zvc_compress"])  # average launch duration

@@ -122,6 +122,35 @@ int cdma_compress(int algo, int esz, const void *d_src, uint64_t n,
                   void *d_dst, uint64_t dst_capacity, uint64_t *d_out_bytes,
                   void *d_ws, uint64_t ws_bytes, void *stream);
 
+/* element formats of cdma_relu_compress (2- or 4-byte IEEE-style patterns) */
+#define CDMA_FMT_F32  0
+#define CDMA_FMT_F16  1
+#define CDMA_FMT_BF16 2
+
+/*
+ * Fused producer epilogue: compress ReLU(x) straight from the pre-activation
+ * values x, and optionally write ReLU(x) densely too.  The page compresses
+ * activation maps on the fly as they leave GPU memory (§I, §V.B); on a GPU the
+ * nearest equivalent is for the kernel that makes the activations to code
+ * them as it writes them, so the map is not read a second time.  ReLU is
+ * max(x, 0) on the element's pattern: a value with the sign bit set that is
+ * not a NaN (-0.0, negative denormals and normals, -inf) becomes +0.0; NaNs
+ * (either sign) and all other values pass unchanged.  NaN is decided on the
+ * pattern for the format: fp32 |bits| > 0x7F800000, fp16 > 0x7C00, bf16 >
+ * 0x7F80 (|bits| = the pattern without its sign bit).
+ *   fmt           CDMA_FMT_F32 (esz 4), CDMA_FMT_F16 or CDMA_FMT_BF16 (esz 2).
+ *   d_src         device, 16-byte aligned, n elements of x, read only.
+ *   d_act         device, 16-byte aligned, n elements; receives ReLU(x), or
+ *                 NULL to skip the dense output.  Must not overlap d_src or
+ *                 d_dst (CDMA_ERR_INVALID_ARG).
+ * The stream, its size word, the workspace and the errors are exactly those of
+ * cdma_compress(algo, esz, ReLU(x), ...): the output stream is byte for byte
+ * the stream of the ReLU'd map.
+ */
+int cdma_relu_compress(int algo, int fmt, const void *d_src, uint64_t n, void *d_act,
+                       void *d_dst, uint64_t dst_capacity, uint64_t *d_out_bytes,
+                       void *d_ws, uint64_t ws_bytes, void *stream);
+
 /*
  * Decompress a stream back into n elements of esz bytes (§V.A; the inverse
  * of cdma_compress, as for the prefetch before reuse of §V.D).

@@ -77,6 +77,8 @@ def load(path: str | None = None):
         f = getattr(lib, name)
         f.restype = ctypes.c_int
         f.argtypes = [vp, u64, u64, ctypes.c_int, vp, u32p]
+    lib.oracle_relu.restype = ctypes.c_int
+    lib.oracle_relu.argtypes = [vp, u64, ctypes.c_int, vp]
     if path is None:
         _lib = lib
     return lib
@@ -182,3 +184,20 @@ def restore(image, chunk_bytes, n: int, esz: int, chunk_elems: int, algo: str = 
         err |= e
         off += size
     return out, err
+
+
+FMT_F32, FMT_F16, FMT_BF16 = 0, 1, 2
+
+
+def relu(x, fmt: int, lib=None) -> np.ndarray:
+    """ReLU of the raw patterns of ``x`` (fmt 0 = fp32, 1 = fp16, 2 = bf16):
+    a NaN passes unchanged, any other value with the sign bit set becomes
+    +0.0, everything else passes unchanged."""
+    b = _bits(x)
+    if b.dtype.itemsize != (4 if fmt == FMT_F32 else 2):
+        raise ValueError("element size does not match the format")
+    out = np.zeros(max(1, b.size), dtype=b.dtype)
+    rc = (lib or load()).oracle_relu(b.ctypes.data, b.size, fmt, out.ctypes.data)
+    if rc != 0:
+        raise RuntimeError(f"oracle_relu failed with {rc}")
+    return out[: b.size]

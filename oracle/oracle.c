@@ -314,3 +314,31 @@ int oracle_rle_decompress(const uint8_t *src, uint64_t src_bytes, uint64_t n, in
     *err = e;
     return OR_OK;
 }
+
+/* ---- ReLU of the producing layer (fused epilogue) ------------------------ */
+/*
+ * ReLU(x) = max(x, 0), written out on the element's sign, exponent and
+ * mantissa fields (IEEE-754 binary32 / binary16, and bfloat16 = the top half
+ * of a binary32).  A NaN (exponent all ones, mantissa not zero) passes
+ * unchanged whatever its sign; any other value whose sign bit is set
+ * (-0.0, negative denormals and normals, -inf) becomes +0.0; everything else
+ * passes unchanged.  fmt: 0 = fp32, 1 = fp16, 2 = bf16.
+ */
+int oracle_relu(const void *src, uint64_t n, int fmt, void *dst)
+{
+    int esz, exp_bits, man_bits;
+    if (fmt == 0) { esz = 4; exp_bits = 8; man_bits = 23; }
+    else if (fmt == 1) { esz = 2; exp_bits = 5; man_bits = 10; }
+    else if (fmt == 2) { esz = 2; exp_bits = 8; man_bits = 7; }
+    else return OR_ERR_ARG;
+    for (uint64_t i = 0; i < n; i++) {
+        uint64_t v = elem(src, i, esz);
+        uint64_t sign = v >> (exp_bits + man_bits);
+        uint64_t exponent = (v >> man_bits) & (((uint64_t)1 << exp_bits) - 1);
+        uint64_t mantissa = v & (((uint64_t)1 << man_bits) - 1);
+        int is_nan = exponent == ((uint64_t)1 << exp_bits) - 1 && mantissa != 0;
+        uint64_t y = (sign && !is_nan) ? 0 : v;
+        put_le((uint8_t *)dst + i * (uint64_t)esz, y, esz);
+    }
+    return OR_OK;
+}

@@ -21,6 +21,9 @@ from .binding import (  # noqa: F401
     CDMA_E_RUN_SUM,
     CDMA_E_SIZE,
     CDMA_E_VAL_COUNT,
+    FMT_BF16,
+    FMT_F16,
+    FMT_F32,
     CdmaError,
     Offload,
     Prefetch,
@@ -35,6 +38,7 @@ from .binding import (  # noqa: F401
     cdma_prefetch_destroy,
     cdma_prefetch_scratch_bytes,
     cdma_prefetch_wait,
+    cdma_relu_compress,
     cdma_status_string,
     cdma_version,
     cdma_workspace_bytes,
@@ -43,4 +47,5 @@ from .binding import (  # noqa: F401
     library_path,
     offload,
     prefetch,
+    relu_compress,
 )

@@ -18,6 +18,10 @@ _LIB_PATH = os.path.join(_PKG, "libcdma.so")
 ALGO_ZVC = 0
 ALGO_RLE = 1
 
+FMT_F32 = 0
+FMT_F16 = 1
+FMT_BF16 = 2
+
 CDMA_E_MASK_PAST_N = 1 << 0
 CDMA_E_SIZE = 1 << 1
 CDMA_E_INDEX = 1 << 3
@@ -49,6 +53,7 @@ def _load():
         "cdma_max_compressed_bytes": (u64, [i32, i32, u64]),
         "cdma_workspace_bytes": (u64, [i32, i32, u64]),
         "cdma_compress": (i32, [i32, i32, vp, u64, vp, u64, vp, vp, u64, vp]),
+        "cdma_relu_compress": (i32, [i32, i32, vp, u64, vp, vp, u64, vp, vp, u64, vp]),
         "cdma_decompress": (i32, [i32, i32, vp, u64, vp, u64, vp, vp, vp, u64, vp]),
         "cdma_offload_scratch_bytes": (u64, [i32, i32, u64, i32]),
         "cdma_offload_async": (i32, [i32, i32, vp, u64, u64, vp, u64, vp, u64, i32, vp, vp,
@@ -87,6 +92,12 @@ def cdma_workspace_bytes(algo: int, esz: int, n: int) -> int:
 def cdma_compress(algo, esz, d_src, n, d_dst, dst_capacity, d_out_bytes, d_ws, ws_bytes, stream) -> int:
     return int(_lib.cdma_compress(algo, esz, d_src, n, d_dst, dst_capacity, d_out_bytes, d_ws,
                                   ws_bytes, stream))
+
+
+def cdma_relu_compress(algo, fmt, d_src, n, d_act, d_dst, dst_capacity, d_out_bytes, d_ws, ws_bytes,
+                       stream) -> int:
+    return int(_lib.cdma_relu_compress(algo, fmt, d_src, n, d_act, d_dst, dst_capacity, d_out_bytes, d_ws,
+                                       ws_bytes, stream))
 
 
 def cdma_decompress(algo, esz, d_src, src_capacity, d_src_bytes, n, d_dst, d_error, d_ws, ws_bytes,
@@ -199,6 +210,41 @@ def compress(x, algo="zvc", dst=None, out_bytes=None, ws=None, stream=None):
                        ws.data_ptr(), ws.numel(), _stream_handle(stream))
     _check("cdma_compress", rc)
     return dst, out_bytes
+
+
+def _fmt_of(x) -> int:
+    import torch
+    fmts = {torch.float32: FMT_F32, torch.float16: FMT_F16, torch.bfloat16: FMT_BF16}
+    if x.dtype not in fmts:
+        raise ValueError("ReLU compression takes float32, float16 or bfloat16 tensors")
+    return fmts[x.dtype]
+
+
+def relu_compress(x, algo="zvc", act=None, dst=None, out_bytes=None, ws=None, stream=None):
+    """Compress ReLU(x) straight from the pre-activation tensor ``x``
+    (float32 / float16 / bfloat16, contiguous, on the device).
+
+    ``act``: a tensor like ``x`` that receives ReLU(x) densely, True to
+    allocate one, or None to skip the dense output.  Returns
+    (dst, out_bytes, act) as :func:`compress` does, plus the dense output."""
+    import torch
+    a = _ALGOS[algo]
+    if not x.is_contiguous():
+        raise ValueError("input must be contiguous")
+    fmt, esz, n = _fmt_of(x), x.element_size(), x.numel()
+    if act is True:
+        act = torch.empty_like(x)
+    cap = cdma_max_compressed_bytes(a, esz, n)
+    if dst is None:
+        dst = torch.empty(max(16, cap), dtype=torch.uint8, device=x.device)
+    if out_bytes is None:
+        out_bytes = torch.empty(1, dtype=torch.int64, device=x.device)
+    if ws is None:
+        ws = workspace(a, esz, n, x.device)
+    rc = cdma_relu_compress(a, fmt, x.data_ptr(), n, act.data_ptr() if act is not None else None, dst.data_ptr(),
+                            dst.numel(), out_bytes.data_ptr(), ws.data_ptr(), ws.numel(), _stream_handle(stream))
+    _check("cdma_relu_compress", rc)
+    return dst, out_bytes, act
 
 
 def decompress(src, n: int, esz: int, algo="zvc", src_bytes=None, out=None, error=None, ws=None,

@@ -54,8 +54,40 @@ int cdma_compress(int algo, int esz, const void* d_src, uint64_t n, void* d_dst,
   }
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = algo == CDMA_ALGO_ZVC
-                           ? cdma::zvc_compress_launch(esz, d_src, n, d_dst, d_out_bytes, d_ws, s)
-                           : cdma::rle_compress_launch(esz, d_src, n, d_dst, d_out_bytes, d_ws, s);
+                           ? cdma::zvc_compress_launch(esz, 0, d_src, n, nullptr, d_dst, d_out_bytes, d_ws, s)
+                           : cdma::rle_compress_launch(esz, 0, d_src, n, nullptr, d_dst, d_out_bytes, d_ws, s);
+  return e == hipSuccess ? CDMA_OK : CDMA_ERR_HIP;
+}
+
+int cdma_relu_compress(int algo, int fmt, const void* d_src, uint64_t n, void* d_act, void* d_dst,
+                       uint64_t dst_capacity, uint64_t* d_out_bytes, void* d_ws, uint64_t ws_bytes, void* stream) {
+  if (fmt != CDMA_FMT_F32 && fmt != CDMA_FMT_F16 && fmt != CDMA_FMT_BF16) return CDMA_ERR_INVALID_ARG;
+  const int esz = fmt == CDMA_FMT_F32 ? 4 : 2;
+  if (!algo_ok(algo) || n > max_n(algo)) return CDMA_ERR_INVALID_ARG;
+  if (!d_out_bytes || !aligned(d_out_bytes, 8)) return CDMA_ERR_INVALID_ARG;
+  if (!d_dst || !aligned(d_dst, 16)) {
+    if (n > 0 || algo == CDMA_ALGO_RLE) return CDMA_ERR_INVALID_ARG;
+  }
+  if (dst_capacity < cdma_max_compressed_bytes(algo, esz, n)) return CDMA_ERR_CAPACITY;
+  if (n > 0) {
+    if (!d_src || !d_ws) return CDMA_ERR_INVALID_ARG;
+    if (!aligned(d_src, 16) || !aligned(d_ws, 8)) return CDMA_ERR_INVALID_ARG;
+    if (d_act) {
+      // the dense output is written while later tiles of the input are still
+      // being read, so it must not overlap the input (or the stream)
+      const uintptr_t a = reinterpret_cast<uintptr_t>(d_act), bytes = (uintptr_t)(n * (uint64_t)esz);
+      const uintptr_t x = reinterpret_cast<uintptr_t>(d_src), y = reinterpret_cast<uintptr_t>(d_dst);
+      if (!aligned(d_act, 16)) return CDMA_ERR_INVALID_ARG;
+      if (a < x + bytes && x < a + bytes) return CDMA_ERR_INVALID_ARG;
+      if (a < y + dst_capacity && y < a + bytes) return CDMA_ERR_INVALID_ARG;
+    }
+    if (ws_bytes < cdma_workspace_bytes(algo, esz, n)) return CDMA_ERR_CAPACITY;
+  }
+  const int op = fmt == CDMA_FMT_F32 ? 1 : fmt == CDMA_FMT_F16 ? 2 : 3;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = algo == CDMA_ALGO_ZVC
+                           ? cdma::zvc_compress_launch(esz, op, d_src, n, d_act, d_dst, d_out_bytes, d_ws, s)
+                           : cdma::rle_compress_launch(esz, op, d_src, n, d_act, d_dst, d_out_bytes, d_ws, s);
   return e == hipSuccess ? CDMA_OK : CDMA_ERR_HIP;
 }
 

@@ -76,18 +76,18 @@ static uint64_t resident_groups(const void* kernel, int block = kBlock) {
   return groups;
 }
 
-template <int ESZ>
-static hipError_t zvc_compress_t(const void* src, uint64_t n, void* dst, uint64_t* out_bytes, void* ws,
+template <int ESZ, int OP>
+static hipError_t zvc_compress_t(const void* src, uint64_t n, void* act, void* dst, uint64_t* out_bytes, void* ws,
                                  hipStream_t s) {
   const uint64_t tiles = zvc_compress_tiles(ESZ, n);
   hipError_t e = clear_workspace(ws, tiles, out_bytes, s);
   if (e != hipSuccess) return e;
   // persistent grid: about one workgroup per CU, tiles handed out by ticket
-  auto kern = zvc_compress_kernel<ESZ>;
+  auto kern = zvc_compress_kernel<ESZ, OP>;
   const uint64_t res = resident_groups(reinterpret_cast<const void*>(kern), kCBlock);
   const unsigned grid = (unsigned)(tiles < res ? tiles : res);
   kern<<<grid, kCBlock, 0, s>>>(static_cast<const uint8_t*>(src), n, static_cast<uint8_t*>(dst), out_bytes,
-                                ws_counter(ws), ws_agg(ws), (uint32_t)tiles);
+                                ws_counter(ws), ws_agg(ws), (uint32_t)tiles, static_cast<uint8_t*>(act));
   return hipGetLastError();
 }
 
@@ -132,14 +132,20 @@ __global__ void empty_stream_check_kernel(const uint8_t* src, uint64_t cap, cons
   if (e) atomicOr(error, e);
 }
 
-hipError_t zvc_compress_launch(int esz, const void* src, uint64_t n, void* dst, uint64_t* out_bytes,
-                               void* ws, hipStream_t s) {
+hipError_t zvc_compress_launch(int esz, int op, const void* src, uint64_t n, void* act, void* dst,
+                               uint64_t* out_bytes, void* ws, hipStream_t s) {
   if (n == 0) {
     store_u64_kernel<<<1, 64, 0, s>>>(out_bytes, 0);
     return hipGetLastError();
   }
-  return esz == 4 ? zvc_compress_t<4>(src, n, dst, out_bytes, ws, s)
-                  : zvc_compress_t<2>(src, n, dst, out_bytes, ws, s);
+  switch (op) {
+    case kOpReluF32: return zvc_compress_t<4, kOpReluF32>(src, n, act, dst, out_bytes, ws, s);
+    case kOpReluF16: return zvc_compress_t<2, kOpReluF16>(src, n, act, dst, out_bytes, ws, s);
+    case kOpReluBF16: return zvc_compress_t<2, kOpReluBF16>(src, n, act, dst, out_bytes, ws, s);
+    default:
+      return esz == 4 ? zvc_compress_t<4, kOpNone>(src, n, nullptr, dst, out_bytes, ws, s)
+                      : zvc_compress_t<2, kOpNone>(src, n, nullptr, dst, out_bytes, ws, s);
+  }
 }
 
 hipError_t zvc_decompress_launch(int esz, const void* src, uint64_t cap, const uint64_t* src_bytes,
@@ -162,18 +168,18 @@ uint64_t rle_compress_tiles(int esz, uint64_t n) {
   return (n + te - 1) / te;
 }
 
-template <int ESZ>
-static hipError_t rle_compress_t(const void* src, uint64_t n, void* dst, uint64_t* out_bytes, void* ws,
+template <int ESZ, int OP>
+static hipError_t rle_compress_t(const void* src, uint64_t n, void* act, void* dst, uint64_t* out_bytes, void* ws,
                                  hipStream_t s) {
   constexpr int block = RleCShape<ESZ>::BLOCK;
   const uint64_t tiles = rle_compress_tiles(ESZ, n);
   hipError_t e = clear_workspace(ws, tiles, out_bytes, s);
   if (e != hipSuccess) return e;
-  auto kern = rle_compress_kernel<ESZ>;
+  auto kern = rle_compress_kernel<ESZ, OP>;
   const uint64_t res = resident_groups(reinterpret_cast<const void*>(kern), block);
   const unsigned grid = (unsigned)(tiles < res ? tiles : res);
   kern<<<grid, block, 0, s>>>(static_cast<const uint8_t*>(src), n, static_cast<uint8_t*>(dst), out_bytes,
-                              ws_counter(ws), ws_agg(ws), (uint32_t)tiles);
+                              ws_counter(ws), ws_agg(ws), (uint32_t)tiles, static_cast<uint8_t*>(act));
   return hipGetLastError();
 }
 
@@ -195,14 +201,20 @@ __global__ void rle_empty_kernel(uint8_t* dst, uint64_t* out_bytes) {
   }
 }
 
-hipError_t rle_compress_launch(int esz, const void* src, uint64_t n, void* dst, uint64_t* out_bytes, void* ws,
-                               hipStream_t s) {
+hipError_t rle_compress_launch(int esz, int op, const void* src, uint64_t n, void* act, void* dst,
+                               uint64_t* out_bytes, void* ws, hipStream_t s) {
   if (n == 0) {
     rle_empty_kernel<<<1, 64, 0, s>>>(static_cast<uint8_t*>(dst), out_bytes);
     return hipGetLastError();
   }
-  return esz == 4 ? rle_compress_t<4>(src, n, dst, out_bytes, ws, s)
-                  : rle_compress_t<2>(src, n, dst, out_bytes, ws, s);
+  switch (op) {
+    case kOpReluF32: return rle_compress_t<4, kOpReluF32>(src, n, act, dst, out_bytes, ws, s);
+    case kOpReluF16: return rle_compress_t<2, kOpReluF16>(src, n, act, dst, out_bytes, ws, s);
+    case kOpReluBF16: return rle_compress_t<2, kOpReluBF16>(src, n, act, dst, out_bytes, ws, s);
+    default:
+      return esz == 4 ? rle_compress_t<4, kOpNone>(src, n, nullptr, dst, out_bytes, ws, s)
+                      : rle_compress_t<2, kOpNone>(src, n, nullptr, dst, out_bytes, ws, s);
+  }
 }
 
 hipError_t rle_decompress_launch(int esz, const void* src, uint64_t cap, const uint64_t* src_bytes, uint64_t n,

@@ -120,6 +120,29 @@ __device__ __forceinline__ void rle_c_load_full(u32x4 (&v)[RleCShape<ESZ>::V], c
   for (int j = 0; j < S::V; ++j) v[j] = ld_stream(reinterpret_cast<const u32x4*>(p + o + j * 1024));
 }
 
+// Apply the epilogue OP to a window's vectors in place and, if act is given,
+// store them densely where they were loaded from.
+template <int ESZ, int OP>
+__device__ __forceinline__ void rle_c_epilogue(u32x4 (&v)[RleCShape<ESZ>::V], uint8_t* __restrict__ act,
+                                               uint64_t n, uint32_t t, uint64_t e_win, bool full_tile, int wave,
+                                               int lane) {
+  using S = RleCShape<ESZ>;
+#pragma unroll
+  for (int j = 0; j < S::V; ++j) v[j] = apply_op<OP>(v[j]);
+  if (!act) return;
+  if (full_tile) {
+    uint8_t* p = act + (uint64_t)t * (S::NW * 4096);
+    uint32_t o = (uint32_t)(wave * 4096 + lane * 16);
+    asm volatile("" : "+v"(o));
+#pragma unroll
+    for (int j = 0; j < S::V; ++j) st_stream(reinterpret_cast<u32x4*>(p + o + j * 1024), v[j]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < S::V; ++j)
+      store_vec<ESZ>(act, e_win + (uint64_t)(lane * S::EPL + j * 64 * S::EPL), n, v[j]);
+  }
+}
+
 // Packed (entries << 15 | nonzeros) aggregate word -> (entries << 31 | nonzeros).
 struct RleAggDec {
   __device__ uint64_t operator()(uint32_t v) const { return ((uint64_t)(v >> 15) << 31) | (v & 0x7FFFu); }
@@ -127,7 +150,7 @@ struct RleAggDec {
 
 // One pipeline iteration (the structure of the ZVC compressor's).  Returns
 // the ticket the data waves prefetch in the next iteration.
-template <int ESZ>
+template <int ESZ, int OP>
 __device__ __forceinline__ uint32_t rle_c_iteration(RleCLds<ESZ>& L, u32x4 (&cur)[RleCShape<ESZ>::V],
                                                     u32x4 (&nxt)[RleCShape<ESZ>::V], ChainRound& cr,
                                                     uint64_t& chain_lo, uint64_t& pfx, uint32_t& pend, uint32_t t,
@@ -135,7 +158,8 @@ __device__ __forceinline__ uint32_t rle_c_iteration(RleCLds<ESZ>& L, u32x4 (&cur
                                                     const uint8_t* __restrict__ src, uint64_t n,
                                                     uint8_t* __restrict__ dst, uint64_t* __restrict__ out_bytes,
                                                     uint32_t* __restrict__ aggw, uint32_t* __restrict__ counter,
-                                                    uint32_t num_tiles, int tid, int wave, int lane) {
+                                                    uint32_t num_tiles, uint8_t* __restrict__ act, int tid,
+                                                    int wave, int lane) {
   using S = RleCShape<ESZ>;
   constexpr int V = S::V;
   const bool have_cur = t < num_tiles;
@@ -158,6 +182,7 @@ __device__ __forceinline__ uint32_t rle_c_iteration(RleCLds<ESZ>& L, u32x4 (&cur
       for (int j = 0; j < V; ++j) cur[j] = load_vec<ESZ>(src, e_win + (el + (uint32_t)(j * 64 * S::EPL)), n);
       __builtin_amdgcn_s_waitcnt(0);
     }
+    if constexpr (OP != kOpNone) rle_c_epilogue<ESZ, OP>(cur, act, n, t, e_win, t < full, wave, lane);
     uint32_t* wmask = L.mask + wave * S::WPW + lane / S::LPW;
     uint32_t v_w = 0;
 #pragma unroll
@@ -296,11 +321,12 @@ __device__ __forceinline__ uint32_t rle_c_iteration(RleCLds<ESZ>& L, u32x4 (&cur
   return __builtin_amdgcn_readfirstlane(L.next);  // uniform: keeps tile bases in SGPRs
 }
 
-template <int ESZ>
+// OP / act: the epilogue and its optional dense output, as for zvc_compress_kernel.
+template <int ESZ, int OP>
 __global__ __launch_bounds__(RleCShape<ESZ>::BLOCK) void rle_compress_kernel(
     const uint8_t* __restrict__ src, uint64_t n, uint8_t* __restrict__ dst,
     uint64_t* __restrict__ out_bytes, uint32_t* __restrict__ counter,
-    uint32_t* __restrict__ aggw, uint32_t num_tiles) {
+    uint32_t* __restrict__ aggw, uint32_t num_tiles, uint8_t* __restrict__ act) {
   using S = RleCShape<ESZ>;
   __shared__ RleCLds<ESZ> L;
   const int tid = threadIdx.x;
@@ -325,14 +351,14 @@ __global__ __launch_bounds__(RleCShape<ESZ>::BLOCK) void rle_compress_kernel(
   uint64_t pfx = 0;       // control wave: packed inclusive prefix of the last resolved tile
   if (wave < S::NW && t < full) rle_c_load_full<ESZ>(ra, src, t, wave, lane);
   for (;;) {
-    uint32_t tnn = rle_c_iteration<ESZ>(L, ra, rb, cr, chain_lo, pfx, pend, t, tn, tp, 0, full, Wr, src, n, dst,
-                                        out_bytes, aggw, counter, num_tiles, tid, wave, lane);
+    uint32_t tnn = rle_c_iteration<ESZ, OP>(L, ra, rb, cr, chain_lo, pfx, pend, t, tn, tp, 0, full, Wr, src, n,
+                                            dst, out_bytes, aggw, counter, num_tiles, act, tid, wave, lane);
     if (t >= num_tiles) break;
     tp = t;
     t = tn;
     tn = tnn;
-    tnn = rle_c_iteration<ESZ>(L, rb, ra, cr, chain_lo, pfx, pend, t, tn, tp, 1, full, Wr, src, n, dst, out_bytes,
-                               aggw, counter, num_tiles, tid, wave, lane);
+    tnn = rle_c_iteration<ESZ, OP>(L, rb, ra, cr, chain_lo, pfx, pend, t, tn, tp, 1, full, Wr, src, n, dst,
+                                   out_bytes, aggw, counter, num_tiles, act, tid, wave, lane);
     if (t >= num_tiles) break;
     tp = t;
     t = tn;

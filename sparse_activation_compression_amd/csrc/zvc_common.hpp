@@ -29,6 +29,37 @@ struct ZvcShape {
   static constexpr int STAGE = TE * ESZ + 32;       // LDS staging bytes
 };
 
+// Activation epilogue applied to every loaded vector before it is coded (the
+// fused producer: the compressor reads the layer's pre-activation output and
+// codes its ReLU).  ReLU is max(x, 0) on the raw pattern: a value whose sign
+// bit is set and that is not a NaN (-0.0, negative denormals and normals,
+// -inf) becomes +0; NaNs and everything else pass unchanged.  A NaN is an
+// all-ones exponent with a nonzero mantissa, i.e. |bits| > the +inf pattern.
+enum { kOpNone = 0, kOpReluF32 = 1, kOpReluF16 = 2, kOpReluBF16 = 3 };
+
+__device__ __forceinline__ uint32_t relu16(uint32_t h, uint32_t inf) {
+  return ((h & 0x8000u) && (h & 0x7FFFu) <= inf) ? 0u : h;
+}
+
+template <int OP>
+__device__ __forceinline__ u32x4 apply_op(u32x4 v) {
+  if constexpr (OP == kOpReluF32) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t w = v[k];
+      v[k] = ((w >> 31) && (w & 0x7FFFFFFFu) <= 0x7F800000u) ? 0u : w;
+    }
+  } else if constexpr (OP == kOpReluF16 || OP == kOpReluBF16) {
+    constexpr uint32_t inf = OP == kOpReluF16 ? 0x7C00u : 0x7F80u;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t w = v[k];
+      v[k] = relu16(w & 0xFFFFu, inf) | (relu16(w >> 16, inf) << 16);
+    }
+  }
+  return v;
+}
+
 // Per-element nonzero bits of one 16-byte vector (bit k = element k).
 template <int ESZ>
 __device__ __forceinline__ uint32_t vec_nz_bits(u32x4 v) {

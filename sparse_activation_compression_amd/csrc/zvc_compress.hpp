@@ -100,9 +100,34 @@ __device__ __forceinline__ void zvc_c_load_bounded(u32x4 (&v)[ZvcCShape<ESZ>::V]
   }
 }
 
+// Apply the epilogue OP to a classified tile's vectors in place and, if act is
+// given, store them densely at the places they were loaded from.
+template <int ESZ, int OP>
+__device__ __forceinline__ void zvc_c_epilogue(u32x4 (&v)[ZvcCShape<ESZ>::V], uint8_t* __restrict__ act,
+                                               uint64_t n, uint32_t t, bool full_tile, int wave, int lane) {
+  using S = ZvcCShape<ESZ>;
+#pragma unroll
+  for (int j = 0; j < S::V; ++j) v[j] = apply_op<OP>(v[j]);
+  if (!act) return;
+  if (full_tile) {
+    uint8_t* p = act + (uint64_t)t * (S::TE * ESZ);
+    uint32_t o = (uint32_t)((wave * S::V * 64 + lane) * 16);
+    asm volatile("" : "+v"(o));
+#pragma unroll
+    for (int j = 0; j < S::V; ++j) st_stream(reinterpret_cast<u32x4*>(p + o + j * 1024), v[j]);
+  } else {
+    const uint64_t e_tile = (uint64_t)t * S::TE;
+#pragma unroll
+    for (int j = 0; j < S::V; ++j) {
+      const uint32_t c = (uint32_t)((wave * S::V + j) * 64 + lane);
+      store_vec<ESZ>(act, e_tile + (uint64_t)c * S::EPL, n, v[j]);
+    }
+  }
+}
+
 // One pipeline iteration (see above).  Returns the ticket the data waves
 // prefetch in the next iteration, with the workgroup synchronised.
-template <int ESZ>
+template <int ESZ, int OP>
 __device__ __forceinline__ uint32_t zvc_c_iteration(ZvcCLds<ESZ>& L, u32x4 (&cur)[ZvcCShape<ESZ>::V],
                                                     u32x4 (&nxt)[ZvcCShape<ESZ>::V], ChainRound& cr,
                                                     uint64_t& chain_lo, uint64_t& P, uint32_t& pend, uint32_t t,
@@ -110,8 +135,8 @@ __device__ __forceinline__ uint32_t zvc_c_iteration(ZvcCLds<ESZ>& L, u32x4 (&cur
                                                     uint32_t full, uint64_t W, const uint8_t* __restrict__ src,
                                                     uint64_t n, uint8_t* __restrict__ dst,
                                                     uint64_t* __restrict__ out_bytes, uint32_t* __restrict__ agg,
-                                                    uint32_t* __restrict__ counter, uint32_t num_tiles, int tid,
-                                                    int wave, int lane) {
+                                                    uint32_t* __restrict__ counter, uint32_t num_tiles,
+                                                    uint8_t* __restrict__ act, int tid, int wave, int lane) {
   using S = ZvcCShape<ESZ>;
   constexpr int V = S::V;
   const bool have_cur = t < num_tiles;
@@ -124,6 +149,7 @@ __device__ __forceinline__ uint32_t zvc_c_iteration(ZvcCLds<ESZ>& L, u32x4 (&cur
       zvc_c_load_bounded<ESZ>(cur, src, n, t, wave, lane);
       __builtin_amdgcn_s_waitcnt(0);
     }
+    if constexpr (OP != kOpNone) zvc_c_epilogue<ESZ, OP>(cur, act, n, t, t < full, wave, lane);
 #pragma unroll
     for (int j = 0; j < V; ++j) {
       const uint32_t c = (uint32_t)((wave * V + j) * 64 + lane);
@@ -204,11 +230,13 @@ __device__ __forceinline__ uint32_t zvc_c_iteration(ZvcCLds<ESZ>& L, u32x4 (&cur
   return __builtin_amdgcn_readfirstlane(L.next);  // uniform: keeps tile bases in SGPRs
 }
 
-template <int ESZ>
+// OP: epilogue applied to the input before it is coded (kOpNone = plain
+// compression); act: optional dense output of the epilogue (OP != kOpNone).
+template <int ESZ, int OP>
 __global__ __launch_bounds__(kCBlock) void zvc_compress_kernel(
     const uint8_t* __restrict__ src, uint64_t n, uint8_t* __restrict__ dst,
     uint64_t* __restrict__ out_bytes, uint32_t* __restrict__ counter, uint32_t* __restrict__ agg,
-    uint32_t num_tiles) {
+    uint32_t num_tiles, uint8_t* __restrict__ act) {
   using S = ZvcCShape<ESZ>;
   __shared__ ZvcCLds<ESZ> L;
   const int tid = threadIdx.x;
@@ -236,14 +264,14 @@ __global__ __launch_bounds__(kCBlock) void zvc_compress_kernel(
   // two iterations per trip so the register sets swap roles without copies;
   // an iteration with no tile left to classify only stores the last one
   for (;;) {
-    uint32_t tnn = zvc_c_iteration<ESZ>(L, ra, rb, cr, chain_lo, P, pend, t, tn, tp, 0, full, W, src, n, dst,
-                                        out_bytes, agg, counter, num_tiles, tid, wave, lane);
+    uint32_t tnn = zvc_c_iteration<ESZ, OP>(L, ra, rb, cr, chain_lo, P, pend, t, tn, tp, 0, full, W, src, n, dst,
+                                            out_bytes, agg, counter, num_tiles, act, tid, wave, lane);
     if (t >= num_tiles) break;
     tp = t;
     t = tn;
     tn = tnn;
-    tnn = zvc_c_iteration<ESZ>(L, rb, ra, cr, chain_lo, P, pend, t, tn, tp, 1, full, W, src, n, dst, out_bytes,
-                               agg, counter, num_tiles, tid, wave, lane);
+    tnn = zvc_c_iteration<ESZ, OP>(L, rb, ra, cr, chain_lo, P, pend, t, tn, tp, 1, full, W, src, n, dst,
+                                   out_bytes, agg, counter, num_tiles, act, tid, wave, lane);
     if (t >= num_tiles) break;
     tp = t;
     t = tn;

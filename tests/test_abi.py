@@ -154,3 +154,22 @@ def test_prefetch_rejects_on_host(cdma):
     assert cdma.cdma_prefetch_scratch_bytes(0, 4, n, chunk, 0) == 0
     # one slot holds the largest chunk's stream, and the layout grows with the slots
     assert cdma.cdma_prefetch_scratch_bytes(0, 4, n, chunk, 3) - sb >= mx[0]
+
+
+def test_relu_compress_rejects_on_host(cdma):
+    n = 1000
+    ok = dict(algo=0, fmt=0, d_src=P, n=n, d_act=8 * P, d_dst=2 * P, dst_capacity=10 ** 6, d_out_bytes=P,
+              d_ws=P, ws_bytes=10 ** 6, stream=None)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return cdma.cdma_relu_compress(*a.values())
+
+    assert call(fmt=3) == 1                        # unknown format
+    assert call(algo=2) == 1
+    assert call(d_act=8 * P + 4) == 1              # misaligned dense output
+    assert call(d_act=P + 16) == 1                 # overlaps the input
+    assert call(d_act=2 * P - 16) == 1             # overlaps the stream
+    assert call(dst_capacity=4 * 32 + 4 * n - 1) == 2
+    assert call(fmt=1, dst_capacity=4 * 32 + 2 * n - 1) == 2  # fp16: 2-byte elements
+    assert call(d_src=P + 8) == 1

@@ -35,7 +35,27 @@ MUTANTS = {
     "rle_values_before_runs": ("uint64_t vpos = rpos + 2 * p;", "uint64_t vpos = rpos;"),
     "zvc_decode_bit_reversed": ("if ((mask >> (idx % 32)) & 1u)", "if ((mask >> (31 - idx % 32)) & 1u)"),
     "zvc_past_n_check_shifted": ("if (last >> (n % 32))", "if (last >> (n % 32 + 1))"),
+    "relu_nan_not_kept": ("uint64_t y = (sign && !is_nan) ? 0 : v;", "uint64_t y = sign ? 0 : v;"),
+    "relu_inf_taken_for_nan": ("&& mantissa != 0;", "&& mantissa == 0;"),
+    "relu_bf16_with_fp16_fields": ("else if (fmt == 2) { esz = 2; exp_bits = 8; man_bits = 7; }",
+                                   "else if (fmt == 2) { esz = 2; exp_bits = 5; man_bits = 10; }"),
+    "relu_sign_bit_one_low": ("uint64_t sign = v >> (exp_bits + man_bits);",
+                              "uint64_t sign = v >> (exp_bits + man_bits - 1);"),
 }
+
+
+def _relu_pins_pass(lib) -> bool:
+    from test_oracle_pins import RELU_HAND, relu_numpy
+    for fmt, table in RELU_HAND.items():
+        dt = np.uint32 if fmt == oracle.FMT_F32 else np.uint16
+        x = np.array([a for a, _ in table], dtype=dt)
+        if not np.array_equal(oracle.relu(x, fmt, lib), np.array([b for _, b in table], dtype=dt)):
+            return False
+    for fmt in (oracle.FMT_F16, oracle.FMT_BF16):
+        x = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+        if not np.array_equal(oracle.relu(x, fmt, lib), relu_numpy(x, fmt)):
+            return False
+    return True
 
 
 def _pins_pass(lib) -> bool:
@@ -73,6 +93,8 @@ def _pins_pass(lib) -> bool:
         bad[0] |= 0x08
         bad = np.concatenate([bad, bad[4:8]])
         if not (oracle.zvc_decompress(bad, 3, 4, lib)[1] & oracle.E_MASK_PAST_N):
+            return False
+        if not _relu_pins_pass(lib):
             return False
     except Exception:
         return False

@@ -380,3 +380,73 @@ def test_restore_reports_a_bad_chunk():
     out, err = oracle.restore(bad, sizes, x.size, 4, 4096)
     assert err & oracle.E_SIZE
     assert np.array_equal(out[:4096], x[:4096]) and np.array_equal(out[8192:], x[8192:])
+
+
+# --------------------------------------------------------------------------
+# ReLU of the producing layer (fused epilogue): max(x, 0) on IEEE patterns
+# --------------------------------------------------------------------------
+
+# (pattern, ReLU pattern) worked by hand from the IEEE-754 field layouts:
+# binary32 = 1 sign, 8 exponent, 23 mantissa bits; binary16 = 1/5/10;
+# bfloat16 = 1/8/7 (the top half of a binary32).
+RELU_HAND = {
+    oracle.FMT_F32: [(0xBF800000, 0), (0x40000000, 0x40000000), (0x80000000, 0), (0x00000000, 0),
+                     (0x7FC00000, 0x7FC00000), (0xFFC00001, 0xFFC00001), (0xFF800000, 0),
+                     (0x7F800000, 0x7F800000), (0x80000001, 0), (0x00000001, 0x00000001),
+                     (0xFF800001, 0xFF800001), (0xC2C80000, 0)],
+    oracle.FMT_F16: [(0xBC00, 0), (0x3C00, 0x3C00), (0x8000, 0), (0x7E00, 0x7E00), (0xFE01, 0xFE01),
+                     (0xFC00, 0), (0x7C00, 0x7C00), (0x8001, 0), (0x0001, 0x0001), (0xFC01, 0xFC01),
+                     (0xFF80, 0xFF80)],
+    oracle.FMT_BF16: [(0xBF80, 0), (0x3F80, 0x3F80), (0x8000, 0), (0x7FC0, 0x7FC0), (0xFFC1, 0xFFC1),
+                      (0xFF80, 0), (0x7F80, 0x7F80), (0x8001, 0), (0x0001, 0x0001), (0xFF81, 0xFF81),
+                      (0xFC00, 0)],
+}
+
+
+def relu_numpy(bits: np.ndarray, fmt: int) -> np.ndarray:
+    """The same rule with library float compares: keep x where x is NaN or
+    x > 0, else +0.0 (bf16 widened exactly to binary32 by a 16-bit shift)."""
+    if fmt == oracle.FMT_F32:
+        f = bits.view(np.float32)
+    elif fmt == oracle.FMT_F16:
+        f = bits.view(np.float16)
+    else:
+        f = (bits.astype(np.uint32) << 16).view(np.float32)
+    with np.errstate(invalid="ignore"):
+        keep = np.isnan(f) | (f > 0)
+    return np.where(keep, bits, np.zeros_like(bits))
+
+
+@pytest.mark.parametrize("fmt", [oracle.FMT_F32, oracle.FMT_F16, oracle.FMT_BF16])
+def test_relu_hand_worked(fmt):
+    dt = np.uint32 if fmt == oracle.FMT_F32 else np.uint16
+    x = np.array([a for a, _ in RELU_HAND[fmt]], dtype=dt)
+    want = np.array([b for _, b in RELU_HAND[fmt]], dtype=dt)
+    assert np.array_equal(oracle.relu(x, fmt), want)
+    assert np.array_equal(relu_numpy(x, fmt), want)
+
+
+@pytest.mark.parametrize("fmt", [oracle.FMT_F16, oracle.FMT_BF16])
+def test_relu_every_16bit_pattern(fmt):
+    x = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    assert np.array_equal(oracle.relu(x, fmt), relu_numpy(x, fmt))
+
+
+def test_relu_fp32_sampled_and_all_exponents():
+    rng = np.random.default_rng(5)
+    x = rng.integers(0, 1 << 32, size=1 << 20, dtype=np.uint64).astype(np.uint32)
+    # every exponent with mantissas 0, 1 and all ones, both signs
+    e = np.arange(256, dtype=np.uint32) << 23
+    extra = np.concatenate([e, e | 1, e | 0x7FFFFF])
+    x = np.concatenate([x, extra, extra | 0x80000000])
+    assert np.array_equal(oracle.relu(x, oracle.FMT_F32), relu_numpy(x, oracle.FMT_F32))
+
+
+def test_relu_then_zvc_is_the_stream_of_the_relu_map():
+    """The fused epilogue's expected stream: ZVC of ReLU(x); its size obeys the
+    closed form with nnz counted by numpy's float compare."""
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal(10000).astype(np.float32)
+    y = oracle.relu(x.view(np.uint32), oracle.FMT_F32)
+    nnz = int(np.count_nonzero(x > 0))
+    assert oracle.zvc_compress(y).size == 4 * ((x.size + 31) // 32) + 4 * nnz
