@@ -146,9 +146,9 @@ def summarize_traffic(fetch_dir: str, write_dir: str, out: str, command: str, ca
     for k, v in sorted(per.items()):
         fb, wb = statistics.mean(a for a, _ in v), statistics.mean(b for _, b in v)
         lines.append(f"| `{k}` | {fb / 1e9:.4f} | {wb / 1e9:.4f} | {(fb + wb) / 1e9:.4f} |")
-    comp = [a + b for k, v in per.items() if "zvc_compress_kernel<4>" in k for a, b in v]
+    comp = [a + b for k, v in per.items() if "zvc_compress_kernel<4, 0>" in k for a, b in v]
     lines += ["", "Machine-readable (read by bench.py; valid only for the kernel source hashed here):", "",
-              f"- kernel: `zvc_compress_kernel<4>`",
+              f"- kernel: `zvc_compress_kernel<4, 0>`",
               f"- hbm_bytes_per_launch: `{statistics.mean(comp):.0f}`",
               f"- kernel_source_sha256: `{kernel_source_hash()}`", ""]
     with open(out, "w") as f:
