@@ -130,7 +130,7 @@ int cdma_compress(int algo, int esz, const void *d_src, uint64_t n,
 /*
  * Fused producer epilogue: compress ReLU(x) straight from the pre-activation
  * values x, and optionally write ReLU(x) densely too.  The page compresses
- * activation maps on the fly as they leave GPU memory (§I, §V.B); on a GPU the
+ * activation maps while they are transferred out of GPU memory (§I, §V.B); on a GPU the
  * nearest equivalent is for the kernel that makes the activations to code
  * them as it writes them, so the map is not read a second time.  ReLU is
  * max(x, 0) on the element's pattern: a value with the sign bit set that is

@@ -1,8 +1,8 @@
 """Fused ReLU + compression on the GPU: the stream must be byte for byte the
 oracle's stream of ReLU(x), and the dense output the oracle's ReLU(x)
 ("Compressing DMA Engine: Leveraging Activation Sparsity for Training Deep
-Neural Networks", §I and §V.B: activation maps are compressed on the fly as
-they leave GPU memory; §V.A: ZVC and run-length coding)."""
+Neural Networks", §I and §V.B: activation maps are compressed while they
+are being moved out of GPU memory; §V.A: ZVC and run-length coding)."""
 
 import numpy as np
 import pytest
