@@ -196,6 +196,42 @@ def cpu_baseline(x_dev, sample: int):
 
 
 # ----------------------------------------------------------------------------
+# layout study: the same maps in three layouts, both codecs
+# ----------------------------------------------------------------------------
+
+def layout_study(max_elems: int) -> int:
+    """One JSON line per (workload, layout) with both codecs' compressed sizes
+    and ratios, computed by the HIP library on the device; the layout change
+    itself is input preparation (a torch permute of the NCHW map)."""
+    import numpy as np
+    import torch
+    import sparse_activation_compression_amd as cdma
+    from synth import LAYOUTS, WORKLOADS, workload
+
+    dev = torch.device("cuda:0")
+    names = [k for k, v in WORKLOADS.items() if v["kind"] in ("clustered", "iid")]
+    for name in names:
+        x = workload(name, scale_n=max_elems)
+        sig = x.view(np.int32 if x.dtype.itemsize == 4 else np.int16)
+        xd = torch.from_numpy(sig).to(dev)
+        row = {"workload": name, "shape_nchw": list(x.shape), "elements": int(x.size),
+               "bytes": int(x.nbytes)}
+        for layout, perm in LAYOUTS.items():
+            y = xd.permute(*perm).contiguous().view(-1)
+            sizes = {}
+            for algo in ("zvc", "rle"):
+                _, nb = cdma.compress(y, algo)
+                torch.cuda.synchronize()
+                sizes[algo] = int(nb.item())
+            row[layout] = {a: {"bytes": b, "ratio": round(x.nbytes / b, 4)} for a, b in sizes.items()}
+            del y
+        print(json.dumps(row), flush=True)
+        del xd
+        torch.cuda.empty_cache()
+    return 0
+
+
+# ----------------------------------------------------------------------------
 # the benchmark
 # ----------------------------------------------------------------------------
 
@@ -210,6 +246,10 @@ def main() -> int:
                     help="time the four codec kernels only (no offload stage); for counter runs")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain device copy of known size (counter calibration)")
+    ap.add_argument("--layout-study", action="store_true",
+                    help="ZVC and RLE ratios of the CNN-like workloads in NCHW, NHWC and CHWN, then exit")
+    ap.add_argument("--layout-elems", type=int, default=1 << 25,
+                    help="elements per workload in the layout study (the batch is cut to fit)")
     ap.add_argument("--summarize-profile", metavar="DIR")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--out")
@@ -233,6 +273,9 @@ def main() -> int:
     __graft_entry__.ensure_built()
     import sparse_activation_compression_amd as cdma
     from synth import SWEEP_SEEDS, SWEEP_ZERO_FRACTIONS, sweep_bits_device
+
+    if args.layout_study:
+        return layout_study(args.layout_elems)
 
     dev = torch.device("cuda:0")
     s = args.zero_frac

@@ -15,5 +15,7 @@ from .activations import (  # noqa: F401
     SWEEP_ZERO_FRACTIONS,
     SWEEP_SEEDS,
     WORKLOADS,
+    LAYOUTS,
+    to_layout,
     workload,
 )

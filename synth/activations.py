@@ -277,3 +277,19 @@ def workload(name: str, scale_n: int | None = None) -> np.ndarray:
         n = shape[0] if scale_n is None else min(shape[0], scale_n)
         x = sweep_bits_host(0, n, spec["zero_frac"], spec["seed"]).view(np.float32)
     return x
+
+
+# ---------------------------------------------------------------------------
+# Activation layouts (for the layout study)
+# ---------------------------------------------------------------------------
+#
+# The page compares the codecs over three activation layouts without naming
+# them (§VII.A); the three common ones for CNN activations are taken: NCHW
+# (the maps' own order, §II.B), NHWC and CHWN.  Each entry is the axis order,
+# as indices into NCHW.
+LAYOUTS = {"NCHW": (0, 1, 2, 3), "NHWC": (0, 2, 3, 1), "CHWN": (1, 2, 3, 0)}
+
+
+def to_layout(x_nchw: np.ndarray, layout: str) -> np.ndarray:
+    """The same values laid out contiguously in ``layout`` (host, numpy)."""
+    return np.ascontiguousarray(np.transpose(x_nchw, LAYOUTS[layout]))
