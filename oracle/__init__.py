@@ -65,15 +65,15 @@ def load(path: str | None = None):
     lib = ctypes.CDLL(p)
     u64, u32p, u64p = ctypes.c_uint64, ctypes.POINTER(ctypes.c_uint32), ctypes.POINTER(ctypes.c_uint64)
     vp = ctypes.c_void_p
-    for name in ("oracle_zvc_size", "oracle_rle_size"):
+    for name in ("oracle_zvc_size", "oracle_rle_size", "oracle_zvci_size"):
         f = getattr(lib, name)
         f.restype = u64
         f.argtypes = [vp, u64, ctypes.c_int]
-    for name in ("oracle_zvc_compress", "oracle_rle_compress"):
+    for name in ("oracle_zvc_compress", "oracle_rle_compress", "oracle_zvci_compress"):
         f = getattr(lib, name)
         f.restype = ctypes.c_int
         f.argtypes = [vp, u64, ctypes.c_int, vp, u64, u64p]
-    for name in ("oracle_zvc_decompress", "oracle_rle_decompress"):
+    for name in ("oracle_zvc_decompress", "oracle_rle_decompress", "oracle_zvci_decompress"):
         f = getattr(lib, name)
         f.restype = ctypes.c_int
         f.argtypes = [vp, u64, u64, ctypes.c_int, vp, u32p]
@@ -146,6 +146,27 @@ def rle_decompress(stream, n: int, esz: int, lib=None):
     return _decompress("oracle_rle_decompress", stream, n, esz, lib or load())
 
 
+def max_zvci_bytes(n: int, esz: int) -> int:
+    E = 4096 // esz
+    return 4 * ((n + E - 1) // E + 1) + 4 * ((n + 31) // 32) + esz * n
+
+
+def zvci_compress(x, lib=None) -> np.ndarray:
+    """Interleaved ZVC stream (per window: mask, then its nonzeros; a u32
+    nonzero-count index per 4 KB block in front) of the patterns of ``x``."""
+    return _compress("oracle_zvci_compress", x, max_zvci_bytes, lib or load())
+
+
+def zvci_decompress(stream, n: int, esz: int, lib=None):
+    """(patterns, error bits) decoded from an interleaved ZVC stream."""
+    return _decompress("oracle_zvci_decompress", stream, n, esz, lib or load())
+
+
+def zvci_size(x, lib=None) -> int:
+    b = _bits(x)
+    return int((lib or load()).oracle_zvci_size(b.ctypes.data, b.size, b.dtype.itemsize))
+
+
 def zvc_size(x, lib=None) -> int:
     b = _bits(x)
     return int((lib or load()).oracle_zvc_size(b.ctypes.data, b.size, b.dtype.itemsize))
@@ -161,7 +182,7 @@ def offload_stream(x, chunk_elems: int, algo: str = "zvc", lib=None):
     chunks of ``chunk_elems`` elements, each compressed on its own, laid back
     to back, plus each chunk's byte count."""
     b = _bits(x)
-    comp = zvc_compress if algo == "zvc" else rle_compress
+    comp = {"zvc": zvc_compress, "rle": rle_compress, "zvci": zvci_compress}[algo]
     parts = [comp(b[lo: lo + chunk_elems], lib) for lo in range(0, b.size, chunk_elems)]
     sizes = [p.size for p in parts]
     return (np.concatenate(parts) if parts else np.zeros(0, np.uint8)), sizes
@@ -173,7 +194,7 @@ def restore(image, chunk_bytes, n: int, esz: int, chunk_elems: int, algo: str = 
     ``chunk_bytes[k]`` bytes of ``image``.  Returns (patterns, OR of every
     chunk's error bits)."""
     img = np.ascontiguousarray(np.asarray(image, dtype=np.uint8))
-    dec = zvc_decompress if algo == "zvc" else rle_decompress
+    dec = {"zvc": zvc_decompress, "rle": rle_decompress, "zvci": zvci_decompress}[algo]
     out = np.zeros(n, dtype=np.uint32 if esz == 4 else np.uint16)
     err, off = 0, 0
     for k, size in enumerate(chunk_bytes):

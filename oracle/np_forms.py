@@ -95,3 +95,30 @@ def rle_decompress(stream, n: int, esz: int) -> np.ndarray:
         seg[kind] = vals
         out[w * E: w * E + seg.size] = seg
     return out
+
+
+def zvci_from_zvc(zvc_stream, n: int, esz: int) -> np.ndarray:
+    """The interleaved stream as a rearrangement of the masks-then-values
+    stream (the two hold the same masks and the same values): window w's mask
+    is followed by its popcount(mask_w) values; a u32 index of nonzeros before
+    each 4 KB block (np.cumsum of the per-block popcounts) goes in front."""
+    s = np.asarray(zvc_stream, dtype=np.uint8)
+    W = (n + 31) // 32
+    E = 4096 // esz
+    wr = (n + E - 1) // E
+    masks = s[: 4 * W].view("<u4")
+    counts = np.unpackbits(masks.view(np.uint8), bitorder="little").reshape(W, 32).sum(axis=1).astype(np.int64)
+    vals = s[4 * W:].reshape(-1, esz)
+    starts = np.concatenate([np.zeros(1, np.int64), np.cumsum(counts)])
+    parts = []
+    for w in range(W):
+        parts.append(masks[w: w + 1].view(np.uint8))
+        parts.append(vals[starts[w]: starts[w + 1]].reshape(-1))
+    per_block = np.add.reduceat(counts, np.arange(0, W, E // 32)) if W else np.zeros(0, np.int64)
+    index = np.concatenate([np.zeros(1, np.int64), np.cumsum(per_block)]).astype("<u4")
+    return np.concatenate([index.view(np.uint8)] + parts) if W else index.view(np.uint8)
+
+
+def zvci_compress(x) -> np.ndarray:
+    b = _bits(x)
+    return zvci_from_zvc(zvc_compress(b), b.size, b.dtype.itemsize)

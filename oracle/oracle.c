@@ -315,6 +315,111 @@ int oracle_rle_decompress(const uint8_t *src, uint64_t src_bytes, uint64_t n, in
     return OR_OK;
 }
 
+/* ---- ZVC, per-window interleaved form with a block index ----------------- */
+/*
+ * The page's literal description of ZVC (§V.A): a window's 32-bit mask is
+ * followed by that window's nonzero values.  Windows follow each other in
+ * order; an index of u32 val_off[Wr+1] (nonzeros before each block of
+ * E = 4096/esz elements, the 4 KB window of §VII.A; entry Wr = the total) lets
+ * each block be found without reading the ones before it:
+ *     [u32 val_off[Wr+1]] [mask_0][values_0] [mask_1][values_1] ...
+ *     block b starts at 4(Wr+1) + 4 * b * (E/32) + esz * val_off[b]
+ *     size = 4(Wr+1) + 4 * ceil(n/32) + esz * nnz.
+ */
+static uint64_t zvci_block(int esz) { return (uint64_t)(4096 / esz); } /* elements per 4 KB */
+
+uint64_t oracle_zvci_size(const void *src, uint64_t n, int esz)
+{
+    uint64_t E = zvci_block(esz), Wr = (n + E - 1) / E, nnz = 0;
+    for (uint64_t i = 0; i < n; i++)
+        if (elem(src, i, esz) != 0)
+            nnz++;
+    return 4 * (Wr + 1) + 4 * ((n + 31) / 32) + (uint64_t)esz * nnz;
+}
+
+int oracle_zvci_compress(const void *src, uint64_t n, int esz,
+                         uint8_t *dst, uint64_t capacity, uint64_t *out_bytes)
+{
+    if (!esz_ok(esz) || !out_bytes)
+        return OR_ERR_ARG;
+    uint64_t size = oracle_zvci_size(src, n, esz);
+    *out_bytes = size;
+    if (size > capacity)
+        return OR_ERR_CAPACITY;
+    uint64_t E = zvci_block(esz), Wr = (n + E - 1) / E, W = (n + 31) / 32;
+    uint64_t pos = 4 * (Wr + 1), nnz = 0;
+    for (uint64_t w = 0; w < W; w++) {
+        if ((32 * w) % E == 0)
+            put_le(dst + 4 * ((32 * w) / E), nnz, 4); /* val_off of the block w opens */
+        uint32_t mask = 0;
+        for (int i = 31; i >= 0; i--) { /* bit i <-> element 32w + i */
+            uint64_t idx = 32 * w + (uint64_t)i;
+            mask <<= 1;
+            if (idx < n && elem(src, idx, esz))
+                mask |= 1u;
+        }
+        put_le(dst + pos, mask, 4);
+        pos += 4;
+        for (int i = 0; i < 32; i++) {
+            uint64_t idx = 32 * w + (uint64_t)i;
+            if ((mask >> i) & 1u) {
+                put_le(dst + pos, elem(src, idx, esz), esz);
+                pos += (uint64_t)esz;
+                nnz++;
+            }
+        }
+    }
+    put_le(dst + 4 * Wr, nnz, 4);
+    return OR_OK;
+}
+
+int oracle_zvci_decompress(const uint8_t *src, uint64_t src_bytes, uint64_t n, int esz,
+                           void *dst, uint32_t *err)
+{
+    if (!esz_ok(esz) || !err)
+        return OR_ERR_ARG;
+    uint8_t *out = (uint8_t *)dst;
+    uint64_t E = zvci_block(esz), Wr = (n + E - 1) / E, W = (n + 31) / 32;
+    uint64_t hdr = 4 * (Wr + 1), wpb = E / 32;
+    uint32_t e = 0;
+    for (uint64_t i = 0; i < n * (uint64_t)esz; i++)
+        out[i] = 0;
+    if (get_stream(src, src_bytes, 0, 4) != 0)
+        e |= OR_E_INDEX;
+    for (uint64_t b = 0; b < Wr; b++) {
+        uint64_t v0 = get_stream(src, src_bytes, 4 * b, 4);
+        uint64_t v1 = get_stream(src, src_bytes, 4 * (b + 1), 4);
+        if (v1 < v0) {
+            e |= OR_E_INDEX;
+            continue;
+        }
+        /* every block is decoded from its own index entry */
+        uint64_t pos = hdr + 4 * b * wpb + (uint64_t)esz * v0, count = 0;
+        for (uint64_t w = b * wpb; w < W && w < (b + 1) * wpb; w++) {
+            uint32_t mask = (uint32_t)get_stream(src, src_bytes, pos, 4);
+            pos += 4;
+            for (int i = 0; i < 32; i++) {
+                if (!((mask >> i) & 1u))
+                    continue;
+                uint64_t idx = 32 * w + (uint64_t)i;
+                count++;
+                if (idx >= n) {
+                    e |= OR_E_MASK_PAST_N;
+                    continue;
+                }
+                put_le(out + idx * (uint64_t)esz, get_stream(src, src_bytes, pos, esz), esz);
+                pos += (uint64_t)esz;
+            }
+        }
+        if (count != v1 - v0)
+            e |= OR_E_VAL_COUNT;
+    }
+    if (hdr + 4 * W + (uint64_t)esz * get_stream(src, src_bytes, 4 * Wr, 4) != src_bytes)
+        e |= OR_E_SIZE;
+    *err = e;
+    return OR_OK;
+}
+
 /* ---- ReLU of the producing layer (fused epilogue) ------------------------ */
 /*
  * ReLU(x) = max(x, 0), written out on the element's sign, exponent and

@@ -35,6 +35,11 @@ MUTANTS = {
     "rle_values_before_runs": ("uint64_t vpos = rpos + 2 * p;", "uint64_t vpos = rpos;"),
     "zvc_decode_bit_reversed": ("if ((mask >> (idx % 32)) & 1u)", "if ((mask >> (31 - idx % 32)) & 1u)"),
     "zvc_past_n_check_shifted": ("if (last >> (n % 32))", "if (last >> (n % 32 + 1))"),
+    "zvci_index_counts_windows": ("put_le(dst + 4 * ((32 * w) / E), nnz, 4);", "put_le(dst + 4 * ((32 * w) / E), w, 4);"),
+    "zvci_mask_bits_reversed": ("mask <<= 1;\n            if (idx < n && elem(src, idx, esz))\n                mask |= 1u;",
+                                "mask >>= 1;\n            if (idx < n && elem(src, idx, esz))\n                mask |= 0x80000000u;"),
+    "zvci_decode_block_skips_masks": ("uint64_t pos = hdr + 4 * b * wpb + (uint64_t)esz * v0, count = 0;",
+                                      "uint64_t pos = hdr + (uint64_t)esz * v0, count = 0;"),
     "relu_nan_not_kept": ("uint64_t y = (sign && !is_nan) ? 0 : v;", "uint64_t y = sign ? 0 : v;"),
     "relu_inf_taken_for_nan": ("&& mantissa != 0;", "&& mantissa == 0;"),
     "relu_bf16_with_fp16_fields": ("else if (fmt == 2) { esz = 2; exp_bits = 8; man_bits = 7; }",
@@ -62,8 +67,10 @@ def _pins_pass(lib) -> bool:
     """True iff every independent pin passes against ``lib``."""
     try:
         for c in golden_io.all_cases():
-            comp = oracle.zvc_compress if c["algo"] == "zvc" else oracle.rle_compress
-            dec = oracle.zvc_decompress if c["algo"] == "zvc" else oracle.rle_decompress
+            comp = {"zvc": oracle.zvc_compress, "rle": oracle.rle_compress,
+                    "zvci": oracle.zvci_compress}[c["algo"]]
+            dec = {"zvc": oracle.zvc_decompress, "rle": oracle.rle_decompress,
+                   "zvci": oracle.zvci_decompress}[c["algo"]]
             if bytes(comp(c["x"], lib)) != bytes(c["stream"]):
                 return False
             out, err = dec(c["stream"], c["n"], c["esz"], lib)

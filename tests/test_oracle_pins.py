@@ -33,28 +33,31 @@ CASES = golden_io.all_cases()
 # hand-worked streams
 # --------------------------------------------------------------------------
 
+C_COMP = {"zvc": oracle.zvc_compress, "rle": oracle.rle_compress, "zvci": oracle.zvci_compress}
+C_DEC = {"zvc": oracle.zvc_decompress, "rle": oracle.rle_decompress, "zvci": oracle.zvci_decompress}
+NP_COMP = {"zvc": np_forms.zvc_compress, "rle": np_forms.rle_compress, "zvci": np_forms.zvci_compress}
+
+
 @pytest.mark.parametrize("case", CASES, ids=[c["name"] for c in CASES])
 def test_golden_stream_c_oracle(case):
-    comp = oracle.zvc_compress if case["algo"] == "zvc" else oracle.rle_compress
-    s = comp(case["x"])
+    s = C_COMP[case["algo"]](case["x"])
     assert s.size == case["size"]
     assert bytes(s) == bytes(case["stream"])
 
 
 @pytest.mark.parametrize("case", CASES, ids=[c["name"] for c in CASES])
 def test_golden_stream_numpy_form(case):
-    comp = np_forms.zvc_compress if case["algo"] == "zvc" else np_forms.rle_compress
-    assert bytes(comp(case["x"])) == bytes(case["stream"])
+    assert bytes(NP_COMP[case["algo"]](case["x"])) == bytes(case["stream"])
 
 
 @pytest.mark.parametrize("case", CASES, ids=[c["name"] for c in CASES])
 def test_golden_decode(case):
-    dec = oracle.zvc_decompress if case["algo"] == "zvc" else oracle.rle_decompress
-    out, err = dec(case["stream"], case["n"], case["esz"])
+    out, err = C_DEC[case["algo"]](case["stream"], case["n"], case["esz"])
     assert err == 0
     assert np.array_equal(out, case["x"])
-    ndec = np_forms.zvc_decompress if case["algo"] == "zvc" else np_forms.rle_decompress
-    assert np.array_equal(ndec(case["stream"], case["n"], case["esz"]), case["x"])
+    if case["algo"] != "zvci":
+        ndec = np_forms.zvc_decompress if case["algo"] == "zvc" else np_forms.rle_decompress
+        assert np.array_equal(ndec(case["stream"], case["n"], case["esz"]), case["x"])
 
 
 # --------------------------------------------------------------------------
@@ -450,3 +453,55 @@ def test_relu_then_zvc_is_the_stream_of_the_relu_map():
     y = oracle.relu(x.view(np.uint32), oracle.FMT_F32)
     nnz = int(np.count_nonzero(x > 0))
     assert oracle.zvc_compress(y).size == 4 * ((x.size + 31) // 32) + 4 * nnz
+
+
+# --------------------------------------------------------------------------
+# interleaved ZVC (per window: mask then values; 4 KB block index)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("esz", [4, 2])
+@pytest.mark.parametrize("n", [1, 31, 32, 33, 1023, 1024, 1025, 2048, 2049, 5000, 3 * 2048 + 7])
+def test_zvci_c_equals_rearranged_zvc_and_closed_form(esz, n):
+    """The interleaved stream is the masks-then-values stream rearranged
+    window by window (np_forms builds it from the packbits form), and its size
+    is 4(Wr+1) + 4*ceil(n/32) + esz*nnz with nnz counted by numpy."""
+    rng = np.random.default_rng(n * 7 + esz)
+    dt = np.uint32 if esz == 4 else np.uint16
+    x = rng.integers(1, 2 ** (8 * esz), size=n, dtype=np.uint64).astype(dt)
+    x[rng.random(n) < 0.6] = 0
+    x[n // 3: n // 2] = 0
+    s = oracle.zvci_compress(x)
+    assert bytes(s) == bytes(np_forms.zvci_compress(x))
+    E = 4096 // esz
+    nnz = int(np.count_nonzero(x))
+    assert s.size == 4 * ((n + E - 1) // E + 1) + 4 * ((n + 31) // 32) + esz * nnz == oracle.zvci_size(x)
+    # same masks and values as the masks-then-values stream, so the same payload size
+    assert s.size - 4 * ((n + E - 1) // E + 1) == oracle.zvc_compress(x).size
+    out, err = oracle.zvci_decompress(s, n, esz)
+    assert err == 0 and np.array_equal(out, x)
+
+
+def test_zvci_round_trips_special_patterns():
+    x = np.array([0x80000000, 0, 1, 0x7FC00001, 0xFF800000, 0, 0x00800000] * 400, dtype=np.uint32)
+    out, err = oracle.zvci_decompress(oracle.zvci_compress(x), x.size, 4)
+    assert err == 0 and np.array_equal(out, x)
+
+
+def test_zvci_corruptions_are_reported():
+    x = np.zeros(3000, dtype=np.uint32)
+    x[::5] = 9
+    s = oracle.zvci_compress(x)  # Wr = 3 blocks, index = 16 bytes
+    n = x.size
+    bad = s.copy()
+    bad[4:8] = np.frombuffer(np.uint32(1 << 20).tobytes(), np.uint8)  # val_off[1] too large
+    assert oracle.zvci_decompress(bad, n, 4)[1] & oracle.E_INDEX or \
+        oracle.zvci_decompress(bad, n, 4)[1] & oracle.E_VAL_COUNT
+    bad = s.copy()
+    bad[16] |= 0x02  # window 0 claims element 1, which is zero: one value too many
+    assert oracle.zvci_decompress(bad, n, 4)[1] & oracle.E_VAL_COUNT
+    assert oracle.zvci_decompress(s[:-4], n, 4)[1] & oracle.E_SIZE
+    y = np.array([5, 0, 0], dtype=np.uint32)
+    t = oracle.zvci_compress(y)  # index [0, 1], mask 0x1, value 5
+    bad = np.concatenate([t, t[-4:]])
+    bad[8] |= 0x10  # bit 4 of the only window: element 4 >= n
+    assert oracle.zvci_decompress(bad, 3, 4)[1] & oracle.E_MASK_PAST_N
