@@ -294,8 +294,7 @@ def main() -> int:
     rdst = torch.empty(rcap, dtype=torch.uint8, device=dev)
     zsz = torch.zeros(1, dtype=torch.int64, device=dev)
     rsz = torch.zeros(1, dtype=torch.int64, device=dev)
-    ws = torch.empty(max(cdma.cdma_workspace_bytes(0, 4, n), cdma.cdma_workspace_bytes(1, 4, n)),
-                     dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(cdma.cdma_workspace_bytes(a, 4, n) for a in (0, 1, 2)), dtype=torch.uint8, device=dev)
     zout = torch.empty_like(x)
     rout = torch.empty_like(x)
     zerr = torch.zeros(1, dtype=torch.int32, device=dev)
@@ -424,12 +423,45 @@ def main() -> int:
                  "unfused": "torch.clamp_min then zvc compress", "ok": bool(fused_ok)}
         del pre, act, fdst
 
+    # interleaved ZVC (each window's mask in front of its values, plus the
+    # 4 KB block index), compress and decompress, timed after the steps
+    inter = {}
+    if not args.rows_only:
+        idst = torch.empty(cdma.cdma_max_compressed_bytes(2, 4, n), dtype=torch.uint8, device=dev)
+        isz = torch.zeros(1, dtype=torch.int64, device=dev)
+        iout = torch.empty_like(x)
+        ierr = torch.zeros(1, dtype=torch.int32, device=dev)
+        tc, td = [], []
+        for r in range(max(1, args.warmup) + 5):
+            torch.cuda._sleep(SPIN_CYCLES)
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record(stream)
+            cdma.compress(x, "zvci", dst=idst, out_bytes=isz, ws=ws)
+            e[1].record(stream)
+            cdma.decompress(idst, n, 4, "zvci", src_bytes=isz, out=iout, error=ierr, ws=ws)
+            e[2].record(stream)
+            e[2].synchronize()
+            if r >= max(1, args.warmup):
+                tc.append(e[0].elapsed_time(e[1]) * 1e3)
+                td.append(e[1].elapsed_time(e[2]) * 1e3)
+        Wr = (n + 1023) // 1024
+        isize = int(isz.item())
+        i_alg = 4 * n + 4 * (Wr + 1) + 4 * W + 4 * nnz
+        inter_ok = isize == i_alg - 4 * n and int(ierr.item()) == 0 and torch.equal(iout, x)
+        for k, v in (("zvci_compress", tc), ("zvci_decompress", td)):
+            us = statistics.median(v)
+            inter[k] = {"us": round(us, 1), "gbs_uncompressed": round(4 * n / us / 1e3, 1),
+                        "gbs_algorithmic": round(i_alg / us / 1e3, 1),
+                        "hbm_frac": round(i_alg / us / 1e3 / PEAK_HBM_GBS, 4), "ok": bool(inter_ok),
+                        "timed": "separately, after the steps (not part of ms_per_step)"}
+        del idst, iout
+
     # correctness of what was timed (outside the timed region)
     zsize, rsize = int(zsz.item()), int(rsz.item())
     ok = (zsize == 4 * W + 4 * nnz and int(zerr.item()) == 0 and int(rerr.item()) == 0
           and torch.equal(zout, x) and torch.equal(rout, x) and all(t == off_totals[0] for t in off_totals)
           and (args.rows_only or off_totals[0] == zsize_chunks(x, cdma)) and pre_ok
-          and fused.get("ok", True))
+          and fused.get("ok", True) and all(v["ok"] for v in inter.values()))
 
     # raw PCIe device-to-host copy of the dense buffer, for comparison
     raw = []
@@ -475,6 +507,8 @@ def main() -> int:
 
     if fused:
         rows["relu_zvc_compress"] = dict(fused, timed="separately, after the steps (not part of ms_per_step)")
+
+    rows.update(inter)
 
     ms_per_step = t_total / args.steps * 1e3
     comp_us = statistics.mean(ev_times["zvc_compress"])  # average launch duration

@@ -36,6 +36,12 @@
  *        v_w; entry Wr holds the totals), then block_w for each window: its
  *        p_w u16 entries followed by its v_w nonzero elements.
  *        size = 8*(Wr+1) + 2*sum(p_w) + esz*nnz.
+ *   ZVCI: the same masks and values as ZVC, interleaved as the page describes
+ *        one window (§V.A): per window its u32 mask, then its nonzero
+ *        elements, windows in order.  In front, u32 val_off[Wr+1] with the
+ *        nonzeros before each block of E = 4096/esz elements (entry Wr = nnz),
+ *        so block b starts at 4*(Wr+1) + 4*b*(E/32) + esz*val_off[b] and decodes
+ *        on its own.  size = 4*(Wr+1) + 4*ceil(n/32) + esz*nnz.
  *
  * Ownership.  The caller owns every buffer (sources, destinations,
  * workspaces, scratch, pinned host memory, size and error words) and keeps it
@@ -68,16 +74,18 @@ extern "C" {
 #define CDMA_ERR_HIP         4  /* a HIP runtime call failed */
 
 /* algorithms */
-#define CDMA_ALGO_ZVC 0
-#define CDMA_ALGO_RLE 1
+#define CDMA_ALGO_ZVC  0
+#define CDMA_ALGO_RLE  1
+#define CDMA_ALGO_ZVCI 2  /* ZVC with each window's mask in front of its values */
 
 /* decode error bits, OR-ed into *d_error by cdma_decompress */
-#define CDMA_E_MASK_PAST_N (1u << 0) /* ZVC: mask bit set for an index >= n */
+#define CDMA_E_MASK_PAST_N (1u << 0) /* ZVC, ZVCI: mask bit set for an index >= n */
 #define CDMA_E_SIZE        (1u << 1) /* stream size differs from what it describes,
                                         or the described data lies past src_capacity */
-#define CDMA_E_INDEX       (1u << 3) /* RLE: index does not start at 0 or decreases */
+#define CDMA_E_INDEX       (1u << 3) /* RLE, ZVCI: index does not start at 0 or decreases */
 #define CDMA_E_RUN_SUM     (1u << 4) /* RLE: runs do not sum to the window length */
-#define CDMA_E_VAL_COUNT   (1u << 5) /* RLE: nonzero runs disagree with val_off */
+#define CDMA_E_VAL_COUNT   (1u << 5) /* RLE: nonzero runs, ZVCI: a block's mask bits,
+                                        disagree with val_off */
 #define CDMA_E_RUN_FORM    (1u << 6) /* RLE: zero-length run other than the first, or bad padding */
 #define CDMA_E_INTERNAL    (1u << 7) /* the cross-workgroup scan did not complete (never expected) */
 
@@ -87,13 +95,14 @@ extern "C" {
 
 /* limits on n (elements) */
 #define CDMA_ZVC_MAX_N (1ull << 31)
-#define CDMA_RLE_MAX_N (1ull << 30)
+#define CDMA_RLE_MAX_N (1ull << 30)   /* ZVCI: as ZVC */
 
 /*
  * Upper bound of the compressed size of n elements (the size of an all-dense
  * input), in bytes.  Returns 0 for an invalid algo/esz.
- *   ZVC: 4*ceil(n/32) + esz*n
- *   RLE: 8*(ceil(n/E)+1) + 2*(n + 2*ceil(n/E)) + esz*n
+ *   ZVC:  4*ceil(n/32) + esz*n
+ *   RLE:  8*(ceil(n/E)+1) + 2*(n + 2*ceil(n/E)) + esz*n
+ *   ZVCI: 4*(ceil(n/E)+1) + 4*ceil(n/32) + esz*n
  */
 uint64_t cdma_max_compressed_bytes(int algo, int esz, uint64_t n);
 
@@ -138,6 +147,7 @@ int cdma_compress(int algo, int esz, const void *d_src, uint64_t n,
  * (either sign) and all other values pass unchanged.  NaN is decided on the
  * pattern for the format: fp32 |bits| > 0x7F800000, fp16 > 0x7C00, bf16 >
  * 0x7F80 (|bits| = the pattern without its sign bit).
+ *   algo          CDMA_ALGO_ZVC or CDMA_ALGO_RLE.
  *   fmt           CDMA_FMT_F32 (esz 4), CDMA_FMT_F16 or CDMA_FMT_BF16 (esz 2).
  *   d_src         device, 16-byte aligned, n elements of x, read only.
  *   d_act         device, 16-byte aligned, n elements; receives ReLU(x), or

@@ -14,6 +14,7 @@ kernels; there is no fallback path.
 
 from .binding import (  # noqa: F401
     ALGO_RLE,
+    ALGO_ZVCI,
     ALGO_ZVC,
     CDMA_E_INDEX,
     CDMA_E_MASK_PAST_N,

@@ -17,6 +17,7 @@ _LIB_PATH = os.path.join(_PKG, "libcdma.so")
 
 ALGO_ZVC = 0
 ALGO_RLE = 1
+ALGO_ZVCI = 2
 
 FMT_F32 = 0
 FMT_F16 = 1
@@ -29,7 +30,8 @@ CDMA_E_RUN_SUM = 1 << 4
 CDMA_E_VAL_COUNT = 1 << 5
 CDMA_E_RUN_FORM = 1 << 6
 
-_ALGOS = {"zvc": ALGO_ZVC, "rle": ALGO_RLE, ALGO_ZVC: ALGO_ZVC, ALGO_RLE: ALGO_RLE}
+_ALGOS = {"zvc": ALGO_ZVC, "rle": ALGO_RLE, "zvci": ALGO_ZVCI, ALGO_ZVC: ALGO_ZVC, ALGO_RLE: ALGO_RLE,
+          ALGO_ZVCI: ALGO_ZVCI}
 
 
 class CdmaError(RuntimeError):

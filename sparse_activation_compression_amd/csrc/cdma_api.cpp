@@ -10,14 +10,15 @@
 
 namespace {
 
-bool algo_ok(int algo) { return algo == CDMA_ALGO_ZVC || algo == CDMA_ALGO_RLE; }
+bool algo_ok(int algo) { return algo == CDMA_ALGO_ZVC || algo == CDMA_ALGO_RLE || algo == CDMA_ALGO_ZVCI; }
 bool esz_ok(int esz) { return esz == 2 || esz == 4; }
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
-uint64_t max_n(int algo) { return algo == CDMA_ALGO_ZVC ? CDMA_ZVC_MAX_N : CDMA_RLE_MAX_N; }
+uint64_t max_n(int algo) { return algo == CDMA_ALGO_RLE ? CDMA_RLE_MAX_N : CDMA_ZVC_MAX_N; }
 uint64_t rle_window(int esz) { return 4096u / (unsigned)esz; }
 
 uint64_t tiles(int algo, int esz, uint64_t n) {
-  return algo == CDMA_ALGO_ZVC ? cdma::zvc_tiles(esz, n) : cdma::rle_compress_tiles(esz, n);
+  if (algo == CDMA_ALGO_ZVC) return cdma::zvc_tiles(esz, n);
+  return algo == CDMA_ALGO_RLE ? cdma::rle_compress_tiles(esz, n) : cdma::zvci_compress_tiles(esz, n);
 }
 
 }  // namespace
@@ -28,6 +29,7 @@ uint64_t cdma_max_compressed_bytes(int algo, int esz, uint64_t n) {
   if (!algo_ok(algo) || !esz_ok(esz) || n > max_n(algo)) return 0;
   if (algo == CDMA_ALGO_ZVC) return 4 * ((n + 31) / 32) + (uint64_t)esz * n;
   const uint64_t wr = (n + rle_window(esz) - 1) / rle_window(esz);
+  if (algo == CDMA_ALGO_ZVCI) return 4 * (wr + 1) + 4 * ((n + 31) / 32) + (uint64_t)esz * n;
   return 8 * (wr + 1) + 2 * (n + 2 * wr) + (uint64_t)esz * n;
 }
 
@@ -53,9 +55,10 @@ int cdma_compress(int algo, int esz, const void* d_src, uint64_t n, void* d_dst,
     if (ws_bytes < cdma_workspace_bytes(algo, esz, n)) return CDMA_ERR_CAPACITY;
   }
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  const hipError_t e = algo == CDMA_ALGO_ZVC
-                           ? cdma::zvc_compress_launch(esz, 0, d_src, n, nullptr, d_dst, d_out_bytes, d_ws, s)
-                           : cdma::rle_compress_launch(esz, 0, d_src, n, nullptr, d_dst, d_out_bytes, d_ws, s);
+  const hipError_t e =
+      algo == CDMA_ALGO_ZVC   ? cdma::zvc_compress_launch(esz, 0, d_src, n, nullptr, d_dst, d_out_bytes, d_ws, s)
+      : algo == CDMA_ALGO_RLE ? cdma::rle_compress_launch(esz, 0, d_src, n, nullptr, d_dst, d_out_bytes, d_ws, s)
+                              : cdma::zvci_compress_launch(esz, d_src, n, d_dst, d_out_bytes, d_ws, s);
   return e == hipSuccess ? CDMA_OK : CDMA_ERR_HIP;
 }
 
@@ -63,7 +66,7 @@ int cdma_relu_compress(int algo, int fmt, const void* d_src, uint64_t n, void* d
                        uint64_t dst_capacity, uint64_t* d_out_bytes, void* d_ws, uint64_t ws_bytes, void* stream) {
   if (fmt != CDMA_FMT_F32 && fmt != CDMA_FMT_F16 && fmt != CDMA_FMT_BF16) return CDMA_ERR_INVALID_ARG;
   const int esz = fmt == CDMA_FMT_F32 ? 4 : 2;
-  if (!algo_ok(algo) || n > max_n(algo)) return CDMA_ERR_INVALID_ARG;
+  if ((algo != CDMA_ALGO_ZVC && algo != CDMA_ALGO_RLE) || n > max_n(algo)) return CDMA_ERR_INVALID_ARG;
   if (!d_out_bytes || !aligned(d_out_bytes, 8)) return CDMA_ERR_INVALID_ARG;
   if (!d_dst || !aligned(d_dst, 16)) {
     if (n > 0 || algo == CDMA_ALGO_RLE) return CDMA_ERR_INVALID_ARG;
@@ -105,7 +108,9 @@ int cdma_decompress(int algo, int esz, const void* d_src, uint64_t src_capacity,
   const hipError_t e =
       algo == CDMA_ALGO_ZVC
           ? cdma::zvc_decompress_launch(esz, d_src, src_capacity, d_src_bytes, n, d_dst, d_error, d_ws, s)
-          : cdma::rle_decompress_launch(esz, d_src, src_capacity, d_src_bytes, n, d_dst, d_error, d_ws, s);
+      : algo == CDMA_ALGO_RLE
+          ? cdma::rle_decompress_launch(esz, d_src, src_capacity, d_src_bytes, n, d_dst, d_error, d_ws, s)
+          : cdma::zvci_decompress_launch(esz, d_src, src_capacity, d_src_bytes, n, d_dst, d_error, s);
   return e == hipSuccess ? CDMA_OK : CDMA_ERR_HIP;
 }
 

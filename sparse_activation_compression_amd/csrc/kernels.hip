@@ -5,6 +5,7 @@
 #include "zvc_compress.hpp"
 #include "zvc_decompress.hpp"
 #include "rle_kernels.hpp"
+#include "zvci_kernels.hpp"
 
 namespace cdma {
 
@@ -225,6 +226,74 @@ hipError_t rle_decompress_launch(int esz, const void* src, uint64_t cap, const u
   }
   return esz == 4 ? rle_decompress_t<4>(src, cap, src_bytes, n, dst, error, s)
                   : rle_decompress_t<2>(src, cap, src_bytes, n, dst, error, s);
+}
+
+uint64_t zvci_compress_tiles(int esz, uint64_t n) {
+  const uint64_t te = esz == 4 ? ZviCShape<4>::TE : ZviCShape<2>::TE;
+  return (n + te - 1) / te;
+}
+
+template <int ESZ>
+static hipError_t zvci_compress_t(const void* src, uint64_t n, void* dst, uint64_t* out_bytes, void* ws,
+                                  hipStream_t s) {
+  constexpr int block = ZviCShape<ESZ>::BLOCK;
+  const uint64_t tiles = zvci_compress_tiles(ESZ, n);
+  hipError_t e = clear_workspace(ws, tiles, out_bytes, s);
+  if (e != hipSuccess) return e;
+  auto kern = zvci_compress_kernel<ESZ>;
+  const uint64_t res = resident_groups(reinterpret_cast<const void*>(kern), block);
+  const unsigned grid = (unsigned)(tiles < res ? tiles : res);
+  kern<<<grid, block, 0, s>>>(static_cast<const uint8_t*>(src), n, static_cast<uint8_t*>(dst), out_bytes,
+                              ws_counter(ws), ws_agg(ws), (uint32_t)tiles);
+  return hipGetLastError();
+}
+
+// n = 0: the index of one entry (4 bytes of zeros).
+__global__ void zvci_empty_kernel(uint8_t* dst, uint64_t* out_bytes) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) {
+    reinterpret_cast<uint32_t*>(dst)[0] = 0;
+    *out_bytes = 4;
+  }
+}
+
+hipError_t zvci_compress_launch(int esz, const void* src, uint64_t n, void* dst, uint64_t* out_bytes, void* ws,
+                                hipStream_t s) {
+  if (n == 0) {
+    zvci_empty_kernel<<<1, 64, 0, s>>>(static_cast<uint8_t*>(dst), out_bytes);
+    return hipGetLastError();
+  }
+  return esz == 4 ? zvci_compress_t<4>(src, n, dst, out_bytes, ws, s) : zvci_compress_t<2>(src, n, dst, out_bytes, ws, s);
+}
+
+// n = 0: the stream must be the 4-byte zero index.
+__global__ void zvci_empty_check_kernel(const uint8_t* src, uint64_t cap, const uint64_t* src_bytes,
+                                        uint32_t* error) {
+  if (threadIdx.x != 0 || blockIdx.x != 0 || !error) return;
+  const uint64_t claimed = src_bytes ? *src_bytes : cap;
+  const uint64_t eff = claimed < cap ? claimed : cap;
+  uint32_t idx = 0, e = 0;
+  for (uint64_t b = 0; b < 4 && b < eff; ++b) idx |= src[b];
+  if (idx) e |= CDMA_E_INDEX;
+  if (src_bytes && *src_bytes != 4) e |= CDMA_E_SIZE;
+  if (e) atomicOr(error, e);
+}
+
+hipError_t zvci_decompress_launch(int esz, const void* src, uint64_t cap, const uint64_t* src_bytes, uint64_t n,
+                                  void* dst, uint32_t* error, hipStream_t s) {
+  if (n == 0) {
+    zvci_empty_check_kernel<<<1, 64, 0, s>>>(static_cast<const uint8_t*>(src), cap, src_bytes, error);
+    return hipGetLastError();
+  }
+  const uint64_t E = 4096 / (uint64_t)esz;
+  const uint64_t blocks = (n + E - 1) / E;
+  const unsigned grid = (unsigned)((blocks + kWaves - 1) / kWaves);
+  if (esz == 4)
+    zvci_decompress_kernel<4><<<grid, kBlock, 0, s>>>(static_cast<const uint8_t*>(src), cap, src_bytes, n,
+                                                     static_cast<uint8_t*>(dst), error, grid);
+  else
+    zvci_decompress_kernel<2><<<grid, kBlock, 0, s>>>(static_cast<const uint8_t*>(src), cap, src_bytes, n,
+                                                     static_cast<uint8_t*>(dst), error, grid);
+  return hipGetLastError();
 }
 
 }  // namespace cdma

@@ -14,6 +14,7 @@ uint64_t zvc_tiles(int esz, uint64_t n);           // decompress tiles
 uint64_t zvc_compress_tiles(int esz, uint64_t n);  // compress tiles (fewer, larger)
 uint64_t rle_tiles(int esz, uint64_t n);           // decompress tiles
 uint64_t rle_compress_tiles(int esz, uint64_t n);  // compress tiles (fewer, larger)
+uint64_t zvci_compress_tiles(int esz, uint64_t n);
 
 // op: 0 = plain compression; 1/2/3 = ReLU of fp32/fp16/bf16 patterns coded
 // (and stored densely to act unless it is null).
@@ -25,5 +26,10 @@ hipError_t rle_compress_launch(int esz, int op, const void* src, uint64_t n, voi
                                uint64_t* out_bytes, void* ws, hipStream_t s);
 hipError_t rle_decompress_launch(int esz, const void* src, uint64_t src_capacity, const uint64_t* src_bytes,
                                  uint64_t n, void* dst, uint32_t* error, void* ws, hipStream_t s);
+
+hipError_t zvci_compress_launch(int esz, const void* src, uint64_t n, void* dst, uint64_t* out_bytes, void* ws,
+                                hipStream_t s);
+hipError_t zvci_decompress_launch(int esz, const void* src, uint64_t src_capacity, const uint64_t* src_bytes,
+                                  uint64_t n, void* dst, uint32_t* error, hipStream_t s);
 
 }  // namespace cdma

@@ -144,7 +144,8 @@ int cdma_offload_async(int algo, int esz, const void* d_src, uint64_t n, uint64_
                        void* compute_stream, void* copy_stream, cdma_offload_t* out) {
   if (!out) return CDMA_ERR_INVALID_ARG;
   *out = nullptr;
-  if ((algo != CDMA_ALGO_ZVC && algo != CDMA_ALGO_RLE) || (esz != 2 && esz != 4)) return CDMA_ERR_INVALID_ARG;
+  if ((algo != CDMA_ALGO_ZVC && algo != CDMA_ALGO_RLE && algo != CDMA_ALGO_ZVCI) || (esz != 2 && esz != 4))
+    return CDMA_ERR_INVALID_ARG;
   if (slots < 1 || chunk_elems == 0 || chunk_elems % 2048 != 0) return CDMA_ERR_INVALID_ARG;
   if (cdma_max_compressed_bytes(algo, esz, chunk_elems) == 0) return CDMA_ERR_INVALID_ARG;
   if (compute_stream == copy_stream) return CDMA_ERR_INVALID_ARG;

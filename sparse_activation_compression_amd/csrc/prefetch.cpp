@@ -49,7 +49,8 @@ PrefetchLayout prefetch_layout(int algo, int esz, uint64_t n, uint64_t chunk, in
 }
 
 bool args_ok(int algo, int esz, uint64_t chunk, int slots) {
-  if ((algo != CDMA_ALGO_ZVC && algo != CDMA_ALGO_RLE) || (esz != 2 && esz != 4)) return false;
+  if ((algo != CDMA_ALGO_ZVC && algo != CDMA_ALGO_RLE && algo != CDMA_ALGO_ZVCI) || (esz != 2 && esz != 4))
+    return false;
   if (slots < 1 || chunk == 0 || chunk % 2048 != 0) return false;
   return cdma_max_compressed_bytes(algo, esz, chunk) != 0;
 }
@@ -103,7 +104,7 @@ int cdma_prefetch_async(int algo, int esz, const void* h_src, uint64_t h_src_byt
   if (!out) return CDMA_ERR_INVALID_ARG;
   *out = nullptr;
   if (!args_ok(algo, esz, chunk_elems, slots)) return CDMA_ERR_INVALID_ARG;
-  if (n > (algo == CDMA_ALGO_ZVC ? CDMA_ZVC_MAX_N : CDMA_RLE_MAX_N)) return CDMA_ERR_INVALID_ARG;
+  if (n > (algo == CDMA_ALGO_RLE ? CDMA_RLE_MAX_N : CDMA_ZVC_MAX_N)) return CDMA_ERR_INVALID_ARG;
   if (compute_stream == copy_stream) return CDMA_ERR_INVALID_ARG;
   const uint64_t K = (n + chunk_elems - 1) / chunk_elems;
   if (n_chunks != K) return CDMA_ERR_INVALID_ARG;

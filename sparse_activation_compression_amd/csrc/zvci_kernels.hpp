@@ -1,0 +1,390 @@
+// zvci_kernels.hpp -- ZVC in its per-window interleaved form, for gfx950.
+//
+// "Compressing DMA Engine: Leveraging Activation Sparsity for Training Deep
+// Neural Networks", §V.A Compression Algorithm: each window of 32 values is
+// coded as its 32-bit nonzero mask followed by its nonzero values.  Windows
+// follow each other in order; in front sits an index u32 val_off[Wr+1], the
+// nonzeros before each block of E = 4096/ESZ elements (the 4 KB window of
+// §VII.A), so a block starts at 4(Wr+1) + 4*b*(E/32) + ESZ*val_off[b] and can be
+// decoded without the blocks before it.  Same masks and values as the
+// masks-then-values stream of zvc_common.hpp, in a different order.
+//
+// compress:   the run-length compressor's pipeline (persistent workgroups, one
+//             data wavefront per block, a control wavefront drawing tickets and
+//             chain-summing the tiles' nonzero counts), with the block built in
+//             LDS as mask, values, mask, values, ...: the mask of window w goes
+//             to 4w + ESZ*(nonzeros before w), a lane's values to
+//             4(w+1) + ESZ*(nonzeros before the lane), both from the wave's
+//             prefix sums of per-lane counts.
+// decompress: one wavefront per block: the index gives the block's place, the
+//             block is read into LDS, the wave walks its masks in order (each
+//             window starts after the previous window's values, so this step is
+//             sequential) and then every lane expands its 16-byte vector.
+#pragma once
+
+#include "rle_kernels.hpp"  // stream_u32
+#include "zvc_common.hpp"
+
+namespace cdma {
+
+template <int ESZ>
+struct ZviShape {
+  static constexpr int V = 4;                   // 16-byte vectors per lane
+  static constexpr int EPL = 16 / ESZ;          // elements per vector
+  static constexpr int LPW = 32 / EPL;          // lanes per 32-element window
+  static constexpr int E = 4096 / ESZ;          // elements per index block (one wavefront)
+  static constexpr int WPB = E / 32;            // windows per block: 32 (fp32) / 64 (fp16)
+  static constexpr int WPV = 64 / LPW;          // windows per 16-byte vector row of the wave
+  static constexpr int BLKMAX = 4 * WPB + 4096;  // largest block in bytes
+  static_assert(V * 64 * EPL == E, "a wavefront must cover one block");
+};
+
+template <int ESZ>
+struct ZviCShape : ZviShape<ESZ> {
+  static constexpr int BLOCK = 1024;                 // threads
+  static constexpr int NW = BLOCK / 64 - 1;          // blocks per tile: one per data wave
+  static constexpr int TE = NW * ZviShape<ESZ>::E;   // elements per tile
+  static constexpr int STAGE = NW * ZviShape<ESZ>::BLKMAX + 16;
+};
+
+template <int ESZ>
+struct ZviCLds {
+  using S = ZviCShape<ESZ>;
+  uint64_t excl;                          // exclusive nonzero prefix of the tile being stored
+  uint32_t total[2];                      // nonzeros of the tile in stage[b]
+  uint32_t vw[S::NW], bw[S::NW];          // per-block nonzeros and bytes (read between B1 and B2)
+  uint32_t ivw[2][S::NW];                 // in-tile nonzero prefix of each block, for stage[b]
+  uint32_t span[2];                       // staged bytes of stage[b]
+  uint32_t next;                          // ticket handed from the control wave to the data waves
+  uint32_t init[3];                       // the first three tickets
+  __attribute__((aligned(16))) uint8_t stage[2][S::STAGE];
+};
+
+// 32-bit LDS word at a 2-byte aligned address, as two halves.
+__device__ __forceinline__ void lds_u32_at2(uint8_t* base, uint32_t byte, uint32_t v) {
+  *reinterpret_cast<uint16_t*>(base + byte) = (uint16_t)v;
+  *reinterpret_cast<uint16_t*>(base + byte + 2) = (uint16_t)(v >> 16);
+}
+__device__ __forceinline__ uint32_t lds_get_u32_at2(const uint8_t* base, uint32_t byte) {
+  return (uint32_t)*reinterpret_cast<const uint16_t*>(base + byte) |
+         ((uint32_t)*reinterpret_cast<const uint16_t*>(base + byte + 2) << 16);
+}
+
+template <int ESZ>
+__device__ __forceinline__ void zvi_c_load_full(u32x4 (&v)[ZviShape<ESZ>::V], const uint8_t* __restrict__ src,
+                                                uint32_t t, int wave, int lane) {
+  using S = ZviCShape<ESZ>;
+  const uint8_t* p = src + (uint64_t)t * (S::NW * 4096);
+  uint32_t o = (uint32_t)(wave * 4096 + lane * 16);
+  asm volatile("" : "+v"(o));  // keep base + o from being hoisted into a 64-bit register pair
+#pragma unroll
+  for (int j = 0; j < S::V; ++j) v[j] = ld_stream(reinterpret_cast<const u32x4*>(p + o + j * 1024));
+}
+
+// One pipeline iteration (the structure of the run-length compressor's).
+// Returns the ticket the data waves prefetch in the next iteration.
+template <int ESZ>
+__device__ __forceinline__ uint32_t zvi_c_iteration(ZviCLds<ESZ>& L, u32x4 (&cur)[ZviShape<ESZ>::V],
+                                                    u32x4 (&nxt)[ZviShape<ESZ>::V], ChainRound& cr,
+                                                    uint64_t& chain_lo, uint64_t& pfx, uint32_t& pend, uint32_t t,
+                                                    uint32_t tn, uint32_t tp, int buf, uint32_t full, uint64_t Wr,
+                                                    const uint8_t* __restrict__ src, uint64_t n,
+                                                    uint8_t* __restrict__ dst, uint64_t* __restrict__ out_bytes,
+                                                    uint32_t* __restrict__ agg, uint32_t* __restrict__ counter,
+                                                    uint32_t num_tiles, int tid, int wave, int lane) {
+  using S = ZviCShape<ESZ>;
+  constexpr int V = S::V;
+  const bool have_cur = t < num_tiles;
+  const bool have_prev = tp < num_tiles;
+  const bool data = wave < S::NW;
+  const uint64_t H = 4 * (Wr + 1);
+
+  // data waves: classify this wave's block, count its values and windows
+  const uint64_t gw = (uint64_t)t * S::NW + wave;
+  const uint64_t e_win = gw * S::E;
+  const uint32_t Lw = data && have_cur && gw < Wr ? (uint32_t)(n - e_win < (uint64_t)S::E ? n - e_win : S::E) : 0u;
+  const uint32_t nwin = (Lw + 31) / 32;
+  uint32_t bits[V], pre[V], msk[V];
+  uint32_t v_w = 0;
+  if (data && have_cur) {
+    if (t >= full) {  // the one partial tile: load bounded, drain so nothing stays pending on cur
+      uint32_t el = (uint32_t)lane * S::EPL;
+      asm volatile("" : "+v"(el));
+      for (int j = 0; j < V; ++j) cur[j] = load_vec<ESZ>(src, e_win + (el + (uint32_t)(j * 64 * S::EPL)), n);
+      __builtin_amdgcn_s_waitcnt(0);
+    }
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      bits[j] = vec_nz_bits<ESZ>(cur[j]);
+      msk[j] = group_or<S::LPW>(bits[j] << ((lane % S::LPW) * S::EPL));
+      const uint32_t cnt = (uint32_t)__builtin_popcount(bits[j]);
+      const uint32_t inc = wave_incl_scan(cnt);
+      pre[j] = v_w + inc - cnt;  // nonzeros of the block before this lane's elements of row j
+      v_w += read_lane(inc, 63);
+    }
+    if (lane == 0) {
+      L.vw[wave] = v_w;
+      L.bw[wave] = 4 * nwin + ESZ * v_w;
+    }
+  }
+  __syncthreads();
+
+  if (data) {
+    if (have_cur) {
+      uint32_t B = 0, Vs = 0;  // staged bytes and nonzeros of the blocks before this one
+      for (int w = 0; w < wave; ++w) {
+        B += L.bw[w];
+        Vs += L.vw[w];
+      }
+      if (lane == 0) L.ivw[buf][wave] = Vs;
+      if (wave == S::NW - 1 && lane == 0) L.span[buf] = B + L.bw[wave];
+      uint8_t* st = L.stage[buf] + B;
+#pragma unroll
+      for (int j = 0; j < V; ++j) {
+        const uint32_t wl = (uint32_t)(j * S::WPV + lane / S::LPW);  // window of this lane in the block
+        if (wl < nwin) {
+          // the window's mask sits after the masks and values of the windows before it
+          if (lane % S::LPW == 0) {  // the window's first lane: nothing of the window before it
+            if constexpr (ESZ == 4) *reinterpret_cast<uint32_t*>(st + 4 * wl + ESZ * pre[j]) = msk[j];
+            else lds_u32_at2(st, 4 * wl + ESZ * pre[j], msk[j]);
+          }
+          uint32_t pos = 4 * (wl + 1) + ESZ * pre[j];
+#pragma unroll
+          for (int k = 0; k < S::EPL; ++k) {
+            if ((bits[j] >> k) & 1u) {
+              store_elem<ESZ>(st + pos, vec_elem<ESZ>(cur[j], k));
+              pos += ESZ;
+            }
+          }
+        }
+      }
+      if (tn < full) zvi_c_load_full<ESZ>(nxt, src, tn, wave, lane);
+    }
+  } else {
+    // control wave (see the ZVC compressor)
+    if (lane == 0) L.next = pend;
+    if (have_cur) {
+      const uint32_t vl = lane < S::NW ? L.vw[lane] : 0u;
+      const uint32_t T = read_lane(wave_incl_scan(vl), 63);
+      if (lane == 0) {
+        L.total[buf] = T;
+        agg_publish(agg, t, T);
+      }
+    }
+    if (have_prev) {
+      bool stuck = false;
+      const uint64_t X = pfx + chain_sum(agg, chain_lo, tp, cr, &stuck, [](uint32_t v) { return (uint64_t)v; });
+      if (lane == 0) {
+        L.excl = X;
+        if (stuck) atomicMax(reinterpret_cast<unsigned long long*>(out_bytes), kSizeInternalError);
+      }
+      pfx = X + L.total[buf ^ 1];  // tp's inclusive prefix
+    }
+  }
+  __syncthreads();
+
+  if (data) {
+    if (have_prev) {
+      const int pb = buf ^ 1;
+      const uint64_t X = L.excl;
+      // full tiles only precede tp, so the windows before it are tp * NW * WPB
+      const uint64_t O = H + 4 * ((uint64_t)tp * S::NW * S::WPB) + (uint64_t)ESZ * X;
+      const uint32_t span = L.span[pb];
+      store_staged<ESZ == 4 ? 4 : 2, S::NW * 64>(L.stage[pb], span, O, dst, tid);
+      if (tid < S::NW) {
+        const uint64_t w = (uint64_t)tp * S::NW + tid;
+        if (w < Wr) reinterpret_cast<uint32_t*>(dst)[w] = (uint32_t)(X + L.ivw[pb][tid]);
+      }
+      if (tp == num_tiles - 1 && tid == 0) {
+        reinterpret_cast<uint32_t*>(dst)[Wr] = (uint32_t)(X + L.total[pb]);
+        atomicMax(reinterpret_cast<unsigned long long*>(out_bytes), O + span);
+      }
+    }
+  } else if (have_cur) {
+    chain_lo = have_prev ? (uint64_t)tp + 1 : 0;
+    chain_issue(agg, chain_lo, t, cr);
+    if (lane == 0) pend = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  return __builtin_amdgcn_readfirstlane(L.next);  // uniform: keeps tile bases in SGPRs
+}
+
+template <int ESZ>
+__global__ __launch_bounds__(ZviCShape<ESZ>::BLOCK) void zvci_compress_kernel(
+    const uint8_t* __restrict__ src, uint64_t n, uint8_t* __restrict__ dst,
+    uint64_t* __restrict__ out_bytes, uint32_t* __restrict__ counter,
+    uint32_t* __restrict__ agg, uint32_t num_tiles) {
+  using S = ZviCShape<ESZ>;
+  __shared__ ZviCLds<ESZ> L;
+  const int tid = threadIdx.x;
+  const int lane = (int)lane_id();
+  const int wave = tid >> 6;
+  const uint64_t Wr = (n + S::E - 1) / S::E;
+  const uint32_t full = (uint32_t)(n / S::TE);  // tiles with no element past n
+  if (tid < 3 * 64 && lane == 0)
+    L.init[wave] = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const uint32_t a = __builtin_amdgcn_readfirstlane(L.init[0]);
+  const uint32_t b = __builtin_amdgcn_readfirstlane(L.init[1]);
+  const uint32_t c = __builtin_amdgcn_readfirstlane(L.init[2]);
+  const uint32_t lo = min(a, min(b, c)), hi = max(a, max(b, c));
+  uint32_t t = lo;
+  uint32_t tn = a + b + c - lo - hi;
+  uint32_t pend = hi;     // control wave: ticket to hand over next
+  uint32_t tp = num_tiles;
+  u32x4 ra[S::V], rb[S::V];
+  ChainRound cr;          // control wave: chain sum in flight
+  uint64_t chain_lo = 0;  // control wave: first tile of that sum
+  uint64_t pfx = 0;       // control wave: inclusive prefix of the last resolved tile
+  if (wave < S::NW && t < full) zvi_c_load_full<ESZ>(ra, src, t, wave, lane);
+  for (;;) {
+    uint32_t tnn = zvi_c_iteration<ESZ>(L, ra, rb, cr, chain_lo, pfx, pend, t, tn, tp, 0, full, Wr, src, n, dst,
+                                        out_bytes, agg, counter, num_tiles, tid, wave, lane);
+    if (t >= num_tiles) break;
+    tp = t;
+    t = tn;
+    tn = tnn;
+    tnn = zvi_c_iteration<ESZ>(L, rb, ra, cr, chain_lo, pfx, pend, t, tn, tp, 1, full, Wr, src, n, dst, out_bytes,
+                               agg, counter, num_tiles, tid, wave, lane);
+    if (t >= num_tiles) break;
+    tp = t;
+    t = tn;
+    tn = tnn;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// decompress: one wavefront per block
+// ---------------------------------------------------------------------------
+
+template <int ESZ>
+__global__ __launch_bounds__(kBlock) void zvci_decompress_kernel(
+    const uint8_t* __restrict__ src, uint64_t src_capacity, const uint64_t* __restrict__ src_bytes,
+    uint64_t n, uint8_t* __restrict__ dst, uint32_t* __restrict__ error, uint32_t num_tiles) {
+  using S = ZviShape<ESZ>;
+  constexpr int V = S::V;
+  constexpr int WSTAGE = S::BLKMAX + 32;
+  __shared__ uint32_t s_err;
+  __shared__ uint32_t s_mask[kWaves][S::WPB];  // each window's mask (bits past n cleared)
+  __shared__ uint32_t s_vpos[kWaves][S::WPB];  // staged byte of each window's first value
+  __shared__ __attribute__((aligned(16))) uint8_t s_blk[kWaves][WSTAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = (int)lane_id();
+  const int wave = tid >> 6;
+  const uint32_t t = blockIdx.x;
+  if (tid == 0) s_err = 0;
+  const uint64_t claimed = src_bytes ? *src_bytes : src_capacity;
+  const uint64_t eff = claimed < src_capacity ? claimed : src_capacity;
+  const uint64_t Wr = (n + S::E - 1) / S::E;
+  const uint64_t W = (n + 31) / 32;
+  const uint64_t H = 4 * (Wr + 1);
+  const uint64_t gw = (uint64_t)t * kWaves + wave;
+  const uint64_t e_win = gw * S::E;
+  const uint32_t Lw = gw < Wr ? (uint32_t)(n - e_win < (uint64_t)S::E ? n - e_win : S::E) : 0u;
+  const uint32_t nwin = (Lw + 31) / 32;
+  uint32_t err = 0;
+  if (t == 0 && tid == 0 && stream_u32(src, eff, 0) != 0) err |= CDMA_E_INDEX;
+  if (t == num_tiles - 1 && tid == 0 && src_bytes) {
+    const uint64_t vt = stream_u32(src, eff, 4 * Wr);
+    if (H + 4 * W + (uint64_t)ESZ * vt != *src_bytes) err |= CDMA_E_SIZE;
+  }
+  __syncthreads();
+
+  // this wave's block
+  bool valid = false;
+  uint32_t nv = 0;
+  uint64_t B = 0, span = 0;
+  if (Lw) {
+    const uint32_t v0 = stream_u32(src, eff, 4 * gw), v1 = stream_u32(src, eff, 4 * gw + 4);
+    if (v1 < v0) {
+      err |= CDMA_E_INDEX;
+    } else {
+      valid = true;
+      nv = v1 - v0;
+      B = H + 4 * gw * S::WPB + (uint64_t)ESZ * v0;
+      // never stage more than a block of this many windows can hold
+      const uint64_t most = 4 * (uint64_t)nwin + (uint64_t)ESZ * 32 * nwin;
+      span = 4 * (uint64_t)nwin + (uint64_t)ESZ * nv;
+      if (span > most) span = most;
+    }
+  }
+  uint8_t* blk = s_blk[wave];
+  uint32_t shift = 0;
+  if (valid) {
+    const uint64_t beg = B, end = B + span;
+    shift = (uint32_t)(beg & 15);
+    const uint64_t q0 = beg >> 4, q1 = (end + 15) >> 4;
+    bool short_read = false;
+    for (uint64_t q = q0 + lane; q < q1; q += 64) {
+      const uint64_t qb = q << 4;
+      const uint32_t lo = (uint32_t)(qb - (q0 << 4));
+      if (qb + 16 <= eff) {
+        *reinterpret_cast<u32x4*>(blk + lo) = ld_stream(reinterpret_cast<const u32x4*>(src + qb));
+      } else {
+        for (int k = 0; k < 16; k += 2) {
+          const uint64_t b = qb + k;
+          uint32_t e = 0;
+          if (b + 2 <= eff) e = *reinterpret_cast<const uint16_t*>(src + b);
+          else if (b >= beg && b < end) short_read = true;
+          *reinterpret_cast<uint16_t*>(blk + lo + k) = (uint16_t)e;
+        }
+      }
+    }
+    if (__ballot(short_read)) err |= CDMA_E_SIZE;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  // walk the masks: window w starts after window w-1's mask and values
+  if (valid) {
+    uint32_t p = 0, count = 0;
+    for (uint32_t w = 0; w < nwin; ++w) {
+      uint32_t m = p + 4 <= (uint32_t)span ? lds_get_u32_at2(blk + shift, p) : 0u;
+      count += (uint32_t)__builtin_popcount(m);
+      const uint64_t g = gw * S::WPB + w;  // global window
+      if (g == W - 1 && (n & 31)) {
+        const uint32_t ok = (1u << (n & 31)) - 1;
+        if (m & ~ok) err |= CDMA_E_MASK_PAST_N;
+        m &= ok;
+      }
+      if (lane == 0) {
+        s_mask[wave][w] = m;
+        s_vpos[wave][w] = p + 4;
+      }
+      p += 4 + ESZ * (uint32_t)__builtin_popcount(m);
+    }
+    if (count != nv) err |= CDMA_E_VAL_COUNT;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  // expand
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    const uint32_t wl = (uint32_t)(j * S::WPV + lane / S::LPW);
+    const uint32_t c = (uint32_t)(j * 64 + lane);
+    u32x4 o = {0u, 0u, 0u, 0u};
+    if (valid && wl < nwin) {
+      const uint32_t m = s_mask[wave][wl];
+      const uint32_t sub = (lane % S::LPW) * S::EPL;
+      const uint32_t b = (m >> sub) & ((1u << S::EPL) - 1u);
+      uint32_t at = s_vpos[wave][wl] + ESZ * (uint32_t)__builtin_popcount(m & ((1u << sub) - 1u));
+#pragma unroll
+      for (int k = 0; k < S::EPL; ++k) {
+        if ((b >> k) & 1u) {
+          if (at + ESZ <= (uint32_t)span) vec_set<ESZ>(o, k, load_elem<ESZ>(blk + shift + at));
+          at += ESZ;
+        }
+      }
+    }
+    if (Lw) store_vec<ESZ>(dst, e_win + (uint64_t)c * S::EPL, n, o);
+  }
+
+  if (err) atomicOr(&s_err, err);
+  __syncthreads();
+  if (tid == 0 && s_err && error) atomicOr(error, s_err);
+}
+
+}  // namespace cdma

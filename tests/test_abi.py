@@ -51,8 +51,16 @@ def test_max_compressed_bytes_closed_forms(cdma, esz, n):
     assert cdma.cdma_max_compressed_bytes(1, esz, n) == 8 * (wr + 1) + 2 * (n + 2 * wr) + esz * n
 
 
+@pytest.mark.parametrize("esz", [2, 4])
+@pytest.mark.parametrize("n", [0, 1, 31, 32, 33, 4096, 1 << 30])
+def test_interleaved_max_bytes_closed_form(cdma, esz, n):
+    E = 4096 // esz
+    assert cdma.cdma_max_compressed_bytes(2, esz, n) == 4 * ((n + E - 1) // E + 1) + 4 * ((n + 31) // 32) + esz * n
+    assert cdma.cdma_workspace_bytes(2, esz, n) > 0
+
+
 def test_sizes_reject_bad_algo_esz_n(cdma):
-    assert cdma.cdma_max_compressed_bytes(2, 4, 10) == 0
+    assert cdma.cdma_max_compressed_bytes(3, 4, 10) == 0
     assert cdma.cdma_max_compressed_bytes(0, 3, 10) == 0
     assert cdma.cdma_max_compressed_bytes(0, 4, (1 << 31) + 1) == 0
     assert cdma.cdma_max_compressed_bytes(1, 4, (1 << 30) + 1) == 0
@@ -71,7 +79,8 @@ P = 1 << 20
 
 
 @pytest.mark.parametrize("args,status", [
-    ((2, 4, P, 100, P, 10 ** 6, P, P, 10 ** 6, None), 1),          # bad algo
+    ((3, 4, P, 100, P, 10 ** 6, P, P, 10 ** 6, None), 1),          # bad algo
+    ((2, 4, P, 100, P, 423, P, P, 10 ** 6, None), 2),              # interleaved: one byte short
     ((0, 3, P, 100, P, 10 ** 6, P, P, 10 ** 6, None), 1),          # bad element size
     ((0, 4, None, 100, P, 10 ** 6, P, P, 10 ** 6, None), 1),       # NULL source
     ((0, 4, P + 4, 100, P, 10 ** 6, P, P, 10 ** 6, None), 1),      # misaligned source
@@ -138,7 +147,7 @@ def test_prefetch_rejects_on_host(cdma):
         a = dict(ok, **kw)
         return cdma.cdma_prefetch_async(*a.values())[0]
 
-    assert call(algo=2) == 1
+    assert call(algo=3) == 1
     assert call(chunk_elems=1000) == 1                  # not a multiple of 2048
     assert call(n_chunks=2) == 1                         # must be ceil(n / chunk_elems)
     assert call(copy_stream=16) == 1                     # same stream twice
@@ -166,7 +175,8 @@ def test_relu_compress_rejects_on_host(cdma):
         return cdma.cdma_relu_compress(*a.values())
 
     assert call(fmt=3) == 1                        # unknown format
-    assert call(algo=2) == 1
+    assert call(algo=2) == 1                       # ZVC and RLE only
+    assert call(algo=3) == 1
     assert call(d_act=8 * P + 4) == 1              # misaligned dense output
     assert call(d_act=P + 16) == 1                 # overlaps the input
     assert call(d_act=2 * P - 16) == 1             # overlaps the stream

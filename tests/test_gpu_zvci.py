@@ -1,0 +1,125 @@
+"""Interleaved ZVC on the GPU against the CPU oracle: byte-exact streams,
+bitwise round trips and identical error reports ("Compressing DMA Engine:
+Leveraging Activation Sparsity for Training Deep Neural Networks", §V.A: a
+window's mask, then its nonzero values; §VII.A: the 4 KB block of the
+index)."""
+
+import numpy as np
+import pytest
+
+import oracle
+
+from gpu_util import bits_of, device, gpu_compress, gpu_decompress, random_patterns, to_device
+
+pytestmark = pytest.mark.gpu
+
+# elements per compress tile (15 blocks of 4 KB) and per index block
+TE = {4: 15 * 1024, 2: 15 * 2048}
+E = {4: 1024, 2: 2048}
+
+
+def _sizes(esz):
+    t, e = TE[esz], E[esz]
+    return [1, 5, 31, 32, 33, 63, 65, e - 1, e, e + 1, t - 1, t, t + 1, 2 * t + 17, 5 * t + 3 * e + 33]
+
+
+@pytest.mark.parametrize("esz", [4, 2])
+@pytest.mark.parametrize("density", [0.0, 0.5, 1.0])
+def test_edge_sizes_stream_and_round_trip(esz, density):
+    device()
+    for n in _sizes(esz):
+        x = random_patterns(n, esz, density, seed=n * 5 + esz)
+        expect = oracle.zvci_compress(x)
+        got, size = gpu_compress(x, "zvci")
+        assert size == expect.size, (n, size, expect.size)
+        assert np.array_equal(got, expect), f"stream differs at n={n}"
+        out, err = gpu_decompress(expect, n, esz, "zvci")
+        assert err == 0, (n, err)
+        assert np.array_equal(out, x), f"round trip differs at n={n}"
+
+
+@pytest.mark.parametrize("name", ["alexnet_conv1_fp32_128x96x55x55", "fp16_256x256x56x56_s0.6_specials"])
+def test_workloads(name):
+    from synth import workload
+    device()
+    x = bits_of(workload(name, scale_n=1 << 23))
+    expect = oracle.zvci_compress(x)
+    got, size = gpu_compress(x, "zvci")
+    assert size == expect.size and np.array_equal(got, expect)
+    out, err = gpu_decompress(expect, x.size, x.dtype.itemsize, "zvci")
+    assert err == 0 and np.array_equal(out, x)
+
+
+def test_zero_length():
+    import torch
+    import sparse_activation_compression_amd as cdma
+    dev = device()
+    x = torch.empty(0, dtype=torch.int32, device=dev)
+    dst, nb = cdma.compress(x, "zvci")
+    torch.cuda.synchronize()
+    assert int(nb.item()) == 4 and not dst[:4].cpu().numpy().any()
+
+
+def test_corrupt_streams_report_like_the_oracle():
+    device()
+    x = np.zeros(3 * 1024 + 40, dtype=np.uint32)
+    x[::5] = 9
+    n = x.size
+    s = oracle.zvci_compress(x)  # 4 blocks: index of 5 words
+    cases = []
+    bad = s.copy()
+    bad[8:12] = np.frombuffer(np.uint32(1).tobytes(), np.uint8)  # index decreases
+    cases.append(("index", bad, True))
+    bad = s.copy()
+    bad[0] = 1  # the first entry must be zero
+    cases.append(("first entry", bad, True))
+    bad = s.copy()
+    bad[20] |= 0x02  # block 0, window 0 claims zero element 1
+    cases.append(("extra mask bit", bad, True))
+    cases.append(("truncated", s[:-8], True))
+    y = np.array([5, 0, 0], dtype=np.uint32)
+    t = oracle.zvci_compress(y)
+    bad = np.concatenate([t, t[-4:]])
+    bad[8] |= 0x10
+    cases.append(("mask past n", bad, True))
+    for what, stream, _ in cases:
+        m = 3 if what == "mask past n" else n
+        _, werr = oracle.zvci_decompress(stream, m, 4)
+        _, gerr = gpu_decompress(stream, m, 4, "zvci")
+        assert werr != 0, what
+        assert gerr == werr, (what, gerr, werr)
+
+
+def test_sweep_4GiB():
+    import torch
+    from synth import sweep_bits_device
+    import sparse_activation_compression_amd as cdma
+    dev = device()
+    n = 1 << 30
+    xd = sweep_bits_device(n, 0.5, 52, device=dev)
+    dst, nb = cdma.compress(xd, "zvci")
+    out, err = cdma.decompress(dst, n, 4, "zvci", src_bytes=nb)
+    torch.cuda.synchronize()
+    size = int(nb.item())
+    assert int(err.item()) == 0 and torch.equal(out, xd)
+    got = dst[:size].cpu().numpy()
+    x = xd.cpu().numpy().view(np.uint32)
+    del xd, out
+    torch.cuda.empty_cache()
+    want = oracle.zvci_compress(x)
+    assert got.size == want.size and np.array_equal(got, want)
+
+
+def test_offload_and_prefetch():
+    import torch
+    import sparse_activation_compression_amd as cdma
+    device()
+    x = random_patterns(6 * 65536 + 999, 4, 0.4, seed=77)
+    want, wsizes = oracle.offload_stream(x, 65536, "zvci")
+    xd = to_device(x)
+    host = torch.zeros(want.size + 7 * 4096, dtype=torch.uint8, pin_memory=True)
+    rc, total, sizes = cdma.offload(xd, host, 65536, "zvci", 2).wait()
+    assert rc == 0 and sizes == wsizes and np.array_equal(host.numpy()[:total], want)
+    rc, out, err = cdma.prefetch(host, sizes, x.size, 4, 65536, "zvci", 2).wait()
+    torch.cuda.synchronize()
+    assert rc == 0 and int(err.item()) == 0 and torch.equal(out, xd)
