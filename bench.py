@@ -481,6 +481,27 @@ def main() -> int:
         raw_h2d.append(time.perf_counter() - t0)
     raw_h2d_gbs = 4 * n / min(raw_h2d) / 1e9
 
+    # what PyTorch's own streaming kernels reach on the same 4 GiB buffer:
+    # context for the HBM fractions (mixed read/write traffic peaks well
+    # below the 8 TB/s interface figure on this part)
+    ceil = {}
+    if not args.rows_only:
+        def timed(fn, moved):
+            ts = []
+            for _ in range(4):
+                torch.cuda._sleep(SPIN_CYCLES)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                e1.synchronize()
+                ts.append(e0.elapsed_time(e1) * 1e3)
+            return round(moved / statistics.median(ts[1:]) / 1e3, 1)
+        ceil = {"torch_copy_gbs": timed(lambda: zout.copy_(x), 8 * n),
+                "torch_fill_gbs": timed(lambda: zout.fill_(7), 4 * n),
+                "torch_amax_gbs": timed(lambda: torch.amax(x), 4 * n),
+                "note": "read+write bytes per second of torch's copy_, fill_ and amax on the same buffer"}
+
     in_bytes = 4 * n
     zvc_alg = in_bytes + 4 * W + 4 * nnz
     med = {k: statistics.median(v) for k, v in ev_times.items()}
@@ -537,6 +558,7 @@ def main() -> int:
         },
         "compression_ratio": {"zvc": round(in_bytes / zsize, 4), "rle": round(in_bytes / rsize, 4)},
         "rows": rows,
+        "hbm_context": ceil,
         "roofline": {
             "kernel": "zvc_compress (workspace clear + zvc_compress_kernel)",
             "bound": "hbm",

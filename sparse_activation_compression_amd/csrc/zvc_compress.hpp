@@ -28,10 +28,13 @@ namespace cdma {
 //                 tn's loads -> B2 -> store tp's staged values at the offset
 //                 the control wave resolved;
 //   control wave: B1 -> hand the data waves the ticket drawn one iteration
-//                 earlier -> publish t's aggregate -> finish tp's chain sum
-//                 (aggregates of the tiles between this workgroup's previous
-//                 tile and tp, read one iteration earlier) -> B2 -> issue the
-//                 first round of t's chain sum and draw a ticket.
+//                 earlier and draw the next one -> publish t's aggregate ->
+//                 finish tp's chain sum (aggregates of the tiles between this
+//                 workgroup's previous tile and tp, read one iteration earlier)
+//                 -> B2 -> issue the first round of t's chain sum.
+// The ticket counter is one word hit by every workgroup, so its atomic comes
+// back slower than a load; drawing right after the hand-over gives it a whole
+// iteration.
 // The size is reported with 64-bit atomic max operations on a word cleared
 // before the launch: the last tile writes the stream size and a control wave
 // whose chain sum hit the spin bound writes the all-ones error value, which
@@ -191,7 +194,13 @@ __device__ __forceinline__ uint32_t zvc_c_iteration(ZvcCLds<ESZ>& L, u32x4 (&cur
     // control wave.  The ticket drawn last iteration goes out first: waiting
     // for it also covers the status reads issued before it, which the resolve
     // below needs anyway.
+    // what this wave issued last iteration (chain round, ticket) must be back
+    // before the hand-over; waiting here on every path keeps the compiler from
+    // waiting again after the ticket drawn next
+    __builtin_amdgcn_s_waitcnt(0);
     if (lane == 0) L.next = pend;
+    // the next ticket goes out now and has a whole iteration to come back
+    if (lane == 0 && have_cur) pend = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (have_cur) {
       const uint32_t x = lane < S::SEG ? L.tot[lane] : 0u;
       const uint32_t T = read_lane(wave_incl_scan(x), 63);
@@ -225,7 +234,6 @@ __device__ __forceinline__ uint32_t zvc_c_iteration(ZvcCLds<ESZ>& L, u32x4 (&cur
     // late enough that the tiles drawn just before t are mostly classified
     chain_lo = have_prev ? (uint64_t)tp + 1 : 0;
     chain_issue(agg, chain_lo, t, cr);
-    if (lane == 0) pend = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   return __builtin_amdgcn_readfirstlane(L.next);  // uniform: keeps tile bases in SGPRs
 }

@@ -162,7 +162,13 @@ __device__ __forceinline__ uint32_t zvi_c_iteration(ZviCLds<ESZ>& L, u32x4 (&cur
     }
   } else {
     // control wave (see the ZVC compressor)
+    // what this wave issued last iteration (chain round, ticket) must be back
+    // before the hand-over; waiting here on every path keeps the compiler from
+    // waiting again after the ticket drawn next
+    __builtin_amdgcn_s_waitcnt(0);
     if (lane == 0) L.next = pend;
+    // the next ticket goes out now and has a whole iteration to come back
+    if (lane == 0 && have_cur) pend = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (have_cur) {
       const uint32_t vl = lane < S::NW ? L.vw[lane] : 0u;
       const uint32_t T = read_lane(wave_incl_scan(vl), 63);
@@ -203,7 +209,6 @@ __device__ __forceinline__ uint32_t zvi_c_iteration(ZviCLds<ESZ>& L, u32x4 (&cur
   } else if (have_cur) {
     chain_lo = have_prev ? (uint64_t)tp + 1 : 0;
     chain_issue(agg, chain_lo, t, cr);
-    if (lane == 0) pend = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   return __builtin_amdgcn_readfirstlane(L.next);  // uniform: keeps tile bases in SGPRs
 }
