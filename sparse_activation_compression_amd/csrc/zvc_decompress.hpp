@@ -1,8 +1,8 @@
 // zvc_decompress.hpp -- ZVC decompression for gfx950 (stream format in
 // zvc_common.hpp): per-tile value offsets from the masks alone (a count pass
-// and a one-workgroup scan), then an expand pass in which each tile's value
-// span is read into LDS with aligned 16-byte loads and each lane expands its
-// vector from LDS -> aligned 16-byte stores.
+// and a one-workgroup scan), then an expand pass, one workgroup per 16 KB
+// tile, in which the tile's value span is read into LDS with aligned 16-byte
+// loads and each lane expands its vector from LDS -> aligned 16-byte stores.
 #pragma once
 
 #include "zvc_common.hpp"
@@ -284,6 +284,12 @@ __device__ __forceinline__ uint32_t zvc_tile_offset(const uint32_t* __restrict__
   return sup[t / C::SUPER] + local[t];
 }
 
+// Pass 3: one tile per workgroup, grid = tiles, no inter-workgroup dependency.
+// Workgroups are dispatched in tile order, so the tiles in flight stay one
+// narrow window of the output and of the stream.  How many are in flight per
+// CU is set by the launcher (see expand_lds_pad): more workgroups hide the
+// latency of the mask and value reads when a tile has few values, fewer keep
+// the mixed read/write traffic efficient when it has many.
 template <int ESZ, int V>
 __global__ __launch_bounds__(kBlock) void zvc_expand_kernel(
     const uint8_t* __restrict__ src, uint64_t src_capacity, const uint64_t* __restrict__ src_bytes,
@@ -293,54 +299,17 @@ __global__ __launch_bounds__(kBlock) void zvc_expand_kernel(
   const int tid = threadIdx.x;
   const int lane = (int)lane_id();
   const int wave = tid >> 6;
-  const uint32_t G = gridDim.x;
+  const uint32_t t = blockIdx.x;
+  if (t >= num_tiles) return;
   const uint64_t W = (n + 31) / 32;
   const uint64_t claimed = src_bytes ? *src_bytes : src_capacity;
   const uint64_t eff = claimed < src_capacity ? claimed : src_capacity;
-  uint32_t err = 0;
-  uint32_t ta = blockIdx.x;
-  if (ta >= num_tiles) return;
-  ZvcTileIn<ESZ, V> A, B;
-  zvc_fetch_tile<ESZ, V>(A, src, eff, W, ta, zvc_tile_offset<ESZ, V>(local, sup, ta, num_tiles),
-                         zvc_tile_offset<ESZ, V>(local, sup, ta + 1, num_tiles), tid);
-  uint32_t tb = ta + G;
-  uint32_t ob0 = 0, ob1 = 0;
-  if (tb < num_tiles) {
-    ob0 = zvc_tile_offset<ESZ, V>(local, sup, tb, num_tiles);
-    ob1 = zvc_tile_offset<ESZ, V>(local, sup, tb + 1, num_tiles);
-  }
-  for (;;) {
-    // A holds tile ta; fetch tile tb into B; offsets of the tile after tb
-    uint32_t tc = tb + G, oc0 = 0, oc1 = 0;
-    if (tb < num_tiles) zvc_fetch_tile<ESZ, V>(B, src, eff, W, tb, ob0, ob1, tid);
-    if (tc < num_tiles) {
-      oc0 = zvc_tile_offset<ESZ, V>(local, sup, tc, num_tiles);
-      oc1 = zvc_tile_offset<ESZ, V>(local, sup, tc + 1, num_tiles);
-    }
-    if (A.short_read) err |= CDMA_E_SIZE;
-    zvc_expand_tile<ESZ, V>(L, A, ta, n, dst, tid, wave, lane);
-    if (ta == num_tiles - 1 && tid == 0 && src_bytes && A.end != *src_bytes) err |= CDMA_E_SIZE;
-    if (tb >= num_tiles) break;
-    ta = tb;
-    tb = tc;
-    ob0 = oc0;
-    ob1 = oc1;
-    // same step with the roles of A and B swapped
-    tc = tb + G;
-    if (tb < num_tiles) zvc_fetch_tile<ESZ, V>(A, src, eff, W, tb, ob0, ob1, tid);
-    if (tc < num_tiles) {
-      oc0 = zvc_tile_offset<ESZ, V>(local, sup, tc, num_tiles);
-      oc1 = zvc_tile_offset<ESZ, V>(local, sup, tc + 1, num_tiles);
-    }
-    if (B.short_read) err |= CDMA_E_SIZE;
-    zvc_expand_tile<ESZ, V>(L, B, ta, n, dst, tid, wave, lane);
-    if (ta == num_tiles - 1 && tid == 0 && src_bytes && B.end != *src_bytes) err |= CDMA_E_SIZE;
-    if (tb >= num_tiles) break;
-    ta = tb;
-    tb = tc;
-    ob0 = oc0;
-    ob1 = oc1;
-  }
+  ZvcTileIn<ESZ, V> in;
+  zvc_fetch_tile<ESZ, V>(in, src, eff, W, t, zvc_tile_offset<ESZ, V>(local, sup, t, num_tiles),
+                         zvc_tile_offset<ESZ, V>(local, sup, t + 1, num_tiles), tid);
+  uint32_t err = in.short_read ? CDMA_E_SIZE : 0u;
+  zvc_expand_tile<ESZ, V>(L, in, t, n, dst, tid, wave, lane);
+  if (t == num_tiles - 1 && tid == 0 && src_bytes && in.end != *src_bytes) err |= CDMA_E_SIZE;
   if (err && error) atomicOr(error, err);
 }
 
