@@ -17,9 +17,11 @@
 //             4(w+1) + ESZ*(nonzeros before the lane), both from the wave's
 //             prefix sums of per-lane counts.
 // decompress: one wavefront per block: the index gives the block's place, the
-//             block is read into LDS, the wave walks its masks in order (each
+//             block is read into LDS, the masks are walked in order (each
 //             window starts after the previous window's values, so this step is
-//             sequential) and then every lane expands its 16-byte vector.
+//             sequential: by one wave per block, or for sparse workgroups by
+//             one wave with a lane per block), and then every lane expands its
+//             16-byte vector.
 #pragma once
 
 #include "rle_kernels.hpp"  // stream_u32
@@ -272,6 +274,7 @@ __global__ __launch_bounds__(kBlock) void zvci_decompress_kernel(
   __shared__ uint32_t s_mask[kWaves][S::WPB];  // each window's mask (bits past n cleared)
   __shared__ uint32_t s_vpos[kWaves][S::WPB];  // staged byte of each window's first value
   __shared__ __attribute__((aligned(16))) uint8_t s_blk[kWaves][WSTAGE];
+  __shared__ uint32_t s_span[kWaves], s_shift[kWaves], s_nv[kWaves], s_valid[kWaves];  // for the walk
 
   const int tid = threadIdx.x;
   const int lane = (int)lane_id();
@@ -337,33 +340,53 @@ __global__ __launch_bounds__(kBlock) void zvci_decompress_kernel(
     }
     if (__ballot(short_read)) err |= CDMA_E_SIZE;
   }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-  // walk the masks: window w starts after window w-1's mask and values
-  if (valid) {
-    uint32_t p = 0, count = 0;
-    for (uint32_t w = 0; w < nwin; ++w) {
-      uint32_t m = p + 4 <= (uint32_t)span ? lds_get_u32_at2(blk + shift, p) : 0u;
-      count += (uint32_t)__builtin_popcount(m);
-      const uint64_t g = gw * S::WPB + w;  // global window
-      if (g == W - 1 && (n & 31)) {
-        const uint32_t ok = (1u << (n & 31)) - 1;
-        if (m & ~ok) err |= CDMA_E_MASK_PAST_N;
-        m &= ok;
-      }
-      if (lane == 0) {
-        s_mask[wave][w] = m;
-        s_vpos[wave][w] = p + 4;
-      }
-      p += 4 + ESZ * (uint32_t)__builtin_popcount(m);
-    }
-    if (count != nv) err |= CDMA_E_VAL_COUNT;
+  if (lane == 0) {
+    s_valid[wave] = valid;
+    s_span[wave] = (uint32_t)span;
+    s_shift[wave] = shift;
+    s_nv[wave] = nv;
   }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  __syncthreads();
+
+  // walk the masks: window w starts after window w-1's mask and values, a
+  // chain of dependent reads.  When the workgroup's blocks are sparse (under
+  // 30 % values) one wave walks them all, lane b taking block b: the chain is
+  // cheap per step and the instruction stream, not its latency, is the cost,
+  // so one stream per workgroup beats one per block.  Dense blocks keep one
+  // walk per wave, whose latency then matters more.
+  uint32_t tot = 0;
+#pragma unroll
+  for (int b = 0; b < kWaves; ++b) tot += s_nv[b];
+  const bool shared_walk = (uint64_t)tot * 10 < (uint64_t)3 * kWaves * S::E;
+  const int b = shared_walk ? lane : wave;
+  if (shared_walk ? (wave == 0 && lane < kWaves) : true) {
+    if (s_valid[b]) {
+      const bool writer = shared_walk || lane == 0;
+      const uint64_t gb = (uint64_t)t * kWaves + b;
+      const uint64_t eb = gb * S::E;
+      const uint32_t nwb = ((uint32_t)(n - eb < (uint64_t)S::E ? n - eb : S::E) + 31) / 32;
+      const uint32_t spb = s_span[b];
+      const uint8_t* base = s_blk[b] + s_shift[b];
+      uint32_t p = 0, count = 0;
+      for (uint32_t w = 0; w < nwb; ++w) {
+        uint32_t m = p + 4 <= spb ? lds_get_u32_at2(base, p) : 0u;
+        count += (uint32_t)__builtin_popcount(m);
+        const uint64_t g = gb * S::WPB + w;  // global window
+        if (g == W - 1 && (n & 31)) {
+          const uint32_t ok = (1u << (n & 31)) - 1;
+          if (m & ~ok) err |= CDMA_E_MASK_PAST_N;
+          m &= ok;
+        }
+        if (writer) {
+          s_mask[b][w] = m;
+          s_vpos[b][w] = p + 4;
+        }
+        p += 4 + ESZ * (uint32_t)__builtin_popcount(m);
+      }
+      if (count != s_nv[b]) err |= CDMA_E_VAL_COUNT;
+    }
+  }
+  __syncthreads();
 
   // expand
 #pragma unroll
