@@ -145,6 +145,42 @@ __device__ __forceinline__ void chain_issue(const uint32_t* agg, uint64_t lo, ui
   }
 }
 
+// ---- tile assignment mode, decided once per launch --------------------------
+//
+// Static tiles (workgroup b takes b, b+G, b+2G, ...) need no ticket atomic:
+// the one counter word taken by every workgroup is a contended atomic, about
+// a tenth of the compressors' time when tiles are sparse.  But a workgroup may
+// then wait for a tile whose owner has not been dispatched yet (other work can
+// hold the CUs), which tickets never do.  Static is therefore used only when
+// every workgroup of the grid has started: each counts itself in, the one that
+// completes the count selects static, and one that has waited too long for
+// that selects tickets, both by compare-and-swap from "undecided", so every
+// workgroup follows the same choice.  The two words sit in the cleared
+// workspace header after the ticket counter.
+constexpr uint32_t kModeTickets = 1, kModeStatic = 2;
+constexpr uint32_t kModeSpinLimit = 64;  // polls (each an agent-scope round trip) before choosing tickets
+
+__device__ __forceinline__ uint32_t start_mode(uint32_t* counter) {
+  uint32_t* started = counter + 16;
+  uint32_t* mode = counter + 32;
+  const uint32_t arrived = __hip_atomic_fetch_add(started, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1;
+  if (arrived == gridDim.x) {
+    uint32_t undecided = 0;
+    __hip_atomic_compare_exchange_strong(mode, &undecided, kModeStatic, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+  }
+  uint32_t spins = 0, m;
+  while ((m = __hip_atomic_load(mode, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) == 0) {
+    if (++spins > kModeSpinLimit) {
+      uint32_t undecided = 0;
+      __hip_atomic_compare_exchange_strong(mode, &undecided, kModeTickets, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+  return m;
+}
+
 // Sum over tiles [lo, hi) of dec(aggregate), where r holds the first round
 // (issued from lo).  Unpublished words are read again until they appear;
 // further rounds are issued as needed.  Uniform result; *stuck is set (and the

@@ -14,38 +14,44 @@ namespace cdma {
 // compress: persistent workgroups of data wavefronts plus one control wavefront
 // ---------------------------------------------------------------------------
 //
-// A persistent grid of (about) one workgroup per CU takes tiles from a ticket
-// counter.  Waves 0..kDWaves-1 move data; the last wave, the control wave,
-// draws tickets and computes tile offsets by chaining over published
-// aggregates (see chain_sum).  Vector-memory counters
-// retire in order on this GPU, so a wave that had both prefetched a tile and
-// issued status reads could not use the tile before the status reads came
-// back; with the status traffic in a wave of its own, the data waves wait only
-// for their own loads.  Iteration i of a workgroup holds tile t (loaded), tn
-// (to prefetch) and the previous tile tp (nonzeros staged in LDS):
+// A persistent grid of (about) one workgroup per CU takes its tiles in
+// increasing order: static tiles (workgroup b takes b, b+G, b+2G, ...) when
+// every workgroup of the grid is known to have started, else tiles drawn from
+// a ticket counter (start_mode decides once per launch).  Waves 0..kDWaves-1
+// move data; the last wave, the control wave, hands out tiles and computes
+// tile offsets by chaining over published aggregates (see chain_sum).
+// Vector-memory counters retire in order on this GPU, so a wave that had both
+// prefetched a tile and issued status reads could not use the tile before the
+// status reads came back; with the status traffic in a wave of its own, the
+// data waves wait only for their own loads.  Iteration i of a workgroup holds
+// tile t (loaded), tn (to prefetch) and the previous tile tp (nonzeros staged
+// in LDS):
 //   data waves:   classify t (window masks, nonzero counts) -> B1 -> store
 //                 t's masks, compact t's nonzeros into LDS buffer i%2, issue
 //                 tn's loads -> B2 -> store tp's staged values at the offset
 //                 the control wave resolved;
-//   control wave: B1 -> hand the data waves the ticket drawn one iteration
-//                 earlier and draw the next one -> publish t's aggregate ->
-//                 finish tp's chain sum (aggregates of the tiles between this
-//                 workgroup's previous tile and tp, read one iteration earlier)
-//                 -> B2 -> issue the first round of t's chain sum.
+//   control wave: B1 -> publish t's aggregate (static tiles) -> hand the data
+//                 waves the next tile and, with tickets, draw the one after it
+//                 and publish -> finish tp's chain sum (aggregates of the tiles
+//                 between this workgroup's previous tile and tp, read one
+//                 iteration earlier) -> B2 -> issue the first round of t's
+//                 chain sum.
 // The ticket counter is one word hit by every workgroup, so its atomic comes
 // back slower than a load; drawing right after the hand-over gives it a whole
-// iteration.
+// iteration, and static tiles need none.
 // The size is reported with 64-bit atomic max operations on a word cleared
 // before the launch: the last tile writes the stream size and a control wave
 // whose chain sum hit the spin bound writes the all-ones error value, which
 // wins whatever the order.  (Such a sum returns an under-estimate, so every
 // store still lands inside the stream's bounds.)
-// Progress: a ticket is drawn only by a running workgroup, which classifies
-// its tickets in increasing order, and a tile's aggregate is published in the
-// iteration that classifies it, before that iteration waits for anything.
-// The smallest ticket whose aggregate is unpublished is therefore held by a
-// running workgroup that waits only for aggregates of smaller tickets, all
-// published: no co-residency is assumed and every chain sum ends.
+// Progress: every workgroup takes its tiles in increasing order and publishes
+// a tile's aggregate in the iteration that classifies it, before that
+// iteration waits on any other workgroup.  With tickets, a ticket is drawn only by a
+// running workgroup, so the smallest tile whose aggregate is unpublished is
+// held by a running workgroup that waits only for aggregates of smaller tiles,
+// all published: no co-residency is assumed and every chain sum ends.  Static
+// tiles are used only once every workgroup has started, so the owner of that
+// smallest tile is running too.
 
 #ifndef CDMA_CBLOCK
 #define CDMA_CBLOCK 1024
@@ -74,6 +80,7 @@ struct ZvcCLds {
   uint64_t excl;         // exclusive prefix of the tile being stored
   uint32_t total[2];     // nonzeros held in stage[b]
   uint32_t next;         // ticket handed from the control wave to the data waves
+  uint32_t mode;         // kModeStatic or kModeTickets (start_mode)
   uint32_t init[3];      // the first three tickets
   uint32_t tot[S::SEG];
   uint32_t mask[S::WPT];
@@ -139,7 +146,8 @@ __device__ __forceinline__ uint32_t zvc_c_iteration(ZvcCLds<ESZ>& L, u32x4 (&cur
                                                     uint64_t n, uint8_t* __restrict__ dst,
                                                     uint64_t* __restrict__ out_bytes, uint32_t* __restrict__ agg,
                                                     uint32_t* __restrict__ counter, uint32_t num_tiles,
-                                                    uint8_t* __restrict__ act, int tid, int wave, int lane) {
+                                                    uint8_t* __restrict__ act, int tid, int wave, int lane,
+                                                    bool stat) {
   using S = ZvcCShape<ESZ>;
   constexpr int V = S::V;
   const bool have_cur = t < num_tiles;
@@ -191,20 +199,27 @@ __device__ __forceinline__ uint32_t zvc_c_iteration(ZvcCLds<ESZ>& L, u32x4 (&cur
       if (tn < full) zvc_c_load_full<ESZ>(nxt, src, tn, wave, lane);
     }
   } else {
-    // control wave.  The ticket drawn last iteration goes out first: waiting
-    // for it also covers the status reads issued before it, which the resolve
-    // below needs anyway.
+    // control wave
+    // publish t's aggregate: every other workgroup's chain sum may be waiting
+    // for it.  Static tiles publish before anything else; with tickets the
+    // hand-over below has to wait for the ticket anyway, and the aggregate
+    // follows it (waiting there would also wait for this store).
+    const uint32_t T = read_lane(wave_incl_scan(lane < S::SEG ? L.tot[lane] : 0u), 63);
+    if (stat && have_cur && lane == 0) {
+      L.total[buf] = T;
+      agg_publish(agg, t, T);
+    }
     // what this wave issued last iteration (chain round, ticket) must be back
     // before the hand-over; waiting here on every path keeps the compiler from
     // waiting again after the ticket drawn next
     __builtin_amdgcn_s_waitcnt(0);
     if (lane == 0) L.next = pend;
-    // the next ticket goes out now and has a whole iteration to come back
-    if (lane == 0 && have_cur) pend = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (have_cur) {
-      const uint32_t x = lane < S::SEG ? L.tot[lane] : 0u;
-      const uint32_t T = read_lane(wave_incl_scan(x), 63);
-      if (lane == 0) {
+      if (stat) {
+        pend += gridDim.x;
+      } else if (lane == 0) {
+        // the next ticket goes out now and has a whole iteration to come back
+        pend = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         L.total[buf] = T;
         agg_publish(agg, t, T);
       }
@@ -252,8 +267,12 @@ __global__ __launch_bounds__(kCBlock) void zvc_compress_kernel(
   const int wave = tid >> 6;
   const uint64_t W = (n + 31) / 32;
   const uint32_t full = (uint32_t)(n / S::TE);  // tiles with no element past n
+  if (tid == 0) L.mode = start_mode(counter);
+  __syncthreads();
+  const bool stat = __builtin_amdgcn_readfirstlane(L.mode) == kModeStatic;
   if (tid < 3 * 64 && lane == 0)
-    L.init[wave] = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    L.init[wave] = stat ? blockIdx.x + wave * gridDim.x
+                        : __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   // the first three tickets in increasing order: classify, prefetch, hand over
   const uint32_t a = __builtin_amdgcn_readfirstlane(L.init[0]);
@@ -273,13 +292,13 @@ __global__ __launch_bounds__(kCBlock) void zvc_compress_kernel(
   // an iteration with no tile left to classify only stores the last one
   for (;;) {
     uint32_t tnn = zvc_c_iteration<ESZ, OP>(L, ra, rb, cr, chain_lo, P, pend, t, tn, tp, 0, full, W, src, n, dst,
-                                            out_bytes, agg, counter, num_tiles, act, tid, wave, lane);
+                                            out_bytes, agg, counter, num_tiles, act, tid, wave, lane, stat);
     if (t >= num_tiles) break;
     tp = t;
     t = tn;
     tn = tnn;
     tnn = zvc_c_iteration<ESZ, OP>(L, rb, ra, cr, chain_lo, P, pend, t, tn, tp, 1, full, W, src, n, dst,
-                                   out_bytes, agg, counter, num_tiles, act, tid, wave, lane);
+                                   out_bytes, agg, counter, num_tiles, act, tid, wave, lane, stat);
     if (t >= num_tiles) break;
     tp = t;
     t = tn;

@@ -53,10 +53,11 @@ def test_concurrent_compressions_on_four_streams():
     for (algo, _, xd, dst, nb, ws), st in zip(prepared, streams):
         cdma.compress(xd, algo, dst=dst, out_bytes=nb, ws=ws, stream=st)
     torch.cuda.synchronize()
-    for algo, x, _, dst, nb, _ in prepared:
+    for algo, x, _, dst, nb, ws in prepared:
         want = ORACLE[algo](x)
         size = int(nb.item())
-        print(f"{algo} n={x.size}: size {size}", flush=True)
+        hdr = ws[:256].cpu().numpy().view(np.uint32)  # ticket counter, workgroups started, tile mode
+        print(f"{algo} n={x.size}: size {size}, header words {hdr[0]} {hdr[16]} {hdr[32]}", flush=True)
         assert size == want.size
         assert np.array_equal(dst[:size].cpu().numpy(), want)
 
