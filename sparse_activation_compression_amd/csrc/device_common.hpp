@@ -149,7 +149,10 @@ __device__ __forceinline__ void chain_issue(const uint32_t* agg, uint64_t lo, ui
 //
 // Static tiles (workgroup b takes b, b+G, b+2G, ...) need no ticket atomic:
 // the one counter word taken by every workgroup is a contended atomic, about
-// a tenth of the compressors' time when tiles are sparse.  But a workgroup may
+// a tenth of the ZVC compressor's time when tiles are sparse.  (Its tiles all
+// cost about the same; the run-length and interleaved compressors, whose tile
+// costs vary, keep tickets, which balance the load: static tiles made them up
+// to 6 % slower on dense inputs.)  But a workgroup may
 // then wait for a tile whose owner has not been dispatched yet (other work can
 // hold the CUs), which tickets never do.  Static is therefore used only when
 // every workgroup of the grid has started: each counts itself in, the one that
