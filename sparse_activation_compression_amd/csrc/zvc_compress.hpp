@@ -267,9 +267,11 @@ __global__ __launch_bounds__(kCBlock) void zvc_compress_kernel(
   const int wave = tid >> 6;
   const uint64_t W = (n + 31) / 32;
   const uint32_t full = (uint32_t)(n / S::TE);  // tiles with no element past n
-  if (tid == 0) L.mode = start_mode(counter);
+  // the fused epilogue also streams the dense activation out, which makes its
+  // tiles bandwidth-bound; tickets balance them better (static was 2-5 % slower)
+  if (tid == 0) L.mode = OP == kOpNone ? start_mode(counter) : kModeTickets;
   __syncthreads();
-  const bool stat = __builtin_amdgcn_readfirstlane(L.mode) == kModeStatic;
+  const bool stat = OP == kOpNone && __builtin_amdgcn_readfirstlane(L.mode) == kModeStatic;
   if (tid < 3 * 64 && lane == 0)
     L.init[wave] = stat ? blockIdx.x + wave * gridDim.x
                         : __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
