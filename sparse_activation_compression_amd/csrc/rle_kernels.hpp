@@ -399,7 +399,7 @@ __global__ __launch_bounds__(kBlock) void rle_decompress_kernel(
   const int wave = tid >> 6;
   const uint32_t t = blockIdx.x;
   if (tid == 0) s_err = 0;
-  for (int i = tid; i < kWaves * S::WPW; i += kBlock) s_map[i] = 0;
+  for (int i = lane; i < S::WPW; i += 64) s_map[wave * S::WPW + i] = 0;  // this wave's part only
   const uint64_t claimed = src_bytes ? *src_bytes : src_capacity;
   const uint64_t eff = claimed < src_capacity ? claimed : src_capacity;
   const uint64_t Wr = (n + S::E - 1) / S::E;
@@ -462,7 +462,10 @@ __global__ __launch_bounds__(kBlock) void rle_decompress_kernel(
     }
     if (__ballot(short_read)) err |= CDMA_E_SIZE;
   }
-  __syncthreads();
+  // each wave only touches its own block and its own part of the bitmap
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
   // run starts -> boundary bitmap; checks
   if (valid) {
@@ -495,7 +498,10 @@ __global__ __launch_bounds__(kBlock) void rle_decompress_kernel(
     if (odd_total != nv) err |= CDMA_E_VAL_COUNT;
     if (__ballot(zero_len)) err |= CDMA_E_RUN_FORM;
   }
-  __syncthreads();
+  // each wave only touches its own block and its own part of the bitmap
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
   // boundaries -> nonzero bitmap (prefix XOR across the window)
   {
@@ -513,7 +519,10 @@ __global__ __launch_bounds__(kBlock) void rle_decompress_kernel(
     else if (Lw - 32 * g < 32) x &= (1u << (Lw - 32 * g)) - 1;
     if (g < (uint32_t)S::WPW) s_map[wave * S::WPW + g] = x;
   }
-  __syncthreads();
+  // each wave only touches its own block and its own part of the bitmap
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
   // expand
   const uint32_t vals = shift + 2 * p;
