@@ -25,8 +25,9 @@ __global__ void store_u64_kernel(uint64_t* p, uint64_t v) {
   if (threadIdx.x == 0 && blockIdx.x == 0) *p = v;
 }
 
-// Clear the ticket counter and the per-tile aggregate words with a kernel (not
-// a memset node), so the sequence stays correct if a caller captures it.
+// Clear the workspace header (ticket counter, start-mode words) and the
+// per-tile aggregate words with a kernel (not a memset node), so the sequence
+// stays correct if a caller captures it.
 // The compressors report the stream size with atomic max, so *out_bytes is
 // cleared here too.
 static hipError_t clear_workspace(void* ws, uint64_t tiles, uint64_t* out_bytes, hipStream_t s) {
@@ -83,7 +84,7 @@ static hipError_t zvc_compress_t(const void* src, uint64_t n, void* act, void* d
   const uint64_t tiles = zvc_compress_tiles(ESZ, n);
   hipError_t e = clear_workspace(ws, tiles, out_bytes, s);
   if (e != hipSuccess) return e;
-  // persistent grid: about one workgroup per CU, tiles handed out by ticket
+  // persistent grid: about one workgroup per CU, tiles static or by ticket
   auto kern = zvc_compress_kernel<ESZ, OP>;
   const uint64_t res = resident_groups(reinterpret_cast<const void*>(kern), kCBlock);
   const unsigned grid = (unsigned)(tiles < res ? tiles : res);

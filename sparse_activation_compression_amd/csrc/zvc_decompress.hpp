@@ -139,13 +139,12 @@ __global__ __launch_bounds__(kScanBlock) void zvc_scan_kernel(uint32_t* __restri
 }
 
 // ---------------------------------------------------------------------------
-// decompress, pass 2: expand, persistent grid-stride with prefetch
+// decompress, pass 3: expand
 // ---------------------------------------------------------------------------
 //
-// With the offsets known, tiles are independent.  Each workgroup walks tiles
-// t, t+G, t+2G, ...; while it expands tile a from LDS it already has the
-// masks and value quads of tile b = a+G in flight in registers, and the
-// offsets of tile b+G on their way.
+// With the offsets known, tiles are independent: a tile's masks and value
+// quads are fetched into registers, staged in LDS and expanded (the kernel at
+// the end of this file runs one tile per workgroup).
 
 template <int ESZ, int V>
 struct ZvcExpandShape {
