@@ -173,7 +173,10 @@ __device__ __forceinline__ uint32_t rle_c_iteration(RleCLds<ESZ>& L, u32x4 (&cur
   const uint64_t gw = (uint64_t)t * S::NW + wave;
   const uint64_t e_win = gw * S::E;
   const uint32_t Lw = data && have_cur && gw < Wr ? (uint32_t)(n - e_win < (uint64_t)S::E ? n - e_win : S::E) : 0u;
-  const uint32_t g = (uint32_t)lane;  // lane g holds mask word g of the window
+  // lane l takes SB = E/64 consecutive window positions starting at p0 (16 for
+  // 4-byte elements, 32 for 2-byte), so every lane has a share of the runs
+  constexpr uint32_t SB = (uint32_t)S::E / 64;
+  const uint32_t p0 = SB * (uint32_t)lane;
   uint32_t T = 0, texcl = 0, r_w = 0, p_w = 0;
   if (data && have_cur) {
     if (t >= full) {  // the one partial tile: load bounded, drain so nothing stays pending on cur
@@ -195,12 +198,20 @@ __device__ __forceinline__ uint32_t rle_c_iteration(RleCLds<ESZ>& L, u32x4 (&cur
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    if (g < (uint32_t)S::WPW && 32 * g < Lw) {
-      const uint32_t m = L.mask[wave * S::WPW + g];
-      const uint32_t prev = g ? L.mask[wave * S::WPW + g - 1] : 0u;
-      T = m ^ ((m << 1) | (prev >> 31));  // the element before the window counts as zero
-      const uint32_t rem = Lw - 32 * g;
-      if (rem < 32) T &= (1u << rem) - 1;
+    if (p0 < Lw) {
+      // boundary bits of this lane's positions: element i starts a run when it
+      // differs from element i-1 (the element before the window counts as zero)
+      const uint32_t w0 = p0 / 32, sh = p0 % 32;
+      const uint32_t m = L.mask[wave * S::WPW + w0];
+      const uint32_t before = sh ? (m >> (sh - 1)) & 1u : (w0 ? L.mask[wave * S::WPW + w0 - 1] >> 31 : 0u);
+      if constexpr (SB == 32) {
+        T = m ^ ((m << 1) | before);
+      } else {
+        const uint32_t seg = (m >> sh) & ((1u << SB) - 1);
+        T = (seg ^ ((seg << 1) | before)) & ((1u << SB) - 1);
+      }
+      const uint32_t rem = Lw - p0;
+      if (rem < SB) T &= (1u << rem) - 1;
     }
     const uint32_t tc = (uint32_t)__builtin_popcount(T);
     const uint32_t tinc = wave_incl_scan(tc);
@@ -228,7 +239,7 @@ __device__ __forceinline__ uint32_t rle_c_iteration(RleCLds<ESZ>& L, u32x4 (&cur
       uint8_t* st = L.stage[buf] + 2 * P + ESZ * Vs;
       if (Lw) {
         // run lengths: the gap from the previous boundary (0 at the window start)
-        const uint32_t lastpos = T ? 32 * g + 31 - (uint32_t)__builtin_clz(T) : 0u;
+        const uint32_t lastpos = T ? p0 + 31 - (uint32_t)__builtin_clz(T) : 0u;
         const uint32_t imax = wave_incl_max(lastpos);
         const uint32_t before = __shfl_up(imax, 1, 64);
         uint32_t prev = lane ? before : 0u;
@@ -237,7 +248,7 @@ __device__ __forceinline__ uint32_t rle_c_iteration(RleCLds<ESZ>& L, u32x4 (&cur
         while (x) {
           const uint32_t b = (uint32_t)__builtin_ctz(x);
           x &= x - 1;
-          const uint32_t pos = 32 * g + b;
+          const uint32_t pos = p0 + b;
           lds_u16(st, 2 * k, pos - prev);
           prev = pos;
           ++k;
