@@ -41,9 +41,10 @@ struct RleShape {
   static constexpr int E = 4096 / ESZ;             // window = one wavefront's elements
   static constexpr int TE = kWaves * E;            // elements per tile (4 windows)
   static constexpr int WPW = E / 32;               // mask words per window (32 or 64)
-  static constexpr int MAXENT = E + 2;             // run entries incl. padding, upper bound
-  static constexpr int BLK = 2 * MAXENT + ESZ * E;  // largest block in bytes
-  static constexpr int WSTAGE = BLK + 32;          // decompress: one window's block + alignment
+  // largest block of a window that passes every decode check (bound derived
+  // below, at the compressor)
+  static constexpr int BLKMAX = ESZ == 4 ? 4 * E + 8 : 3 * E + 6;
+  static constexpr int WSTAGE = BLKMAX + 32;       // decompress: one window's block + alignment
   static_assert(V * 64 * EPL == E, "a wavefront must cover one window");
 };
 
@@ -77,6 +78,9 @@ __device__ __forceinline__ void lds_u16(uint8_t* base, uint32_t byte, uint32_t v
 // A window of L elements with v nonzeros has k <= min(v, L - v + 1) nonzero
 // runs and at most 2k + 1 runs, so its block is at most 4L + 8 bytes for
 // 32-bit and 3L + 6 bytes for 16-bit elements; BLKMAX bounds the staging.
+// The decoder's checks (runs alternate from a zero run, none but the first is
+// empty, they sum to L, the nonzero runs sum to v, padding only after an odd
+// list) fix the same structure, so a block that passes them obeys the bound.
 
 template <int ESZ>
 struct RleCShape {
@@ -88,7 +92,7 @@ struct RleCShape {
   static constexpr int E = 4096 / ESZ;
   static constexpr int TE = NW * E;
   static constexpr int WPW = E / 32;
-  static constexpr int BLKMAX = ESZ == 4 ? 4 * E + 8 : 3 * E + 6;
+  static constexpr int BLKMAX = RleShape<ESZ>::BLKMAX;
   static constexpr int STAGE = NW * BLKMAX + 16;
   static_assert(V * 64 * EPL == E, "a wavefront must cover one window");
 };
@@ -444,7 +448,13 @@ __global__ __launch_bounds__(kBlock) void rle_decompress_kernel(
         err |= CDMA_E_RUN_FORM;
       } else {
         valid = true;
-        nvs = nv < Lw ? nv : Lw;  // never stage more values than the window holds
+        // Stage every run entry (2p <= 2E + 4 < BLKMAX) and as many values as
+        // fit in BLKMAX.  A block that passes every check is at most BLKMAX
+        // bytes, so a longer one is corrupt and reported through the checks,
+        // which read run entries only; its output is unspecified anyway.
+        const uint32_t room = ((uint32_t)S::BLKMAX - 2 * p) / ESZ;
+        nvs = nv < Lw ? nv : Lw;
+        nvs = nvs < room ? nvs : room;
         B = H + 2 * (uint64_t)r0 + (uint64_t)ESZ * v0;
       }
     }

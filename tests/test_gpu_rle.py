@@ -136,3 +136,54 @@ def test_corrupt_streams_report_like_the_oracle(esz):
         _, got = gpu_decompress(c, n, esz, "rle")
         assert want != 0, name
         assert got == want, (name, got, want)
+
+
+@pytest.mark.parametrize("esz", [4, 2])
+def test_largest_blocks(esz):
+    """Every other element nonzero: the most run entries a window can have,
+    so each block has the largest size a stream can hold (4E + 4 bytes for
+    32-bit elements with the pad, 3E + 2 for 16-bit)."""
+    device()
+    e = E[esz]
+    for n in (e, 2 * e, 4 * e + 3, 9 * e):
+        for first in (0, 1):
+            x = np.zeros(n, dtype=np.uint32 if esz == 4 else np.uint16)
+            x[first::2] = random_patterns(x[first::2].size, esz, 1.0, seed=n + first)
+            _check(x, esz)
+
+
+def _one_window_stream(esz, runs, nv, seed):
+    """A hand-built one-window RLE stream: index, the given run entries, then
+    nv random nonzero values (the index claims nv values)."""
+    runs = np.asarray(runs, dtype="<u2")
+    idx = np.array([0, runs.size, 0, nv], dtype="<u4")
+    vals = random_patterns(nv, esz, 1.0, seed=seed)
+    return np.concatenate([idx.view(np.uint8), runs.view(np.uint8), vals.view(np.uint8)])
+
+
+@pytest.mark.parametrize("esz", [4, 2])
+def test_oversized_blocks_report_like_the_oracle(esz):
+    """Blocks longer than any window that passes the checks can have: the
+    decoder stages at most that many bytes, and its error bits must still be
+    the oracle's (the checks read run entries only)."""
+    device()
+    e = E[esz]
+    pad = [0] if esz == 4 else []  # a 0 entry after an odd list of 32-bit runs
+    cases = [
+        # runs sum to e but only half of the claimed values: E_VAL_COUNT
+        (e, [0] + [1] * e + pad, e),
+        # one run too many: E_RUN_SUM and E_VAL_COUNT
+        (e, [0] + [1] * (e + 1), e),
+        # an empty run inside the list as well: E_RUN_FORM too
+        (e, [0] + [1] * 500 + [0] + [1] * (e - 500), e),
+        # a short (last) window
+        (e - 5, [0] + [1] * (e - 5), e - 5),
+    ]
+    bound = 4 * e + 8 if esz == 4 else 3 * e + 6
+    for k, (n, runs, nv) in enumerate(cases):
+        assert 2 * len(runs) + esz * nv > bound and len(runs) <= n + 2
+        s = _one_window_stream(esz, runs, nv, seed=900 + k)
+        _, want = oracle.rle_decompress(s, n, esz)
+        _, got = gpu_decompress(s, n, esz, "rle")
+        assert want != 0, k
+        assert got == want, (k, got, want)
