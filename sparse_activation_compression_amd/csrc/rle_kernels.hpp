@@ -405,16 +405,22 @@ __global__ __launch_bounds__(kBlock) void rle_decompress_kernel(
     uint64_t n, uint8_t* __restrict__ dst, uint32_t* __restrict__ error, uint32_t num_tiles) {
   using S = RleShape<ESZ>;
   constexpr int V = S::V;
+  // largest number of u32 run-entry pairs per lane (32-bit elements: at most
+  // E + 2 entries)
+  constexpr int kMaxPer = ((S::E + 2) / 2 + 63) / 64;
   __shared__ uint32_t s_err;
-  __shared__ uint32_t s_map[kWaves * S::WPW];  // boundary bitmap, then nonzero bitmap
+  // per mask word of each wave's window: .x the boundary bitmap, then the
+  // nonzero bitmap; .y the window's nonzeros before that word
+  __shared__ uint2 s_map[kWaves * S::WPW];
   __shared__ __attribute__((aligned(16))) uint8_t s_blk[kWaves][S::WSTAGE];
 
   const int tid = threadIdx.x;
   const int lane = (int)lane_id();
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: window math stays scalar
   const uint32_t t = blockIdx.x;
+  uint2* map = s_map + wave * S::WPW;
   if (tid == 0) s_err = 0;
-  for (int i = lane; i < S::WPW; i += 64) s_map[wave * S::WPW + i] = 0;  // this wave's part only
+  for (int i = lane; i < S::WPW; i += 64) map[i].x = 0;  // this wave's part only
   const uint64_t claimed = src_bytes ? *src_bytes : src_capacity;
   const uint64_t eff = claimed < src_capacity ? claimed : src_capacity;
   const uint64_t Wr = (n + S::E - 1) / S::E;
@@ -431,14 +437,16 @@ __global__ __launch_bounds__(kBlock) void rle_decompress_kernel(
   }
   __syncthreads();
 
-  // this wave's block
+  // this wave's block: lanes 0-3 read run_off[gw], run_off[gw+1], val_off[gw]
+  // and val_off[gw+1]
   bool valid = false;
   uint32_t p = 0, nv = 0, nvs = 0;
   uint64_t B = 0;
   if (Lw) {
-    const uint32_t r0 = stream_u32(src, eff, 4 * gw), r1 = stream_u32(src, eff, 4 * gw + 4);
-    const uint32_t v0 = stream_u32(src, eff, 4 * (Wr + 1) + 4 * gw);
-    const uint32_t v1 = stream_u32(src, eff, 4 * (Wr + 1) + 4 * gw + 4);
+    uint32_t iw = 0;
+    if (lane < 4) iw = stream_u32(src, eff, 4 * ((uint64_t)(lane >> 1) * (Wr + 1) + gw + (lane & 1)));
+    const uint32_t r0 = read_lane(iw, 0), r1 = read_lane(iw, 1);
+    const uint32_t v0 = read_lane(iw, 2), v1 = read_lane(iw, 3);
     if (r1 < r0 || v1 < v0) {
       err |= CDMA_E_INDEX;
     } else {
@@ -464,24 +472,27 @@ __global__ __launch_bounds__(kBlock) void rle_decompress_kernel(
   if (valid) {
     const uint64_t beg = B, end = B + 2 * (uint64_t)p + (uint64_t)ESZ * nvs;
     shift = (uint32_t)(beg & 15);
-    const uint64_t q0 = beg >> 4, q1 = (end + 15) >> 4;
-    bool short_read = false;
-    for (uint64_t q = q0 + lane; q < q1; q += 64) {
-      const uint64_t qb = q << 4;
-      const uint32_t lo = (uint32_t)(qb - (q0 << 4));
-      if (qb + 16 <= eff) {
-        *reinterpret_cast<u32x4*>(blk + lo) = ld_stream(reinterpret_cast<const u32x4*>(src + qb));
-      } else {
+    const uint64_t base = beg - shift;                          // 16-byte aligned
+    const uint32_t nq = (uint32_t)((end - base + 15) >> 4);     // 16-byte pieces to stage
+    const uint64_t whole = eff > base ? (eff - base) >> 4 : 0;  // pieces that end by eff
+    const uint32_t nfull = whole < nq ? (uint32_t)whole : nq;
+    const u32x4* g = reinterpret_cast<const u32x4*>(src + base);
+    for (uint32_t i = (uint32_t)lane; i < nfull; i += 64)
+      *reinterpret_cast<u32x4*>(blk + 16 * i) = ld_stream(g + i);
+    if (nfull < nq) {  // the readable stream ends inside the block: 2 bytes at a time
+      bool short_read = false;
+      for (uint32_t i = nfull + (uint32_t)lane; i < nq; i += 64) {
+        const uint64_t qb = base + 16 * (uint64_t)i;
         for (int k = 0; k < 16; k += 2) {
           const uint64_t b = qb + k;
           uint32_t e = 0;
           if (b + 2 <= eff) e = *reinterpret_cast<const uint16_t*>(src + b);
           else if (b >= beg && b < end) short_read = true;
-          lds_u16(blk, lo + k, e);
+          lds_u16(blk, 16 * i + k, e);
         }
       }
+      if (__ballot(short_read)) err |= CDMA_E_SIZE;
     }
-    if (__ballot(short_read)) err |= CDMA_E_SIZE;
   }
   // each wave only touches its own block and its own part of the bitmap
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -491,27 +502,75 @@ __global__ __launch_bounds__(kBlock) void rle_decompress_kernel(
   // run starts -> boundary bitmap; checks
   if (valid) {
     auto entry = [&](uint32_t k) -> uint32_t { return *reinterpret_cast<const uint16_t*>(blk + shift + 2 * k); };
+    auto toggle = [&](uint32_t pos) { atomicXor(&map[pos / 32].x, 1u << (pos % 32)); };
     uint32_t r = p;
     if (ESZ == 4) {
       if (p & 1) err |= CDMA_E_RUN_FORM;
       else if (entry(p - 1) == 0) r = p - 1;
     }
-    const uint32_t per = (r + 63) / 64;
-    const uint32_t k0 = (uint32_t)lane * per < r ? (uint32_t)lane * per : r;
-    const uint32_t k1 = k0 + per < r ? k0 + per : r;
-    uint32_t sum = 0, odd = 0;
+    uint32_t sum = 0, odd = 0, inc;
     bool zero_len = false;
-    for (uint32_t k = k0; k < k1; ++k) {
-      const uint32_t len = entry(k);
-      sum += len;
-      if (k & 1) odd += len;
-      if (len == 0 && k != 0) zero_len = true;
-    }
-    const uint32_t inc = wave_incl_scan(sum);
-    uint32_t start = inc - sum;
-    for (uint32_t k = k0; k < k1; ++k) {
-      if (k > 0 && start < Lw) atomicXor(&s_map[wave * S::WPW + start / 32], 1u << (start % 32));
-      start += entry(k);
+    if (ESZ == 4 && !(p & 1) && !(shift & 3)) {
+      // (zero run, nonzero run) pairs as aligned u32 words, each lane a
+      // contiguous range of pairs held in registers; the pad, if any, is the
+      // nonzero half of the last pair
+      const uint32_t np = p / 2;
+      const uint32_t per = __builtin_amdgcn_readfirstlane((np + 63) / 64);
+      const uint32_t j0 = (uint32_t)lane * per < np ? (uint32_t)lane * per : np;
+      const uint32_t j1 = j0 + per < np ? j0 + per : np;
+      const uint32_t jpad = r < p ? np - 1 : ~0u;
+      const uint32_t* pw = reinterpret_cast<const uint32_t*>(blk + shift);
+      // words past j1 (at most per - 1 of them) still lie in the stage buffer
+      // and are read, then ignored
+      uint32_t w[kMaxPer];
+#pragma unroll
+      for (int i = 0; i < kMaxPer; ++i)
+        if ((uint32_t)i < per) w[i] = pw[j0 + i];
+      uint32_t bad = 0;
+#pragma unroll
+      for (int i = 0; i < kMaxPer; ++i) {
+        if ((uint32_t)i < per) {
+          const uint32_t j = j0 + i;
+          const uint32_t x = j < j1 ? w[i] : 0u;
+          const uint32_t z = x & 0xFFFFu, nz = x >> 16;
+          sum += z + nz;
+          odd += nz;
+          bad |= (uint32_t)(j < j1) & (((uint32_t)(z == 0) & (uint32_t)(j != 0)) |
+                                       ((uint32_t)(nz == 0) & (uint32_t)(j != jpad)));
+        }
+      }
+      zero_len = bad != 0;
+      inc = wave_incl_scan(sum);
+      uint32_t start = inc - sum;
+#pragma unroll
+      for (int i = 0; i < kMaxPer; ++i) {
+        if ((uint32_t)i < per) {
+          const uint32_t j = j0 + i;
+          const bool in = j < j1;
+          const uint32_t z = w[i] & 0xFFFFu, nz = w[i] >> 16;
+          if (in && j > 0 && start < Lw) toggle(start);
+          const uint32_t s2 = start + z;
+          if (in && j != jpad && s2 < Lw) toggle(s2);
+          start = s2 + nz;
+        }
+      }
+    } else {
+      // one u16 entry at a time, each lane a contiguous range of entries
+      const uint32_t per = (r + 63) / 64;
+      const uint32_t k0 = (uint32_t)lane * per < r ? (uint32_t)lane * per : r;
+      const uint32_t k1 = k0 + per < r ? k0 + per : r;
+      for (uint32_t k = k0; k < k1; ++k) {
+        const uint32_t len = entry(k);
+        sum += len;
+        if (k & 1) odd += len;
+        if (len == 0 && k != 0) zero_len = true;
+      }
+      inc = wave_incl_scan(sum);
+      uint32_t start = inc - sum;
+      for (uint32_t k = k0; k < k1; ++k) {
+        if (k > 0 && start < Lw) toggle(start);
+        start += entry(k);
+      }
     }
     const uint32_t total = read_lane(inc, 63);
     const uint32_t odd_total = read_lane(wave_incl_scan(odd), 63);
@@ -524,12 +583,14 @@ __global__ __launch_bounds__(kBlock) void rle_decompress_kernel(
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-  // boundaries -> nonzero bitmap (prefix XOR across the window)
+  // boundaries -> nonzero bitmap (prefix XOR across the window), and the
+  // nonzeros before each mask word (wave prefix sum of its popcounts)
   {
     const uint32_t g = (uint32_t)lane;
     uint32_t x = 0;
-    if (g < (uint32_t)S::WPW) x = s_map[wave * S::WPW + g];
-    const uint32_t par = wave_incl_scan((uint32_t)__builtin_popcount(x) & 1u) - ((uint32_t)__builtin_popcount(x) & 1u);
+    if (g < (uint32_t)S::WPW) x = map[g].x;
+    const uint32_t pc = (uint32_t)__builtin_popcount(x) & 1u;
+    const uint32_t par = wave_incl_scan(pc) - pc;
     x ^= x << 1;
     x ^= x << 2;
     x ^= x << 4;
@@ -538,23 +599,26 @@ __global__ __launch_bounds__(kBlock) void rle_decompress_kernel(
     if (par & 1u) x = ~x;
     if (!valid || 32 * g >= Lw) x = 0;
     else if (Lw - 32 * g < 32) x &= (1u << (Lw - 32 * g)) - 1;
-    if (g < (uint32_t)S::WPW) s_map[wave * S::WPW + g] = x;
+    const uint32_t c = (uint32_t)__builtin_popcount(x);
+    const uint32_t before = wave_incl_scan(c) - c;
+    if (g < (uint32_t)S::WPW) map[g] = make_uint2(x, before);
   }
   // each wave only touches its own block and its own part of the bitmap
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-  // expand
+  // expand: a lane's first value is the nonzeros before its mask word plus
+  // those below its bits in the word
   const uint32_t vals = shift + 2 * p;
-  uint32_t base = 0;
+  const bool full = Lw == (uint32_t)S::E;
 #pragma unroll
   for (int j = 0; j < V; ++j) {
     const uint32_t c = (uint32_t)(j * 64 + lane);
-    const uint32_t b = (s_map[wave * S::WPW + c / S::LPW] >> ((c % S::LPW) * S::EPL)) & ((1u << S::EPL) - 1);
-    const uint32_t cnt = (uint32_t)__builtin_popcount(b);
-    const uint32_t inc = wave_incl_scan(cnt);
-    uint32_t q = base + inc - cnt;
+    const uint2 m = map[c / S::LPW];
+    const uint32_t sh = (c % S::LPW) * S::EPL;
+    const uint32_t b = (m.x >> sh) & ((1u << S::EPL) - 1);
+    uint32_t q = m.y + (uint32_t)__builtin_popcount(m.x & ((1u << sh) - 1));
     u32x4 o = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int k = 0; k < S::EPL; ++k) {
@@ -563,8 +627,8 @@ __global__ __launch_bounds__(kBlock) void rle_decompress_kernel(
         ++q;
       }
     }
-    base += read_lane(inc, 63);
-    if (Lw) store_vec<ESZ>(dst, e_win + (uint64_t)c * S::EPL, n, o);
+    if (full) st_stream(reinterpret_cast<u32x4*>(dst + (e_win + (uint64_t)c * S::EPL) * ESZ), o);
+    else if (Lw) store_vec<ESZ>(dst, e_win + (uint64_t)c * S::EPL, n, o);
   }
 
   if (err) atomicOr(&s_err, err);
