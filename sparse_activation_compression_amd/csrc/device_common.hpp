@@ -184,6 +184,42 @@ __device__ __forceinline__ uint32_t start_mode(uint32_t* counter) {
   return m;
 }
 
+// ---- ticket classes -----------------------------------------------------------
+//
+// The run-length and interleaved compressors keep tickets (their tile costs
+// vary), but once every workgroup of the grid has started (start_mode chose
+// static) they spread the draws over up to kTicketClasses counters, each on a
+// cache line of its own: workgroup b draws from class c = b % C and receives
+// tiles c, c + C, c + 2C, ... in increasing order, so each counter takes a
+// C-th of the atomics.  Progress: let u be the smallest tile whose aggregate
+// is unpublished.  If u has been drawn, its holder is running and waits only
+// for tiles below u before publishing it.  If not, every workgroup of u's
+// class holds smaller tiles of that class, all published, so one of them
+// finishes its iteration and draws again; the class has running workgroups
+// because all of them have started.  Otherwise (not all started) the one
+// counter is used, as its argument needs no co-residency.
+constexpr uint32_t kTicketClasses = 8;
+constexpr uint32_t kTicketClassWord0 = 256;   // first class counter: byte 1024 of the header
+constexpr uint32_t kTicketClassStride = 32;   // words (128 bytes) from one class counter to the next
+
+struct Tickets {
+  uint32_t* ctr;
+  uint32_t cls, ncls;
+  __device__ __forceinline__ uint32_t draw() const {
+    return cls + ncls * __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+};
+
+__device__ __forceinline__ Tickets ticket_source(uint32_t* counter, uint32_t mode) {
+  Tickets k{counter, 0u, 1u};
+  if (mode == kModeStatic) {
+    k.ncls = gridDim.x < kTicketClasses ? gridDim.x : kTicketClasses;
+    k.cls = blockIdx.x % k.ncls;
+    k.ctr = counter + kTicketClassWord0 + kTicketClassStride * k.cls;
+  }
+  return k;
+}
+
 // Sum over tiles [lo, hi) of dec(aggregate), where r holds the first round
 // (issued from lo).  Unpublished words are read again until they appear;
 // further rounds are issued as needed.  Uniform result; *stuck is set (and the

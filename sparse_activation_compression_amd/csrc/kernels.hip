@@ -38,6 +38,9 @@ static hipError_t clear_workspace(void* ws, uint64_t tiles, uint64_t* out_bytes,
   return hipGetLastError();
 }
 
+static_assert(4 * (kTicketClassWord0 + kTicketClassStride * kTicketClasses) <= kWsHeader,
+              "ticket-class counters must lie in the workspace header");
+
 static uint32_t* ws_counter(void* ws) { return static_cast<uint32_t*>(ws); }
 static uint32_t* ws_agg(void* ws) {
   return reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + kWsHeader);

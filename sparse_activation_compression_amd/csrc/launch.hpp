@@ -8,7 +8,7 @@
 
 namespace cdma {
 
-constexpr uint64_t kWsHeader = 256;  // tile-ticket counter, padded
+constexpr uint64_t kWsHeader = 2048;  // ticket counter, start-mode words, ticket-class counters
 
 uint64_t zvc_tiles(int esz, uint64_t n);           // decompress tiles
 uint64_t zvc_compress_tiles(int esz, uint64_t n);  // compress tiles (fewer, larger)

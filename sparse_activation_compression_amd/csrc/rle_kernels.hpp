@@ -105,6 +105,7 @@ struct RleCLds {
   uint32_t pw[S::NW], vw[S::NW];        // per-window entries and nonzeros (read between B1 and B2)
   uint32_t ipw[2][S::NW], ivw[2][S::NW];  // their exclusive in-tile prefixes, for the tile in stage[b]
   uint32_t next;                        // ticket handed from the control wave to the data waves
+  uint32_t mode;                        // start_mode's choice (selects the ticket source)
   uint32_t init[3];                     // the first three tickets
   uint32_t mask[S::NW * S::WPW];
   __attribute__((aligned(16))) uint8_t stage[2][S::STAGE];
@@ -161,7 +162,7 @@ __device__ __forceinline__ uint32_t rle_c_iteration(RleCLds<ESZ>& L, u32x4 (&cur
                                                     uint32_t tn, uint32_t tp, int buf, uint32_t full, uint64_t Wr,
                                                     const uint8_t* __restrict__ src, uint64_t n,
                                                     uint8_t* __restrict__ dst, uint64_t* __restrict__ out_bytes,
-                                                    uint32_t* __restrict__ aggw, uint32_t* __restrict__ counter,
+                                                    uint32_t* __restrict__ aggw, const Tickets& tk,
                                                     uint32_t num_tiles, uint8_t* __restrict__ act, int tid,
                                                     int wave, int lane) {
   using S = RleCShape<ESZ>;
@@ -290,7 +291,7 @@ __device__ __forceinline__ uint32_t rle_c_iteration(RleCLds<ESZ>& L, u32x4 (&cur
     __builtin_amdgcn_s_waitcnt(0);
     if (lane == 0) L.next = pend;
     // the next ticket goes out now and has a whole iteration to come back
-    if (lane == 0 && have_cur) pend = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (lane == 0 && have_cur) pend = tk.draw();
     if (have_cur) {
       const uint32_t pl = lane < S::NW ? L.pw[lane] : 0u;
       const uint32_t vl = lane < S::NW ? L.vw[lane] : 0u;
@@ -354,8 +355,10 @@ __global__ __launch_bounds__(RleCShape<ESZ>::BLOCK) void rle_compress_kernel(
   const int wave = tid >> 6;
   const uint64_t Wr = (n + S::E - 1) / S::E;
   const uint32_t full = (uint32_t)(n / S::TE);  // tiles with no element past n
-  if (tid < 3 * 64 && lane == 0)
-    L.init[wave] = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) L.mode = start_mode(counter);
+  __syncthreads();
+  const Tickets tk = ticket_source(counter, __builtin_amdgcn_readfirstlane(L.mode));
+  if (tid < 3 * 64 && lane == 0) L.init[wave] = tk.draw();
   __syncthreads();
   const uint32_t a = __builtin_amdgcn_readfirstlane(L.init[0]);
   const uint32_t b = __builtin_amdgcn_readfirstlane(L.init[1]);
@@ -372,13 +375,13 @@ __global__ __launch_bounds__(RleCShape<ESZ>::BLOCK) void rle_compress_kernel(
   if (wave < S::NW && t < full) rle_c_load_full<ESZ>(ra, src, t, wave, lane);
   for (;;) {
     uint32_t tnn = rle_c_iteration<ESZ, OP>(L, ra, rb, cr, chain_lo, pfx, pend, t, tn, tp, 0, full, Wr, src, n,
-                                            dst, out_bytes, aggw, counter, num_tiles, act, tid, wave, lane);
+                                            dst, out_bytes, aggw, tk, num_tiles, act, tid, wave, lane);
     if (t >= num_tiles) break;
     tp = t;
     t = tn;
     tn = tnn;
     tnn = rle_c_iteration<ESZ, OP>(L, rb, ra, cr, chain_lo, pfx, pend, t, tn, tp, 1, full, Wr, src, n, dst,
-                                   out_bytes, aggw, counter, num_tiles, act, tid, wave, lane);
+                                   out_bytes, aggw, tk, num_tiles, act, tid, wave, lane);
     if (t >= num_tiles) break;
     tp = t;
     t = tn;

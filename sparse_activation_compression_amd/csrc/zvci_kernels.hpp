@@ -58,6 +58,7 @@ struct ZviCLds {
   uint32_t ivw[2][S::NW];                 // in-tile nonzero prefix of each block, for stage[b]
   uint32_t span[2];                       // staged bytes of stage[b]
   uint32_t next;                          // ticket handed from the control wave to the data waves
+  uint32_t mode;                          // start_mode's choice (selects the ticket source)
   uint32_t init[3];                       // the first three tickets
   __attribute__((aligned(16))) uint8_t stage[2][S::STAGE];
 };
@@ -92,7 +93,7 @@ __device__ __forceinline__ uint32_t zvi_c_iteration(ZviCLds<ESZ>& L, u32x4 (&cur
                                                     uint32_t tn, uint32_t tp, int buf, uint32_t full, uint64_t Wr,
                                                     const uint8_t* __restrict__ src, uint64_t n,
                                                     uint8_t* __restrict__ dst, uint64_t* __restrict__ out_bytes,
-                                                    uint32_t* __restrict__ agg, uint32_t* __restrict__ counter,
+                                                    uint32_t* __restrict__ agg, const Tickets& tk,
                                                     uint32_t num_tiles, int tid, int wave, int lane) {
   using S = ZviCShape<ESZ>;
   constexpr int V = S::V;
@@ -170,7 +171,7 @@ __device__ __forceinline__ uint32_t zvi_c_iteration(ZviCLds<ESZ>& L, u32x4 (&cur
     __builtin_amdgcn_s_waitcnt(0);
     if (lane == 0) L.next = pend;
     // the next ticket goes out now and has a whole iteration to come back
-    if (lane == 0 && have_cur) pend = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (lane == 0 && have_cur) pend = tk.draw();
     if (have_cur) {
       const uint32_t vl = lane < S::NW ? L.vw[lane] : 0u;
       const uint32_t T = read_lane(wave_incl_scan(vl), 63);
@@ -227,8 +228,10 @@ __global__ __launch_bounds__(ZviCShape<ESZ>::BLOCK) void zvci_compress_kernel(
   const int wave = tid >> 6;
   const uint64_t Wr = (n + S::E - 1) / S::E;
   const uint32_t full = (uint32_t)(n / S::TE);  // tiles with no element past n
-  if (tid < 3 * 64 && lane == 0)
-    L.init[wave] = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) L.mode = start_mode(counter);
+  __syncthreads();
+  const Tickets tk = ticket_source(counter, __builtin_amdgcn_readfirstlane(L.mode));
+  if (tid < 3 * 64 && lane == 0) L.init[wave] = tk.draw();
   __syncthreads();
   const uint32_t a = __builtin_amdgcn_readfirstlane(L.init[0]);
   const uint32_t b = __builtin_amdgcn_readfirstlane(L.init[1]);
@@ -245,13 +248,13 @@ __global__ __launch_bounds__(ZviCShape<ESZ>::BLOCK) void zvci_compress_kernel(
   if (wave < S::NW && t < full) zvi_c_load_full<ESZ>(ra, src, t, wave, lane);
   for (;;) {
     uint32_t tnn = zvi_c_iteration<ESZ>(L, ra, rb, cr, chain_lo, pfx, pend, t, tn, tp, 0, full, Wr, src, n, dst,
-                                        out_bytes, agg, counter, num_tiles, tid, wave, lane);
+                                        out_bytes, agg, tk, num_tiles, tid, wave, lane);
     if (t >= num_tiles) break;
     tp = t;
     t = tn;
     tn = tnn;
     tnn = zvi_c_iteration<ESZ>(L, rb, ra, cr, chain_lo, pfx, pend, t, tn, tp, 1, full, Wr, src, n, dst, out_bytes,
-                               agg, counter, num_tiles, tid, wave, lane);
+                               agg, tk, num_tiles, tid, wave, lane);
     if (t >= num_tiles) break;
     tp = t;
     t = tn;
