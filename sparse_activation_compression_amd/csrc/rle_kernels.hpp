@@ -14,8 +14,9 @@
 // E elements, so each window's bitmap (E/32 mask words), runs and values are
 // produced by one wave.
 //
-// compress:   persistent workgroups of NW waves take tiles of NW windows from a
-//             ticket counter: load -> nonzero bits -> window masks in LDS (DPP
+// compress:   persistent workgroups of NW waves take tiles of NW windows from
+//             tickets (ticket classes once the whole grid has started, see
+//             ticket_source): load -> nonzero bits -> window masks in LDS (DPP
 //             OR) -> run boundaries = mask XOR (mask shifted by one element) ->
 //             per-window entry and nonzero counts -> run lengths (gaps between
 //             boundaries) and values staged in LDS -> a chain sum over the
@@ -26,7 +27,8 @@
 // decompress: the index gives each window's block offset directly (no scan)
 //             -> block read into LDS -> run starts by a wave prefix sum ->
 //             boundary bitmap (LDS XOR) -> prefix-XOR turns boundaries back
-//             into the nonzero bitmap -> the same expansion as ZVC.
+//             into the nonzero bitmap, with each mask word's nonzero prefix ->
+//             the same expansion as ZVC.
 #pragma once
 
 #include "zvc_common.hpp"

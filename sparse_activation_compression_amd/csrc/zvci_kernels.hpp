@@ -10,7 +10,8 @@
 // masks-then-values stream of zvc_common.hpp, in a different order.
 //
 // compress:   the run-length compressor's pipeline (persistent workgroups, one
-//             data wavefront per block, a control wavefront drawing tickets and
+//             data wavefront per block, a control wavefront drawing tickets
+//             (ticket classes once the whole grid has started) and
 //             chain-summing the tiles' nonzero counts), with the block built in
 //             LDS as mask, values, mask, values, ...: the mask of window w goes
 //             to 4w + ESZ*(nonzeros before w), a lane's values to
