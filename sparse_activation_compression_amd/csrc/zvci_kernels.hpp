@@ -307,7 +307,9 @@ __global__ __launch_bounds__(kBlock) void zvci_decompress_kernel(
   uint32_t nv = 0;
   uint64_t B = 0, span = 0;
   if (Lw) {
-    const uint32_t v0 = stream_u32(src, eff, 4 * gw), v1 = stream_u32(src, eff, 4 * gw + 4);
+    uint32_t iw = 0;  // lanes 0 and 1: val_off[gw], val_off[gw + 1]
+    if (lane < 2) iw = stream_u32(src, eff, 4 * (gw + (uint64_t)lane));
+    const uint32_t v0 = read_lane(iw, 0), v1 = read_lane(iw, 1);
     if (v1 < v0) {
       err |= CDMA_E_INDEX;
     } else {
@@ -325,24 +327,27 @@ __global__ __launch_bounds__(kBlock) void zvci_decompress_kernel(
   if (valid) {
     const uint64_t beg = B, end = B + span;
     shift = (uint32_t)(beg & 15);
-    const uint64_t q0 = beg >> 4, q1 = (end + 15) >> 4;
-    bool short_read = false;
-    for (uint64_t q = q0 + lane; q < q1; q += 64) {
-      const uint64_t qb = q << 4;
-      const uint32_t lo = (uint32_t)(qb - (q0 << 4));
-      if (qb + 16 <= eff) {
-        *reinterpret_cast<u32x4*>(blk + lo) = ld_stream(reinterpret_cast<const u32x4*>(src + qb));
-      } else {
+    const uint64_t base = beg - shift;                          // 16-byte aligned
+    const uint32_t nq = (uint32_t)((end - base + 15) >> 4);     // 16-byte pieces to stage
+    const uint64_t whole = eff > base ? (eff - base) >> 4 : 0;  // pieces that end by eff
+    const uint32_t nfull = whole < nq ? (uint32_t)whole : nq;
+    const u32x4* g = reinterpret_cast<const u32x4*>(src + base);
+    for (uint32_t i = (uint32_t)lane; i < nfull; i += 64)
+      *reinterpret_cast<u32x4*>(blk + 16 * i) = ld_stream(g + i);
+    if (nfull < nq) {  // the readable stream ends inside the block: 2 bytes at a time
+      bool short_read = false;
+      for (uint32_t i = nfull + (uint32_t)lane; i < nq; i += 64) {
+        const uint64_t qb = base + 16 * (uint64_t)i;
         for (int k = 0; k < 16; k += 2) {
           const uint64_t b = qb + k;
           uint32_t e = 0;
           if (b + 2 <= eff) e = *reinterpret_cast<const uint16_t*>(src + b);
           else if (b >= beg && b < end) short_read = true;
-          *reinterpret_cast<uint16_t*>(blk + lo + k) = (uint16_t)e;
+          *reinterpret_cast<uint16_t*>(blk + 16 * i + k) = (uint16_t)e;
         }
       }
+      if (__ballot(short_read)) err |= CDMA_E_SIZE;
     }
-    if (__ballot(short_read)) err |= CDMA_E_SIZE;
   }
   if (lane == 0) {
     s_valid[wave] = valid;
@@ -371,13 +376,18 @@ __global__ __launch_bounds__(kBlock) void zvci_decompress_kernel(
       const uint32_t nwb = ((uint32_t)(n - eb < (uint64_t)S::E ? n - eb : S::E) + 31) / 32;
       const uint32_t spb = s_span[b];
       const uint8_t* base = s_blk[b] + s_shift[b];
+      // the window holding element n - 1 when n is not a multiple of 32 (only
+      // the last block has it; ~0 elsewhere)
+      const uint32_t wtail = (n & 31) && gb * S::WPB + nwb == W ? nwb - 1 : ~0u;
+      const uint32_t ok = (1u << (n & 31)) - 1;
       uint32_t p = 0, count = 0;
       for (uint32_t w = 0; w < nwb; ++w) {
-        uint32_t m = p + 4 <= spb ? lds_get_u32_at2(base, p) : 0u;
+        // 32-bit elements keep every mask 4-byte aligned (the block starts so)
+        uint32_t m = 0;
+        if (p + 4 <= spb)
+          m = ESZ == 4 ? *reinterpret_cast<const uint32_t*>(base + p) : lds_get_u32_at2(base, p);
         count += (uint32_t)__builtin_popcount(m);
-        const uint64_t g = gb * S::WPB + w;  // global window
-        if (g == W - 1 && (n & 31)) {
-          const uint32_t ok = (1u << (n & 31)) - 1;
+        if (w == wtail) {
           if (m & ~ok) err |= CDMA_E_MASK_PAST_N;
           m &= ok;
         }
@@ -411,7 +421,8 @@ __global__ __launch_bounds__(kBlock) void zvci_decompress_kernel(
         }
       }
     }
-    if (Lw) store_vec<ESZ>(dst, e_win + (uint64_t)c * S::EPL, n, o);
+    if (Lw == (uint32_t)S::E) st_stream(reinterpret_cast<u32x4*>(dst + (e_win + (uint64_t)c * S::EPL) * ESZ), o);
+    else if (Lw) store_vec<ESZ>(dst, e_win + (uint64_t)c * S::EPL, n, o);
   }
 
   if (err) atomicOr(&s_err, err);
