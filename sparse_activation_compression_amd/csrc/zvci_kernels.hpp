@@ -279,6 +279,7 @@ __global__ __launch_bounds__(kBlock) void zvci_decompress_kernel(
   __shared__ uint32_t s_vpos[kWaves][S::WPB];  // staged byte of each window's first value
   __shared__ __attribute__((aligned(16))) uint8_t s_blk[kWaves][WSTAGE];
   __shared__ uint32_t s_span[kWaves], s_shift[kWaves], s_nv[kWaves], s_valid[kWaves];  // for the walk
+  __shared__ uint32_t s_zero[kWaves];  // block known to hold only zero masks: no walk
 
   const int tid = threadIdx.x;
   const int lane = (int)lane_id();
@@ -349,7 +350,26 @@ __global__ __launch_bounds__(kBlock) void zvci_decompress_kernel(
       if (__ballot(short_read)) err |= CDMA_E_SIZE;
     }
   }
+  // A block whose index claims no values is, if valid, nwin zero masks at 4w:
+  // that is checked with one read per lane, and such a block skips the walk
+  // (any nonzero word sends it through the walk, which reports the errors).
+  bool zero_blk = false;
+  if (valid && nv == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");  // this wave's own staged block
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const uint32_t q = 4 * (uint32_t)lane;  // span = 4 * nwin here
+    uint32_t m = 0;
+    if ((uint32_t)lane < nwin)
+      m = ESZ == 4 ? *reinterpret_cast<const uint32_t*>(blk + shift + q) : lds_get_u32_at2(blk + shift, q);
+    zero_blk = __ballot(m != 0) == 0;
+    if (zero_blk && (uint32_t)lane < nwin) {
+      s_mask[wave][lane] = 0;
+      s_vpos[wave][lane] = q + 4;
+    }
+  }
   if (lane == 0) {
+    s_zero[wave] = zero_blk;
     s_valid[wave] = valid;
     s_span[wave] = (uint32_t)span;
     s_shift[wave] = shift;
@@ -369,7 +389,7 @@ __global__ __launch_bounds__(kBlock) void zvci_decompress_kernel(
   const bool shared_walk = (uint64_t)tot * 10 < (uint64_t)3 * kWaves * S::E;
   const int b = shared_walk ? lane : wave;
   if (shared_walk ? (wave == 0 && lane < kWaves) : true) {
-    if (s_valid[b]) {
+    if (s_valid[b] && !s_zero[b]) {
       const bool writer = shared_walk || lane == 0;
       const uint64_t gb = (uint64_t)t * kWaves + b;
       const uint64_t eb = gb * S::E;

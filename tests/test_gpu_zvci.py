@@ -123,3 +123,38 @@ def test_offload_and_prefetch():
     rc, out, err = cdma.prefetch(host, sizes, x.size, 4, 65536, "zvci", 2).wait()
     torch.cuda.synchronize()
     assert rc == 0 and int(err.item()) == 0 and torch.equal(out, xd)
+
+
+@pytest.mark.parametrize("esz", [4, 2])
+def test_blocks_without_values(esz):
+    """Blocks whose index entry claims no values: all-zero blocks between and
+    after dense ones round-trip, and a nonzero mask word in such a block (the
+    index still claiming none) is reported as the oracle reports it."""
+    device()
+    E = 4096 // esz
+    dt = np.uint32 if esz == 4 else np.uint16
+    for n in (E, 3 * E, 5 * E + 7, 6 * E - 31):
+        x = random_patterns(n, esz, 0.4, seed=n)
+        for b in range(0, (n + E - 1) // E, 2):
+            x[b * E:(b + 1) * E] = 0          # every other block all zero
+        want = oracle.zvci_compress(x)
+        got, size = gpu_compress(x, "zvci")
+        assert size == want.size and np.array_equal(got, want), n
+        out, err = gpu_decompress(want, n, esz, "zvci")
+        assert err == 0 and np.array_equal(out, x), n
+    n = 4 * E + 45                              # last block partial, n % 32 != 0
+    s = oracle.zvci_compress(np.zeros(n, dtype=dt))
+    wr = (n + E - 1) // E
+    H = 4 * (wr + 1)
+    cases = {}
+    bad = s.copy()
+    bad[H + 4 * (E // 32) + 4 * 7] |= 0x01      # block 1, window 7: a bit, no value
+    cases["bit in an empty block"] = bad
+    bad = s.copy()
+    bad[-4 + (45 % 32) // 8] |= 1 << ((45 % 32) % 8)   # last window: a bit past n
+    cases["bit past n in an empty block"] = bad
+    for what, stream in cases.items():
+        _, werr = oracle.zvci_decompress(stream, n, esz)
+        _, gerr = gpu_decompress(stream, n, esz, "zvci")
+        assert werr != 0, what
+        assert gerr == werr, (what, gerr, werr)
