@@ -110,6 +110,7 @@ struct RleCLds {
   uint32_t mode;                        // start_mode's choice (selects the ticket source)
   uint32_t init[3];                     // the first three tickets
   uint32_t mask[S::NW * S::WPW];
+  uint32_t pre[S::NW * S::WPW];         // nonzeros of the window before each mask word
   __attribute__((aligned(16))) uint8_t stage[2][S::STAGE];
 };
 
@@ -194,17 +195,25 @@ __device__ __forceinline__ uint32_t rle_c_iteration(RleCLds<ESZ>& L, u32x4 (&cur
     }
     if constexpr (OP != kOpNone) rle_c_epilogue<ESZ, OP>(cur, act, n, t, e_win, t < full, wave, lane);
     uint32_t* wmask = L.mask + wave * S::WPW + lane / S::LPW;
-    uint32_t v_w = 0;
 #pragma unroll
     for (int j = 0; j < V; ++j) {
       const uint32_t bits = vec_nz_bits<ESZ>(cur[j]);
       const uint32_t m = group_or<S::LPW>(bits << ((lane % S::LPW) * S::EPL));
       if (lane % S::LPW == 0) wmask[j * (64 / S::LPW)] = m;
-      v_w += read_lane(wave_incl_scan((uint32_t)__builtin_popcount(bits)), 63);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // one scan over the window's mask words gives its nonzero count and, for
+    // the value placement below, the nonzeros before every word
+    uint32_t v_w;
+    {
+      const uint32_t x = lane < S::WPW ? L.mask[wave * S::WPW + lane] : 0u;
+      const uint32_t c = (uint32_t)__builtin_popcount(x);
+      const uint32_t inc = wave_incl_scan(c);
+      if (lane < S::WPW) L.pre[wave * S::WPW + lane] = inc - c;
+      v_w = read_lane(inc, 63);
+    }
     if (p0 < Lw) {
       // boundary bits of this lane's positions: element i starts a run when it
       // differs from element i-1 (the element before the window counts as zero)
@@ -264,16 +273,17 @@ __device__ __forceinline__ uint32_t rle_c_iteration(RleCLds<ESZ>& L, u32x4 (&cur
           lds_u16(st, 2 * (r_w - 1), Lw - tau_last);
           if (p_w > r_w) lds_u16(st, 2 * r_w, 0);
         }
-        // values follow the runs; the counts are scanned again here rather
-        // than held in registers across the barrier
-        uint32_t vb = 0;
+        // values follow the runs: a lane's first value of vector j comes after
+        // the nonzeros before its mask word and those below its bits there
+        const uint32_t* wm = L.mask + wave * S::WPW;
+        const uint32_t* wp = L.pre + wave * S::WPW;
 #pragma unroll
         for (int j = 0; j < V; ++j) {
-          const uint32_t bits = vec_nz_bits<ESZ>(cur[j]);
-          const uint32_t cnt = (uint32_t)__builtin_popcount(bits);
-          const uint32_t inc = wave_incl_scan(cnt);
-          uint32_t pos = 2 * p_w + ESZ * (vb + inc - cnt);
-          vb += read_lane(inc, 63);
+          const uint32_t c = (uint32_t)(j * 64 + lane);
+          const uint32_t mw = wm[c / S::LPW];
+          const uint32_t sh = (c % S::LPW) * S::EPL;
+          const uint32_t bits = (mw >> sh) & ((1u << S::EPL) - 1);
+          uint32_t pos = 2 * p_w + ESZ * (wp[c / S::LPW] + (uint32_t)__builtin_popcount(mw & ((1u << sh) - 1)));
 #pragma unroll
           for (int k2 = 0; k2 < S::EPL; ++k2) {
             if ((bits >> k2) & 1u) {
