@@ -405,6 +405,42 @@ __global__ __launch_bounds__(RleCShape<ESZ>::BLOCK) void rle_compress_kernel(
 // decompress
 // ---------------------------------------------------------------------------
 
+// Stage pieces [0, nfull) of a block (16 bytes each, piece i of lane i % 64)
+// into LDS: every load goes out before the first LDS write, so the block
+// costs one memory round trip.  K = load rounds per lane (64 * (K - 1) <
+// nfull <= 64 * K): the rounds before the last are whole, only the last one
+// has lanes past nfull, which stay idle.
+template <int K>
+__device__ __forceinline__ void stage_rounds(uint8_t* blk, const u32x4* __restrict__ g, uint32_t nfull,
+                                             uint32_t lane) {
+  u32x4 q[K];
+#pragma unroll
+  for (int j = 0; j < K - 1; ++j) q[j] = ld_stream(g + lane + 64 * j);
+  const uint32_t il = lane + 64 * (K - 1);
+  if (il < nfull) q[K - 1] = ld_stream(g + il);
+#pragma unroll
+  for (int j = 0; j < K - 1; ++j) *reinterpret_cast<u32x4*>(blk + 16 * (lane + 64 * j)) = q[j];
+  if (il < nfull) *reinterpret_cast<u32x4*>(blk + 16 * il) = q[K - 1];
+}
+
+// The same for any nfull up to 64 * KMAX pieces (uniform across the wave).
+template <int KMAX>
+__device__ __forceinline__ void stage_pieces(uint8_t* blk, const u32x4* __restrict__ g, uint32_t nfull,
+                                             uint32_t lane) {
+  static_assert(KMAX >= 1 && KMAX <= 8, "rounds per lane");
+  switch ((nfull + 63) / 64) {
+    case 0: break;
+    case 1: stage_rounds<1>(blk, g, nfull, lane); break;
+    case 2: stage_rounds<2>(blk, g, nfull, lane); break;
+    case 3: stage_rounds<3>(blk, g, nfull, lane); break;
+    case 4: stage_rounds<4>(blk, g, nfull, lane); break;
+    case 5: if constexpr (KMAX >= 5) stage_rounds<5>(blk, g, nfull, lane); break;
+    case 6: if constexpr (KMAX >= 6) stage_rounds<6>(blk, g, nfull, lane); break;
+    case 7: if constexpr (KMAX >= 7) stage_rounds<7>(blk, g, nfull, lane); break;
+    default: if constexpr (KMAX >= 8) stage_rounds<8>(blk, g, nfull, lane); break;
+  }
+}
+
 // Read a little-endian u32 at stream byte off; bytes at or past eff read as 0.
 __device__ __forceinline__ uint32_t stream_u32(const uint8_t* __restrict__ src, uint64_t eff, uint64_t off) {
   if (off + 4 <= eff && (off & 3) == 0) return *reinterpret_cast<const uint32_t*>(src + off);
@@ -492,8 +528,8 @@ __global__ __launch_bounds__(kBlock) void rle_decompress_kernel(
     const uint64_t whole = eff > base ? (eff - base) >> 4 : 0;  // pieces that end by eff
     const uint32_t nfull = whole < nq ? (uint32_t)whole : nq;
     const u32x4* g = reinterpret_cast<const u32x4*>(src + base);
-    for (uint32_t i = (uint32_t)lane; i < nfull; i += 64)
-      *reinterpret_cast<u32x4*>(blk + 16 * i) = ld_stream(g + i);
+    // pieces per lane at most: nq * 16 <= S::WSTAGE
+    stage_pieces<(S::WSTAGE + 1023) / 1024>(blk, g, nfull, (uint32_t)lane);
     if (nfull < nq) {  // the readable stream ends inside the block: 2 bytes at a time
       bool short_read = false;
       for (uint32_t i = nfull + (uint32_t)lane; i < nq; i += 64) {

@@ -333,8 +333,8 @@ __global__ __launch_bounds__(kBlock) void zvci_decompress_kernel(
     const uint64_t whole = eff > base ? (eff - base) >> 4 : 0;  // pieces that end by eff
     const uint32_t nfull = whole < nq ? (uint32_t)whole : nq;
     const u32x4* g = reinterpret_cast<const u32x4*>(src + base);
-    for (uint32_t i = (uint32_t)lane; i < nfull; i += 64)
-      *reinterpret_cast<u32x4*>(blk + 16 * i) = ld_stream(g + i);
+    // pieces per lane at most: nq * 16 <= WSTAGE
+    stage_pieces<(WSTAGE + 1023) / 1024>(blk, g, nfull, (uint32_t)lane);
     if (nfull < nq) {  // the readable stream ends inside the block: 2 bytes at a time
       bool short_read = false;
       for (uint32_t i = nfull + (uint32_t)lane; i < nq; i += 64) {
