@@ -200,11 +200,6 @@ hipError_t zvc_decompress_launch(int esz, const void* src, uint64_t cap, const u
                   : zvc_decompress_t<2>(src, cap, src_bytes, n, dst, error, ws, s);
 }
 
-uint64_t rle_tiles(int esz, uint64_t n) {
-  const uint64_t te = esz == 4 ? RleShape<4>::TE : RleShape<2>::TE;
-  return (n + te - 1) / te;
-}
-
 uint64_t rle_compress_tiles(int esz, uint64_t n) {
   const uint64_t te = esz == 4 ? RleCShape<4>::TE : RleCShape<2>::TE;
   return (n + te - 1) / te;
@@ -228,9 +223,10 @@ static hipError_t rle_compress_t(const void* src, uint64_t n, void* act, void* d
 template <int ESZ>
 static hipError_t rle_decompress_t(const void* src, uint64_t cap, const uint64_t* src_bytes, uint64_t n,
                                    void* dst, uint32_t* error, hipStream_t s) {
-  const uint64_t tiles = rle_tiles(ESZ, n);
-  rle_decompress_kernel<ESZ><<<(unsigned)tiles, kBlock, 0, s>>>(
-      static_cast<const uint8_t*>(src), cap, src_bytes, n, static_cast<uint8_t*>(dst), error, (uint32_t)tiles);
+  const uint64_t wins = (n + RleShape<ESZ>::E - 1) / RleShape<ESZ>::E;
+  const uint64_t groups = (wins + kRleDecWaves - 1) / kRleDecWaves;
+  rle_decompress_kernel<ESZ><<<(unsigned)groups, kRleDecBlock, 0, s>>>(
+      static_cast<const uint8_t*>(src), cap, src_bytes, n, static_cast<uint8_t*>(dst), error, (uint32_t)groups);
   return hipGetLastError();
 }
 

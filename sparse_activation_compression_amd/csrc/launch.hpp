@@ -12,7 +12,6 @@ constexpr uint64_t kWsHeader = 2048;  // ticket counter, start-mode words, ticke
 
 uint64_t zvc_tiles(int esz, uint64_t n);           // decompress tiles
 uint64_t zvc_compress_tiles(int esz, uint64_t n);  // compress tiles (fewer, larger)
-uint64_t rle_tiles(int esz, uint64_t n);           // decompress tiles
 uint64_t rle_compress_tiles(int esz, uint64_t n);  // compress tiles (fewer, larger)
 uint64_t zvci_compress_tiles(int esz, uint64_t n);
 
