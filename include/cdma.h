@@ -80,8 +80,10 @@ extern "C" {
 
 /* decode error bits, OR-ed into *d_error by cdma_decompress */
 #define CDMA_E_MASK_PAST_N (1u << 0) /* ZVC, ZVCI: mask bit set for an index >= n */
-#define CDMA_E_SIZE        (1u << 1) /* stream size differs from what it describes,
-                                        or the described data lies past src_capacity */
+#define CDMA_E_SIZE        (1u << 1) /* with a size word: the size differs from what the
+                                        stream's index or masks describe, or exceeds
+                                        src_capacity; without one: the described data
+                                        lies past src_capacity */
 #define CDMA_E_INDEX       (1u << 3) /* RLE, ZVCI: index does not start at 0 or decreases */
 #define CDMA_E_RUN_SUM     (1u << 4) /* RLE: runs do not sum to the window length */
 #define CDMA_E_VAL_COUNT   (1u << 5) /* RLE: nonzero runs, ZVCI: a block's mask bits,
@@ -167,8 +169,10 @@ int cdma_relu_compress(int algo, int fmt, const void *d_src, uint64_t n, void *d
  *   d_src         device, 16-byte aligned stream.
  *   src_capacity  bytes readable at d_src (the decoder never reads past it).
  *   d_src_bytes   device u64 with the stream's exact size, or NULL.  When
- *                 given, a size that disagrees with the stream's content sets
- *                 CDMA_E_SIZE; when NULL, src_capacity bounds the reads only.
+ *                 given, a size that disagrees with the stream's content or
+ *                 exceeds src_capacity sets CDMA_E_SIZE, and bytes past it read
+ *                 as 0; when NULL, src_capacity bounds the reads and data the
+ *                 stream describes past it sets CDMA_E_SIZE.
  *   d_dst         device, 16-byte aligned, n*esz bytes, fully written.
  *   d_error       device u32 or NULL; CDMA_E_* bits are OR-ed into it (it is
  *                 not cleared).  After an error the output content is

@@ -491,9 +491,11 @@ __global__ __launch_bounds__(kRleDecBlock) void rle_decompress_kernel(
   uint32_t err = 0;
   if (t == 0 && tid == 0 && (stream_u32(src, eff, 0) | stream_u32(src, eff, 4 * (Wr + 1))))
     err |= CDMA_E_INDEX;
+  // E_SIZE with a size word: the index totals describe another size, or the
+  // size exceeds the readable capacity (bytes past the end read as 0)
   if (t == num_tiles - 1 && tid == 0 && src_bytes) {
     const uint64_t rt = stream_u32(src, eff, 4 * Wr), vt = stream_u32(src, eff, 4 * (Wr + 1) + 4 * Wr);
-    if (H + 2 * rt + (uint64_t)ESZ * vt != *src_bytes) err |= CDMA_E_SIZE;
+    if (H + 2 * rt + (uint64_t)ESZ * vt != *src_bytes || *src_bytes > src_capacity) err |= CDMA_E_SIZE;
   }
   __syncthreads();
 
@@ -551,7 +553,7 @@ __global__ __launch_bounds__(kRleDecBlock) void rle_decompress_kernel(
           lds_u16(blk, 16 * i + k, e);
         }
       }
-      if (__ballot(short_read)) err |= CDMA_E_SIZE;
+      if (!src_bytes && __ballot(short_read)) err |= CDMA_E_SIZE;  // no size word: data past capacity
     }
   }
   // each wave only touches its own block and its own part of the bitmap

@@ -306,9 +306,13 @@ __global__ __launch_bounds__(kBlock) void zvc_expand_kernel(
   ZvcTileIn<ESZ, V> in;
   zvc_fetch_tile<ESZ, V>(in, src, eff, W, t, zvc_tile_offset<ESZ, V>(local, sup, t, num_tiles),
                          zvc_tile_offset<ESZ, V>(local, sup, t + 1, num_tiles), tid);
-  uint32_t err = in.short_read ? CDMA_E_SIZE : 0u;
+  // E_SIZE with a size word: the masks describe another size, or the size
+  // exceeds the readable capacity (bytes past the end read as 0); without
+  // one: described values lie past the capacity
+  uint32_t err = in.short_read && !src_bytes ? CDMA_E_SIZE : 0u;
   zvc_expand_tile<ESZ, V>(L, in, t, n, dst, tid, wave, lane);
-  if (t == num_tiles - 1 && tid == 0 && src_bytes && in.end != *src_bytes) err |= CDMA_E_SIZE;
+  if (t == num_tiles - 1 && tid == 0 && src_bytes && (in.end != *src_bytes || *src_bytes > src_capacity))
+    err |= CDMA_E_SIZE;
   if (err && error) atomicOr(error, err);
 }
 

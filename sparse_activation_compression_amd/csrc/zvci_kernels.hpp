@@ -297,9 +297,11 @@ __global__ __launch_bounds__(kBlock) void zvci_decompress_kernel(
   const uint32_t nwin = (Lw + 31) / 32;
   uint32_t err = 0;
   if (t == 0 && tid == 0 && stream_u32(src, eff, 0) != 0) err |= CDMA_E_INDEX;
+  // E_SIZE with a size word: the index total describes another size, or the
+  // size exceeds the readable capacity (bytes past the end read as 0)
   if (t == num_tiles - 1 && tid == 0 && src_bytes) {
     const uint64_t vt = stream_u32(src, eff, 4 * Wr);
-    if (H + 4 * W + (uint64_t)ESZ * vt != *src_bytes) err |= CDMA_E_SIZE;
+    if (H + 4 * W + (uint64_t)ESZ * vt != *src_bytes || *src_bytes > src_capacity) err |= CDMA_E_SIZE;
   }
   __syncthreads();
 
@@ -347,7 +349,7 @@ __global__ __launch_bounds__(kBlock) void zvci_decompress_kernel(
           *reinterpret_cast<uint16_t*>(blk + 16 * i + k) = (uint16_t)e;
         }
       }
-      if (__ballot(short_read)) err |= CDMA_E_SIZE;
+      if (!src_bytes && __ballot(short_read)) err |= CDMA_E_SIZE;  // no size word: data past capacity
     }
   }
   // A block whose index claims no values is, if valid, nwin zero masks at 4w:
