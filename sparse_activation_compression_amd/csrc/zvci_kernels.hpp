@@ -337,15 +337,19 @@ __global__ __launch_bounds__(kBlock) void zvci_decompress_kernel(
     const u32x4* g = reinterpret_cast<const u32x4*>(src + base);
     // pieces per lane at most: nq * 16 <= WSTAGE
     stage_pieces<(WSTAGE + 1023) / 1024>(blk, g, nfull, (uint32_t)lane);
-    if (nfull < nq) {  // the readable stream ends inside the block: 2 bytes at a time
+    if (nfull < nq) {  // the readable stream ends inside the block: bytes past it read as 0
       bool short_read = false;
       for (uint32_t i = nfull + (uint32_t)lane; i < nq; i += 64) {
         const uint64_t qb = base + 16 * (uint64_t)i;
         for (int k = 0; k < 16; k += 2) {
           const uint64_t b = qb + k;
           uint32_t e = 0;
-          if (b + 2 <= eff) e = *reinterpret_cast<const uint16_t*>(src + b);
-          else if (b >= beg && b < end) short_read = true;
+          if (b + 2 <= eff) {
+            e = *reinterpret_cast<const uint16_t*>(src + b);
+          } else {
+            if (b < eff) e = src[b];  // the last readable byte; the one after it reads as 0
+            if (b >= beg && b < end) short_read = true;
+          }
           *reinterpret_cast<uint16_t*>(blk + 16 * i + k) = (uint16_t)e;
         }
       }

@@ -187,3 +187,15 @@ def test_oversized_blocks_report_like_the_oracle(esz):
         _, got = gpu_decompress(s, n, esz, "rle")
         assert want != 0, k
         assert got == want, (k, got, want)
+
+
+def test_stream_cut_inside_a_run_entry():
+    """A 16-bit stream whose size ends one byte into a run entry: the byte that
+    is there counts and the missing one reads as 0, as in the oracle (found by
+    the corruption fuzz test)."""
+    device()
+    s = np.frombuffer(bytes.fromhex("00000000090000000000000004000000160001000c000100270001000c0001"),
+                      dtype=np.uint8).copy()
+    _, want = oracle.rle_decompress(s, 370, 2)
+    _, got = gpu_decompress(s, 370, 2, "rle")
+    assert want != 0 and got == want, (got, want)

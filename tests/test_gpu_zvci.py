@@ -158,3 +158,21 @@ def test_blocks_without_values(esz):
         _, gerr = gpu_decompress(stream, n, esz, "zvci")
         assert werr != 0, what
         assert gerr == werr, (what, gerr, werr)
+
+
+@pytest.mark.parametrize("esz", [4, 2])
+def test_stream_cut_inside_a_mask(esz):
+    """A stream whose size ends inside a mask word: the readable bytes count
+    and the rest read as 0, as in the oracle.  Window 1's only mask bit is in
+    its first byte, so a cut after that byte leaves the value count right and
+    only the size wrong."""
+    device()
+    dt = np.uint32 if esz == 4 else np.uint16
+    x = np.zeros(40, dtype=dt)
+    x[33] = 5
+    s = oracle.zvci_compress(x)            # index (8 bytes), mask 0, mask 1, one value
+    for cut in (1, 2, 3):
+        t = s[:8 + 4 + cut].copy()
+        _, want = oracle.zvci_decompress(t, x.size, esz)
+        _, got = gpu_decompress(t, x.size, esz, "zvci")
+        assert want != 0 and got == want, (cut, got, want)
