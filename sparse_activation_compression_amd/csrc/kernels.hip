@@ -97,11 +97,17 @@ static hipError_t zvc_compress_t(const void* src, uint64_t n, void* act, void* d
 }
 
 // Workgroups of the ZVC expand pass resident per CU.  Measured on the 4 GiB
-// fp32 sweep (percent of 8 TB/s at zero fraction 1.0 / 0.9 / 0.5 / 0.0):
-// 9 per CU (as many as LDS allows) 76.8 / 68.5 / 71.9 / 70.0, 7 per CU
-// 73.0 / 69.0 / 72.6 / 71.6, 5 per CU 62.7 / 58.8 / 75.1 / 75.9.  Seven is the
-// best floor across densities.
-constexpr int kExpandGroupsPerCU = 7;
+// fp32 sweep (percent of 8 TB/s at zero fraction 0 / 0.25 / 0.5 / 0.75 / 0.9 /
+// 0.99 / 1): 5 per CU 75.8 / 74.7 / 71.7 / 62.2 / 50.1 / 50.4 / 52.3,
+// 6 per CU 76.1 / 74.7 / 75.2 / 71.2 / 58.3 / 52.3 / 62.5,
+// 7 per CU 75.1 / 72.6 / 72.6 / 75.1 / 68.6 / 64.0 / 72.7,
+// 8 per CU (four-wave workgroups fill the CU) 75.5 / 71.7 / 71.5 / 73.3 /
+// 68.4 / 67.3 / 76.3.  Seven is the best floor across densities; the density
+// is known only on the device, after the launch is fixed.  A build option.
+#ifndef CDMA_EXPAND_GROUPS
+#define CDMA_EXPAND_GROUPS 7
+#endif
+constexpr int kExpandGroupsPerCU = CDMA_EXPAND_GROUPS;
 
 // Dynamic LDS to reserve (and leave unused) so that at most `groups`
 // workgroups of `kernel` fit in a CU's LDS; 0 if the kernel alone already
