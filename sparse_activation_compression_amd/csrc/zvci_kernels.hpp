@@ -267,6 +267,12 @@ __global__ __launch_bounds__(ZviCShape<ESZ>::BLOCK) void zvci_compress_kernel(
 // decompress: one wavefront per block
 // ---------------------------------------------------------------------------
 
+// Percent of values below which a workgroup walks its blocks' masks in one
+// wave, a lane per block (see the walk below).
+#ifndef CDMA_ZVCI_SHARED_PCT
+#define CDMA_ZVCI_SHARED_PCT 90
+#endif
+
 template <int ESZ>
 __global__ __launch_bounds__(kBlock) void zvci_decompress_kernel(
     const uint8_t* __restrict__ src, uint64_t src_capacity, const uint64_t* __restrict__ src_bytes,
@@ -384,15 +390,15 @@ __global__ __launch_bounds__(kBlock) void zvci_decompress_kernel(
   __syncthreads();
 
   // walk the masks: window w starts after window w-1's mask and values, a
-  // chain of dependent reads.  When the workgroup's blocks are sparse (under
-  // 30 % values) one wave walks them all, lane b taking block b: the chain is
-  // cheap per step and the instruction stream, not its latency, is the cost,
-  // so one stream per workgroup beats one per block.  Dense blocks keep one
-  // walk per wave, whose latency then matters more.
+  // chain of dependent reads.  Unless the workgroup's blocks are nearly dense
+  // (CDMA_ZVCI_SHARED_PCT percent values or more) one wave walks them all, lane
+  // b taking block b: the instruction stream, not the chain's latency, is the
+  // cost, so one stream per workgroup beats one per block.  Dense blocks keep
+  // one walk per wave.
   uint32_t tot = 0;
 #pragma unroll
   for (int b = 0; b < kWaves; ++b) tot += s_nv[b];
-  const bool shared_walk = (uint64_t)tot * 10 < (uint64_t)3 * kWaves * S::E;
+  const bool shared_walk = (uint64_t)tot * 100 < (uint64_t)CDMA_ZVCI_SHARED_PCT * kWaves * S::E;
   const int b = shared_walk ? lane : wave;
   if (shared_walk ? (wave == 0 && lane < kWaves) : true) {
     if (s_valid[b] && !s_zero[b]) {
