@@ -565,8 +565,19 @@ __global__ __launch_bounds__(kRleDecBlock) void rle_decompress_kernel(
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
+  // A window whose index claims no values and whose run list is one zero run
+  // of Lw elements (then the pad, for 32-bit elements) passes every check and
+  // expands to zeros: it is written directly.
+  bool zero_win = false;
+  if (valid && nv == 0 && p == (ESZ == 4 ? 2u : 1u)) {
+    const uint32_t e0 = __builtin_amdgcn_readfirstlane(*reinterpret_cast<const uint16_t*>(blk + shift));
+    const uint32_t e1 =
+        ESZ == 4 ? __builtin_amdgcn_readfirstlane(*reinterpret_cast<const uint16_t*>(blk + shift + 2)) : 0u;
+    zero_win = e0 == Lw && e1 == 0;
+  }
+
   // run starts -> boundary bitmap; checks
-  if (valid) {
+  if (valid && !zero_win) {
     auto entry = [&](uint32_t k) -> uint32_t { return *reinterpret_cast<const uint16_t*>(blk + shift + 2 * k); };
     auto toggle = [&](uint32_t pos) { atomicXor(&map[pos / 32].x, 1u << (pos % 32)); };
     uint32_t r = p;
@@ -651,7 +662,7 @@ __global__ __launch_bounds__(kRleDecBlock) void rle_decompress_kernel(
 
   // boundaries -> nonzero bitmap (prefix XOR across the window), and the
   // nonzeros before each mask word (wave prefix sum of its popcounts)
-  {
+  if (!zero_win) {
     const uint32_t g = (uint32_t)lane;
     uint32_t x = 0;
     if (g < (uint32_t)S::WPW) x = map[g].x;
@@ -678,23 +689,33 @@ __global__ __launch_bounds__(kRleDecBlock) void rle_decompress_kernel(
   // those below its bits in the word
   const uint32_t vals = shift + 2 * p;
   const bool full = Lw == (uint32_t)S::E;
+  if (zero_win) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-  for (int j = 0; j < V; ++j) {
-    const uint32_t c = (uint32_t)(j * 64 + lane);
-    const uint2 m = map[c / S::LPW];
-    const uint32_t sh = (c % S::LPW) * S::EPL;
-    const uint32_t b = (m.x >> sh) & ((1u << S::EPL) - 1);
-    uint32_t q = m.y + (uint32_t)__builtin_popcount(m.x & ((1u << sh) - 1));
-    u32x4 o = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int k = 0; k < S::EPL; ++k) {
-      if ((b >> k) & 1u) {
-        if (q < nvs) vec_set<ESZ>(o, k, load_elem<ESZ>(blk + vals + ESZ * q));
-        ++q;
-      }
+    for (int j = 0; j < V; ++j) {
+      const uint32_t c = (uint32_t)(j * 64 + lane);
+      if (full) st_stream(reinterpret_cast<u32x4*>(dst + (e_win + (uint64_t)c * S::EPL) * ESZ), z);
+      else store_vec<ESZ>(dst, e_win + (uint64_t)c * S::EPL, n, z);
     }
-    if (full) st_stream(reinterpret_cast<u32x4*>(dst + (e_win + (uint64_t)c * S::EPL) * ESZ), o);
-    else if (Lw) store_vec<ESZ>(dst, e_win + (uint64_t)c * S::EPL, n, o);
+  } else {
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      const uint32_t c = (uint32_t)(j * 64 + lane);
+      const uint2 m = map[c / S::LPW];
+      const uint32_t sh = (c % S::LPW) * S::EPL;
+      const uint32_t b = (m.x >> sh) & ((1u << S::EPL) - 1);
+      uint32_t q = m.y + (uint32_t)__builtin_popcount(m.x & ((1u << sh) - 1));
+      u32x4 o = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int k = 0; k < S::EPL; ++k) {
+        if ((b >> k) & 1u) {
+          if (q < nvs) vec_set<ESZ>(o, k, load_elem<ESZ>(blk + vals + ESZ * q));
+          ++q;
+        }
+      }
+      if (full) st_stream(reinterpret_cast<u32x4*>(dst + (e_win + (uint64_t)c * S::EPL) * ESZ), o);
+      else if (Lw) store_vec<ESZ>(dst, e_win + (uint64_t)c * S::EPL, n, o);
+    }
   }
 
   if (err) atomicOr(&s_err, err);
