@@ -184,6 +184,25 @@ __device__ __forceinline__ uint32_t start_mode(uint32_t* counter) {
   return m;
 }
 
+// ---- XCD-aware tile order -------------------------------------------------
+//
+// Consecutive workgroups of a launch are spread over the GPU's XCDs round
+// robin, and each XCD has its own L2.  A one-tile-per-workgroup decoder maps
+// workgroup b to tile xcd_tile(b, G) instead, so that each XCD takes one
+// contiguous range of tiles (a bijection of [0, G) for any G): neighbouring
+// tiles, whose compressed data share cache lines when it is sparse, then meet
+// in one L2.  Correctness does not depend on the dispatch order.
+#ifndef CDMA_XCD_ORDER
+#define CDMA_XCD_ORDER 1
+#endif
+constexpr uint32_t kXcds = 8;
+
+__device__ __forceinline__ uint32_t xcd_tile(uint32_t b, uint32_t g) {
+  if constexpr (!CDMA_XCD_ORDER) return b;
+  const uint32_t q = g / kXcds, r = g % kXcds, x = b % kXcds, i = b / kXcds;
+  return x * q + (x < r ? x : r) + i;
+}
+
 // ---- ticket classes -----------------------------------------------------------
 //
 // The run-length and interleaved compressors keep tickets (their tile costs

@@ -477,7 +477,7 @@ __global__ __launch_bounds__(kRleDecBlock) void rle_decompress_kernel(
   const int tid = threadIdx.x;
   const int lane = (int)lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: window math stays scalar
-  const uint32_t t = blockIdx.x;
+  const uint32_t t = xcd_tile(blockIdx.x, gridDim.x);  // this workgroup's tile
   uint2* map = s_map + wave * S::WPW;
   if (tid == 0) s_err = 0;
   for (int i = lane; i < S::WPW; i += 64) map[i].x = 0;  // this wave's part only

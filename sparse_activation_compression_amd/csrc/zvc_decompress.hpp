@@ -298,7 +298,7 @@ __global__ __launch_bounds__(kBlock) void zvc_expand_kernel(
   const int tid = threadIdx.x;
   const int lane = (int)lane_id();
   const int wave = tid >> 6;
-  const uint32_t t = blockIdx.x;
+  const uint32_t t = xcd_tile(blockIdx.x, gridDim.x);  // this workgroup's tile
   if (t >= num_tiles) return;
   const uint64_t W = (n + 31) / 32;
   const uint64_t claimed = src_bytes ? *src_bytes : src_capacity;
