@@ -135,3 +135,24 @@ def test_corrupt_streams_report_like_the_oracle(esz):
         _, got = gpu_decompress(c, n, esz)
         assert want != 0, name
         assert got == want, (name, got, want)
+
+
+@pytest.mark.parametrize("algo", ["zvc", "rle", "zvci"])
+def test_size_word_beyond_capacity(algo):
+    """A valid stream whose size word is right but whose readable buffer is 4
+    bytes short of it: the decoder reads nothing past the buffer and reports
+    CDMA_E_SIZE (the oracle has no capacity; the size word alone agrees with
+    the stream, so this bit comes from the capacity check)."""
+    import torch
+    import sparse_activation_compression_amd as cdma
+    dev = device()
+    x = random_patterns(5000, 4, 0.5, seed=123)
+    s = {"zvc": oracle.zvc_compress, "rle": oracle.rle_compress, "zvci": oracle.zvci_compress}[algo](x)
+    src = torch.from_numpy(s[:-4].copy()).to(dev)
+    size = torch.tensor([s.size], dtype=torch.int64, device=dev)
+    _, err = cdma.decompress(src, x.size, 4, algo, src_bytes=size)
+    torch.cuda.synchronize()
+    assert int(err.item()) & oracle.E_SIZE
+    _, err = cdma.decompress(torch.from_numpy(s.copy()).to(dev), x.size, 4, algo, src_bytes=size)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
