@@ -83,9 +83,15 @@ __device__ __forceinline__ void lds_u16(uint8_t* base, uint32_t byte, uint32_t v
 // empty, they sum to L, the nonzero runs sum to v, padding only after an odd
 // list) fix the same structure, so a block that passes them obeys the bound.
 
+// Threads of a 16-bit compressor workgroup: its blocks stage up to 1.5x the
+// window, so two stage buffers of 15 windows would not fit in LDS.
+#ifndef CDMA_RLE_C16_BLOCK
+#define CDMA_RLE_C16_BLOCK 832
+#endif
+
 template <int ESZ>
 struct RleCShape {
-  static constexpr int BLOCK = ESZ == 4 ? 1024 : 512;  // threads (16-bit blocks stage up to 1.5x)
+  static constexpr int BLOCK = ESZ == 4 ? 1024 : CDMA_RLE_C16_BLOCK;  // threads
   static constexpr int NW = BLOCK / 64 - 1;             // windows per tile: one per data wave
   static constexpr int V = 4;
   static constexpr int EPL = 16 / ESZ;

@@ -13,11 +13,13 @@ from gpu_util import bits_of, device, gpu_compress, gpu_decompress, random_patte
 pytestmark = pytest.mark.gpu
 
 E = {4: 1024, 2: 2048}  # RLE window in elements (4 KB)
+CW = {4: 15, 2: 12}     # windows per compressor tile (one per data wave)
 
 
 def _sizes(esz):
-    e, t = E[esz], 4 * E[esz]
-    return [1, 2, 3, 31, 32, 33, 100, e - 1, e, e + 1, 2 * e + 5, t - 1, t, t + 1, 3 * t + 17, 40 * t + 100]
+    e, t, c = E[esz], 4 * E[esz], CW[esz] * E[esz]
+    return [1, 2, 3, 31, 32, 33, 100, e - 1, e, e + 1, 2 * e + 5, t - 1, t, t + 1, 3 * t + 17,
+            c - 1, c, c + 1, 2 * c + e // 2, 40 * t + 100]
 
 
 def _markov(n, esz, p_flip, seed):
