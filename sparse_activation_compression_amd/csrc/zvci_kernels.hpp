@@ -268,9 +268,14 @@ __global__ __launch_bounds__(ZviCShape<ESZ>::BLOCK) void zvci_compress_kernel(
 // ---------------------------------------------------------------------------
 
 // Percent of values below which a workgroup walks its blocks' masks in one
-// wave, a lane per block (see the walk below).
+// wave, a lane per block (see the walk below).  A 16-bit block has twice the
+// mask words of a 32-bit one, so its per-block walks cost more and the shared
+// walk pays at every density (above 100: always taken).
 #ifndef CDMA_ZVCI_SHARED_PCT
 #define CDMA_ZVCI_SHARED_PCT 90
+#endif
+#ifndef CDMA_ZVCI_SHARED_PCT16
+#define CDMA_ZVCI_SHARED_PCT16 101
 #endif
 
 template <int ESZ>
@@ -391,14 +396,15 @@ __global__ __launch_bounds__(kBlock) void zvci_decompress_kernel(
 
   // walk the masks: window w starts after window w-1's mask and values, a
   // chain of dependent reads.  Unless the workgroup's blocks are nearly dense
-  // (CDMA_ZVCI_SHARED_PCT percent values or more) one wave walks them all, lane
+  // (the percentage above, or more, of values) one wave walks them all, lane
   // b taking block b: the instruction stream, not the chain's latency, is the
   // cost, so one stream per workgroup beats one per block.  Dense blocks keep
   // one walk per wave.
   uint32_t tot = 0;
 #pragma unroll
   for (int b = 0; b < kWaves; ++b) tot += s_nv[b];
-  const bool shared_walk = (uint64_t)tot * 100 < (uint64_t)CDMA_ZVCI_SHARED_PCT * kWaves * S::E;
+  constexpr uint64_t kPct = ESZ == 4 ? CDMA_ZVCI_SHARED_PCT : CDMA_ZVCI_SHARED_PCT16;
+  const bool shared_walk = (uint64_t)tot * 100 < kPct * kWaves * S::E;
   const int b = shared_walk ? lane : wave;
   if (shared_walk ? (wave == 0 && lane < kWaves) : true) {
     if (s_valid[b] && !s_zero[b]) {
