@@ -104,10 +104,17 @@ static hipError_t zvc_compress_t(const void* src, uint64_t n, void* act, void* d
 // 8 per CU (four-wave workgroups fill the CU) 75.5 / 71.7 / 71.5 / 73.3 /
 // 68.4 / 67.3 / 76.3.  Seven is the best floor across densities; the density
 // is known only on the device, after the launch is fixed.  A build option.
+// fp16 (2^30 elements, same zero fractions): 7 per CU 73.9 / 71.1 / 71.3 /
+// 69.3 / 61.8 / 57.5 / 67.0, 8 per CU 73.1 / 70.2 / 70.2 / 68.9 / 63.7 / 61.0 /
+// 70.3 (6 per CU falls to 47-52 from s = 0.9 up): eight for 16-bit elements.
 #ifndef CDMA_EXPAND_GROUPS
 #define CDMA_EXPAND_GROUPS 7
 #endif
-constexpr int kExpandGroupsPerCU = CDMA_EXPAND_GROUPS;
+#ifndef CDMA_EXPAND_GROUPS16
+#define CDMA_EXPAND_GROUPS16 8
+#endif
+template <int ESZ>
+constexpr int kExpandGroupsPerCU = ESZ == 4 ? CDMA_EXPAND_GROUPS : CDMA_EXPAND_GROUPS16;
 
 // Dynamic LDS to reserve (and leave unused) so that at most `groups`
 // workgroups of `kernel` fit in a CU's LDS; 0 if the kernel alone already
@@ -156,7 +163,7 @@ static hipError_t zvc_decompress_t(const void* src, uint64_t cap, const uint64_t
   zvc_scan_kernel<<<1, kScanBlock, 0, s>>>(sup, (uint32_t)supers);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   auto kern = zvc_expand_kernel<ESZ, kZvcV>;
-  const int pad = expand_lds_pad(reinterpret_cast<const void*>(kern), kExpandGroupsPerCU);
+  const int pad = expand_lds_pad(reinterpret_cast<const void*>(kern), kExpandGroupsPerCU<ESZ>);
   kern<<<(unsigned)tiles, kBlock, pad, s>>>(static_cast<const uint8_t*>(src), cap, src_bytes, n,
                                             static_cast<uint8_t*>(dst), error, local, sup, (uint32_t)tiles);
   return hipGetLastError();
