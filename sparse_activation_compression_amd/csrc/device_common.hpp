@@ -33,6 +33,12 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #define CDMA_NT_STORE 1
 #endif
 
+// Buffer resource word 3 for raw (untyped, unswizzled) buffer accesses on
+// gfx9-family parts, and the cache-policy operand of buffer loads (bit 1 =
+// non-temporal).
+constexpr int kBufferFlags = 0x00020000;
+constexpr int kLoadAux = CDMA_NT_LOAD ? 2 : 0;
+
 template <typename T>
 __device__ __forceinline__ T ld_stream(const T* p) {
   if constexpr (CDMA_NT_LOAD) return __builtin_nontemporal_load(p);
@@ -135,13 +141,23 @@ struct ChainRound {
 };
 
 // Issue the reads of agg[lo + k*64 + lane] for the round starting at lo;
-// slots at or past hi read as a published zero.
+// slots at or past hi read as a published zero.  With lazy chain reads every
+// slot issues a load (slots past hi read agg[hi - 1], whose value is ignored),
+// so nothing consumes a value here and the wave does not wait for the round
+// until chain_sum needs it.
+#ifndef CDMA_CHAIN_LAZY
+#define CDMA_CHAIN_LAZY 1
+#endif
+#ifndef CDMA_CHAIN_SUM32
+#define CDMA_CHAIN_SUM32 0
+#endif
 __device__ __forceinline__ void chain_issue(const uint32_t* agg, uint64_t lo, uint64_t hi, ChainRound& r) {
   const uint32_t lane = lane_id();
 #pragma unroll
   for (int k = 0; k < kChainK; ++k) {
     const uint64_t i = lo + (uint64_t)(k * 64) + lane;
-    r.w[k] = i < hi ? agg_load(agg, i) : 1u;
+    if constexpr (CDMA_CHAIN_LAZY) r.w[k] = agg_load(agg, i < hi ? i : (hi > 0 ? hi - 1 : 0));
+    else r.w[k] = i < hi ? agg_load(agg, i) : 1u;
   }
 }
 
@@ -253,7 +269,11 @@ __device__ __forceinline__ uint64_t chain_sum(const uint32_t* agg, uint64_t lo, 
   for (;;) {
     bool missing = false;
 #pragma unroll
-    for (int k = 0; k < kChainK; ++k) missing |= r.w[k] == 0;
+    for (int k = 0; k < kChainK; ++k) {
+      if constexpr (CDMA_CHAIN_LAZY)
+        if (base + (uint64_t)(k * 64) + lane >= hi) r.w[k] = 1u;
+      missing |= r.w[k] == 0;
+    }
     if (__ballot(missing)) {
       if (++spins > kChainSpinLimit) {
         *stuck = true;
@@ -265,10 +285,20 @@ __device__ __forceinline__ uint64_t chain_sum(const uint32_t* agg, uint64_t lo, 
         if (r.w[k] == 0) r.w[k] = agg_load(agg, base + (uint64_t)(k * 64) + lane);
       continue;
     }
-    uint64_t part = 0;
+    using Part = decltype(dec(0u));
+    if constexpr (sizeof(Part) == 4 && CDMA_CHAIN_SUM32) {
+      // 32-bit decoded aggregates (nonzero counts): a round's sum fits in 32
+      // bits, and a DPP scan reduces it without LDS round trips
+      uint32_t part = 0;
 #pragma unroll
-    for (int k = 0; k < kChainK; ++k) part += dec(r.w[k] - 1);
-    sum += wave_sum_u64(part);
+      for (int k = 0; k < kChainK; ++k) part += dec(r.w[k] - 1);
+      sum += read_lane(wave_incl_scan(part), 63);
+    } else {
+      uint64_t part = 0;
+#pragma unroll
+      for (int k = 0; k < kChainK; ++k) part += dec(r.w[k] - 1);
+      sum += wave_sum_u64(part);
+    }
     base += 64 * kChainK;
     if (base >= hi) return sum;
     chain_issue(agg, base, hi, r);

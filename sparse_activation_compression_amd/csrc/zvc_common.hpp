@@ -77,6 +77,61 @@ __device__ __forceinline__ uint32_t vec_nz_bits(u32x4 v) {
   }
 }
 
+// Per-element nonzero bits of one 16-byte vector placed at bit sh of a
+// window mask (bit sh + k = element k), with min(x, 1) as the 0/1 test so
+// each element costs one min and one shift-or.
+// min(x, 1): 0 for 0, else 1.  Written as the instruction itself because the
+// compiler turns the plain expression into a compare and a select (two
+// instructions and a hazard wait).
+__device__ __forceinline__ uint32_t nz01(uint32_t x) {
+  uint32_t r;
+  asm("v_min_u32 %0, 1, %1" : "=v"(r) : "v"(x));
+  return r;
+}
+
+template <int ESZ>
+__device__ __forceinline__ uint32_t vec_nz_at(u32x4 v, uint32_t sh) {
+  if constexpr (ESZ == 4) {
+    return (nz01(v.x) << sh) | (nz01(v.y) << (sh + 1)) | (nz01(v.z) << (sh + 2)) | (nz01(v.w) << (sh + 3));
+  } else {
+    uint32_t r = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t w = v[k];
+      r |= (nz01(w & 0xFFFFu) << (sh + 2 * k)) | (nz01(w >> 16) << (sh + 2 * k + 1));
+    }
+    return r;
+  }
+}
+
+// Exclusive prefix over the wavefront's lanes of V per-lane counts at once:
+// the counts are packed into fields of one 32-bit word (8 bits each when a
+// lane's count is at most 4, 16 bits otherwise) and scanned together.  The
+// exclusive prefixes fit their fields (at most 63 * 4 = 252, or 63 * 8), and
+// the packed word is a plain sum of fields, so inclusive minus own count
+// recovers them exactly even when lane 63's inclusive total carries over.
+// Returns each row's exclusive prefix in ex[]; tot[] (lane 63 only) gets the
+// row totals.
+template <int EPL, int V>
+__device__ __forceinline__ void packed_row_scan(const uint32_t (&cnt)[V], uint32_t (&ex)[V], uint32_t (&tot)[V]) {
+  constexpr int F = EPL <= 4 ? 8 : 16;   // field width
+  constexpr int PER = 32 / F;            // rows per scanned word
+  static_assert(V % PER == 0, "rows must fill the packed words");
+#pragma unroll
+  for (int g = 0; g < V / PER; ++g) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) c |= cnt[g * PER + i] << (F * i);
+    const uint32_t e = wave_incl_scan(c) - c;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int j = g * PER + i;
+      ex[j] = __builtin_amdgcn_ubfe(e, F * i, F);
+      tot[j] = ex[j] + cnt[j];
+    }
+  }
+}
+
 template <int ESZ>
 __device__ __forceinline__ uint32_t vec_elem(u32x4 v, int k) {
   if constexpr (ESZ == 4) return v[k];

@@ -1,9 +1,9 @@
 // zvc_compress.hpp -- ZVC compression for gfx950 (stream format in
 // zvc_common.hpp): load -> per-lane nonzero bits -> window masks (DPP OR) and
-// per-lane counts (DPP wave scan) -> LDS pass over the wave segments -> masks
-// stored at their fixed place -> nonzeros compacted into LDS -> the tile's
-// value offset from a per-workgroup chain sum over published tile aggregates
-// -> realigned 16-byte stores.
+// per-lane counts (one packed DPP wave scan) -> LDS pass over the wave
+// segments -> masks stored at their fixed place -> nonzeros compacted into LDS
+// -> the tile's value offset from a per-workgroup chain sum over published
+// tile aggregates -> realigned 16-byte stores.
 #pragma once
 
 #include "zvc_common.hpp"
@@ -23,40 +23,51 @@ namespace cdma {
 // Vector-memory counters retire in order on this GPU, so a wave that had both
 // prefetched a tile and issued status reads could not use the tile before the
 // status reads came back; with the status traffic in a wave of its own, the
-// data waves wait only for their own loads.  Iteration i of a workgroup holds
-// tile t (loaded), tn (to prefetch) and the previous tile tp (nonzeros staged
-// in LDS):
-//   data waves:   classify t (window masks, nonzero counts) -> B1 -> store
-//                 t's masks, compact t's nonzeros into LDS buffer i%2, issue
-//                 tn's loads -> B2 -> store tp's staged values at the offset
-//                 the control wave resolved;
-//   control wave: B1 -> publish t's aggregate (static tiles) -> hand the data
-//                 waves the next tile and, with tickets, draw the one after it
-//                 and publish -> finish tp's chain sum (aggregates of the tiles
-//                 between this workgroup's previous tile and tp, read one
-//                 iteration earlier) -> B2 -> issue the first round of t's
-//                 chain sum.
-// The ticket counter is one word hit by every workgroup, so its atomic comes
-// back slower than a load; drawing right after the hand-over gives it a whole
-// iteration, and static tiles need none.
+// data waves wait only for their own loads.
+//
+// A tile passes through three iterations of its workgroup: iteration i
+// classifies tile t_i, iteration i+1 compacts its nonzeros into LDS stage
+// buffer i%2, iteration i+2 stores them.  Two stage buffers suffice, since the
+// store of t_{i-2} precedes the compaction of t_i into the same buffer by a
+// barrier.  The value offset of t_{i-2} needs the aggregates of every tile
+// before it; those of the tiles classified alongside it by other workgroups
+// are published in their iteration i-2, and this workgroup reads them in its
+// iteration i-1 and sums them at the start of iteration i: a whole iteration
+// of slack, so a workgroup that runs a little behind the others rarely makes
+// another wait.  Iteration i (buffer b = i%2):
+//   phase X  data waves:   compact t_{i-1} into stage[b^1]; issue the loads
+//                          of t_{i+1} into the registers t_{i-1} held; wait
+//                          for t_i (loaded one iteration earlier) and
+//                          classify it (window masks, nonzero counts)
+//            control wave: finish t_{i-2}'s chain sum -> its value offset
+//   B1
+//   phase Y  data waves:   segment bases of t_i; store t_{i-2}'s staged
+//                          values from stage[b]
+//            control wave: publish t_i's aggregate, hand the data waves the
+//                          tile they load next iteration (drawing a ticket
+//                          when tiles are not static), store t_i's masks,
+//                          issue the first round of t_{i-1}'s chain sum
+//   B2
+// The loads of t_{i+1} are issued by every wave on every path (the control
+// wave's and a missing tile's cover no bytes), so the compiler sees the same
+// loads after the other register set on every path and waits only for that
+// set when it classifies.
 // The size is reported with 64-bit atomic max operations on a word cleared
 // before the launch: the last tile writes the stream size and a control wave
 // whose chain sum hit the spin bound writes the all-ones error value, which
 // wins whatever the order.  (Such a sum returns an under-estimate, so every
 // store still lands inside the stream's bounds.)
 // Progress: every workgroup takes its tiles in increasing order and publishes
-// a tile's aggregate in the iteration that classifies it, before that
-// iteration waits on any other workgroup.  With tickets, a ticket is drawn only by a
-// running workgroup, so the smallest tile whose aggregate is unpublished is
-// held by a running workgroup that waits only for aggregates of smaller tiles,
-// all published: no co-residency is assumed and every chain sum ends.  Static
-// tiles are used only once every workgroup has started, so the owner of that
-// smallest tile is running too.
+// a tile's aggregate in the iteration that classifies it.  The only wait on
+// other workgroups, in phase X of iteration i, is for aggregates of tiles
+// before t_{i-2}; by then the workgroup has published every tile up to
+// t_{i-1}.  So the smallest unpublished tile u is held by a workgroup that
+// waits only for tiles below u, all published, and publishes u one phase
+// later.  With tickets, a ticket is drawn only by a running workgroup, so no
+// co-residency is assumed; static tiles are used only once every workgroup
+// has started, so the owner of u is running too.
 
-#ifndef CDMA_CBLOCK
-#define CDMA_CBLOCK 1024
-#endif
-constexpr int kCBlock = CDMA_CBLOCK;
+constexpr int kCBlock = 1024;
 constexpr int kCWaves = kCBlock / 64;
 constexpr int kDWaves = kCWaves - 1;  // data wavefronts; the last one is the control wave
 constexpr int kDThreads = kDWaves * 64;
@@ -77,25 +88,50 @@ struct ZvcCShape {
 template <int ESZ>
 struct ZvcCLds {
   using S = ZvcCShape<ESZ>;
-  uint64_t excl;         // exclusive prefix of the tile being stored
-  uint32_t total[2];     // nonzeros held in stage[b]
-  uint32_t next;         // ticket handed from the control wave to the data waves
+  uint64_t excl;         // value offset of the tile stored this iteration
+  uint32_t next;         // tile handed from the control wave to the data waves
   uint32_t mode;         // kModeStatic or kModeTickets (start_mode)
-  uint32_t init[3];      // the first three tickets
+  uint32_t init[3];      // the first tickets
   uint32_t tot[S::SEG];
-  uint32_t mask[S::WPT];
+  __attribute__((aligned(16))) uint32_t mask[S::WPT];
   __attribute__((aligned(16))) uint8_t stage[2][S::STAGE];
 };
 
+// What a data lane keeps of a classified tile until it is compacted, packed
+// into bit fields to leave registers for the two tiles in flight: per row j
+// (16-byte vector) the element nonzero bits (EPL bits at EPL*j of bits), the
+// nonzeros of the row before this lane (F bits at F*(j%PER) of ex[j/PER])
+// and the nonzeros of the tile before the row (16 bits at 16*(j%2) of
+// base[j/2]; a tile holds fewer than 2^16 elements).
+template <int EPL, int V>
+struct ZvcRows {
+  static constexpr int F = EPL <= 4 ? 8 : 16;
+  static constexpr int PER = 32 / F;
+  static_assert(EPL * V <= 32 && V % PER == 0 && V % 2 == 0, "row fields must fit");
+  uint32_t bits;
+  uint32_t ex[V / PER];
+  uint32_t base[V / 2];
+  __device__ __forceinline__ uint32_t bits_of(int j) const { return __builtin_amdgcn_ubfe(bits, EPL * j, EPL); }
+  __device__ __forceinline__ uint32_t ex_of(int j) const { return __builtin_amdgcn_ubfe(ex[j / PER], F * (j % PER), F); }
+  __device__ __forceinline__ uint32_t base_of(int j) const { return __builtin_amdgcn_ubfe(base[j / 2], 16 * (j % 2), 16); }
+};
+
+// Load tile t into v.  A buffer resource covers exactly the tile when it is
+// full (valid) and nothing otherwise, so an invalid tile's loads return zeros
+// without touching memory.  The loads are therefore issued on every path,
+// which lets the compiler count precisely which loads are still in flight
+// when the registers are next read (a load skipped on some path makes it wait
+// for everything).  valid must be wave-uniform.
 template <int ESZ>
 __device__ __forceinline__ void zvc_c_load_full(u32x4 (&v)[ZvcCShape<ESZ>::V], const uint8_t* __restrict__ src,
-                                                uint32_t t, int wave, int lane) {
+                                                uint32_t t, bool valid, int wave, int lane) {
   using S = ZvcCShape<ESZ>;
   const uint8_t* p = src + (uint64_t)t * (S::TE * ESZ);  // uniform tile base
-  uint32_t o = (uint32_t)((wave * S::V * 64 + lane) * 16);
-  asm volatile("" : "+v"(o));  // keep base + o from being hoisted into a 64-bit register pair
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p), (short)0, valid ? S::TE * ESZ : 0, kBufferFlags);
+  const uint32_t o = (uint32_t)((wave * S::V * 64 + lane) * 16);
 #pragma unroll
-  for (int j = 0; j < S::V; ++j) v[j] = ld_stream(reinterpret_cast<const u32x4*>(p + o + j * 1024));
+  for (int j = 0; j < S::V; ++j) v[j] = __builtin_amdgcn_raw_buffer_load_b128(r, o + j * 1024, 0, kLoadAux);
 }
 
 template <int ESZ>
@@ -135,121 +171,210 @@ __device__ __forceinline__ void zvc_c_epilogue(u32x4 (&v)[ZvcCShape<ESZ>::V], ui
   }
 }
 
-// One pipeline iteration (see above).  Returns the ticket the data waves
-// prefetch in the next iteration, with the workgroup synchronised.
-template <int ESZ, int OP>
-__device__ __forceinline__ uint32_t zvc_c_iteration(ZvcCLds<ESZ>& L, u32x4 (&cur)[ZvcCShape<ESZ>::V],
-                                                    u32x4 (&nxt)[ZvcCShape<ESZ>::V], ChainRound& cr,
-                                                    uint64_t& chain_lo, uint64_t& P, uint32_t& pend, uint32_t t,
-                                                    uint32_t tn, uint32_t tp, int buf,
-                                                    uint32_t full, uint64_t W, const uint8_t* __restrict__ src,
-                                                    uint64_t n, uint8_t* __restrict__ dst,
-                                                    uint64_t* __restrict__ out_bytes, uint32_t* __restrict__ agg,
-                                                    uint32_t* __restrict__ counter, uint32_t num_tiles,
-                                                    uint8_t* __restrict__ act, int tid, int wave, int lane,
-                                                    bool stat) {
+// Classify the tile held in v (data waves): its window masks go to L.mask,
+// each wave row's nonzero count to L.tot, and the lane's per-row bits and
+// in-row prefixes to R.
+template <int ESZ>
+__device__ __forceinline__ void zvc_c_classify(ZvcCLds<ESZ>& L, const u32x4 (&v)[ZvcCShape<ESZ>::V],
+                                               ZvcRows<ZvcCShape<ESZ>::EPL, ZvcCShape<ESZ>::V>& R, int wave, int lane) {
   using S = ZvcCShape<ESZ>;
   constexpr int V = S::V;
-  const bool have_cur = t < num_tiles;
-  const bool have_prev = tp < num_tiles;
-  const bool data = wave < kDWaves;
-
-  uint32_t bits[V], ex[V];
-  if (data && have_cur) {
-    if (t >= full) {  // the one partial tile: load bounded, drain so nothing stays pending on cur
-      zvc_c_load_bounded<ESZ>(cur, src, n, t, wave, lane);
-      __builtin_amdgcn_s_waitcnt(0);
-    }
-    if constexpr (OP != kOpNone) zvc_c_epilogue<ESZ, OP>(cur, act, n, t, t < full, wave, lane);
+  if constexpr (ESZ == 4) {
+    // each lane's bits land at their window-mask position directly, and the
+    // V rows' counts are scanned as one packed word
+    const uint32_t sh = (uint32_t)((lane % S::LPW) * S::EPL);
+    uint32_t cnt[V], ex[V], tot[V];
+    R.bits = 0;
 #pragma unroll
     for (int j = 0; j < V; ++j) {
       const uint32_t c = (uint32_t)((wave * V + j) * 64 + lane);
-      bits[j] = vec_nz_bits<ESZ>(cur[j]);
-      const uint32_t m = group_or<S::LPW>(bits[j] << ((lane % S::LPW) * S::EPL));
+      const uint32_t m = vec_nz_at<ESZ>(v[j], sh);
+      const uint32_t win = group_or<S::LPW>(m);
+      if (lane % S::LPW == 0) L.mask[c / S::LPW] = win;
+      R.bits |= (m >> sh) << (S::EPL * j);
+      cnt[j] = (uint32_t)__builtin_popcount(m);
+    }
+    packed_row_scan<S::EPL, V>(cnt, ex, tot);
+#pragma unroll
+    for (int g = 0; g < V / R.PER; ++g) {
+      R.ex[g] = 0;
+#pragma unroll
+      for (int i = 0; i < R.PER; ++i) R.ex[g] |= ex[g * R.PER + i] << (R.F * i);
+    }
+    if (lane == 63) {
+#pragma unroll
+      for (int j = 0; j < V; ++j) L.tot[wave * V + j] = tot[j];
+    }
+  } else {
+    // 16-bit elements: one scan per row measured faster than the packed form
+    R.bits = 0;
+#pragma unroll
+    for (int g = 0; g < V / R.PER; ++g) R.ex[g] = 0;
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      const uint32_t c = (uint32_t)((wave * V + j) * 64 + lane);
+      const uint32_t b = vec_nz_bits<ESZ>(v[j]);
+      R.bits |= b << (S::EPL * j);
+      const uint32_t m = group_or<S::LPW>(b << ((lane % S::LPW) * S::EPL));
       if (lane % S::LPW == 0) L.mask[c / S::LPW] = m;
-      const uint32_t cnt = (uint32_t)__builtin_popcount(bits[j]);
+      const uint32_t cnt = (uint32_t)__builtin_popcount(b);
       const uint32_t inc = wave_incl_scan(cnt);
-      ex[j] = inc - cnt;
+      R.ex[j / R.PER] |= (inc - cnt) << (R.F * (j % R.PER));
       if (lane == 63) L.tot[wave * V + j] = inc;
     }
   }
+}
+
+// Write the nonzeros of the tile held in v into stage, in index order, at the
+// places R gives (data waves).
+template <int ESZ>
+__device__ __forceinline__ void zvc_c_compact(uint8_t* __restrict__ st, const u32x4 (&v)[ZvcCShape<ESZ>::V],
+                                              const ZvcRows<ZvcCShape<ESZ>::EPL, ZvcCShape<ESZ>::V>& R) {
+  using S = ZvcCShape<ESZ>;
+#pragma unroll
+  for (int j = 0; j < S::V; ++j) {
+    uint32_t pos = ESZ * (R.base_of(j) + R.ex_of(j));
+    const uint32_t bits = R.bits_of(j);
+#pragma unroll
+    for (int k = 0; k < S::EPL; ++k) {
+      if ((bits >> k) & 1u) {
+        store_elem<ESZ>(st + pos, vec_elem<ESZ>(v[j], k));
+        pos += ESZ;
+      }
+    }
+  }
+}
+
+// Store tile t's window masks from L.mask to the stream with 16-byte stores
+// (the control wave; words at or past W are not written).  Issued by the
+// control wave so that no data wave has a store in flight, of a number the
+// compiler cannot count, ahead of the loads it waits for next (its memory
+// operations retire in order).
+template <int ESZ>
+__device__ __forceinline__ void zvc_c_store_masks(const ZvcCLds<ESZ>& L, uint8_t* __restrict__ dst, uint32_t t,
+                                                  uint64_t W, int lane) {
+  using S = ZvcCShape<ESZ>;
+  static_assert(S::WPT % 4 == 0, "whole mask quads per tile");
+  const uint64_t w0 = (uint64_t)t * S::WPT;
+  uint32_t* out = reinterpret_cast<uint32_t*>(dst) + w0;
+#pragma unroll
+  for (int k = 0; k < (S::WPT / 4 + 63) / 64; ++k) {
+    const int q = k * 64 + lane;
+    if (q < S::WPT / 4) {
+      const u32x4 m = *reinterpret_cast<const u32x4*>(&L.mask[4 * q]);
+      if (w0 + 4 * q + 4 <= W) {
+        *reinterpret_cast<u32x4*>(out + 4 * q) = m;
+      } else {
+        for (int i = 0; i < 4; ++i)
+          if (w0 + 4 * q + i < W) out[4 * q + i] = m[i];
+      }
+    }
+  }
+}
+
+// Per-iteration state of the control wave.
+struct ZvcCtl {
+  ChainRound cr;      // first round of the pending chain sum (issued last iteration)
+  uint64_t chain_lo;  // first tile of that sum
+  uint64_t P;         // inclusive value prefix of the last tile resolved
+  uint32_t pend;      // next tile to hand over (drawn ticket, or static successor)
+};
+
+// One iteration (see the description above).  t: tile to classify (its
+// loads were issued last iteration into cur); tp1, tp2: the two tiles before
+// it (compacted / stored now); tl: tile whose loads go into prev now.  T1, T2:
+// nonzeros of tp1, tp2; updated for the next iteration.  Returns the tile the
+// data waves load next iteration, with the workgroup synchronised.
+template <int ESZ, int OP>
+__device__ __forceinline__ uint32_t zvc_c_iteration(
+    ZvcCLds<ESZ>& L, u32x4 (&cur)[ZvcCShape<ESZ>::V], u32x4 (&prev)[ZvcCShape<ESZ>::V],
+    ZvcRows<ZvcCShape<ESZ>::EPL, ZvcCShape<ESZ>::V>& rc, const ZvcRows<ZvcCShape<ESZ>::EPL, ZvcCShape<ESZ>::V>& rp, ZvcCtl& C, uint32_t& T1, uint32_t& T2,
+    uint32_t t, uint32_t tp1, uint32_t tp2, uint32_t tl, int buf, uint32_t full, uint64_t W,
+    const uint8_t* __restrict__ src, uint64_t n, uint8_t* __restrict__ dst, uint64_t* __restrict__ out_bytes,
+    uint32_t* __restrict__ agg, uint32_t* __restrict__ counter, uint32_t num_tiles, uint8_t* __restrict__ act,
+    int tid, int wave, int lane, bool stat) {
+  using S = ZvcCShape<ESZ>;
+  constexpr int V = S::V;
+  const bool have_t = t < num_tiles;
+  const bool have_p1 = tp1 < num_tiles;
+  const bool have_p2 = tp2 < num_tiles;
+  const bool data = wave < kDWaves;
+
+  // ---- phase X ----
+  if (data && have_p1) zvc_c_compact<ESZ>(L.stage[buf ^ 1], prev, rp);
+  {
+    const bool load = __builtin_amdgcn_readfirstlane(wave) < kDWaves && tl < full;
+    zvc_c_load_full<ESZ>(prev, src, tl, load, wave, lane);
+  }
+  if (data) {
+    if (have_t) {
+      if (t >= full) {  // the one partial tile: load bounded, drain so nothing stays pending on cur
+        zvc_c_load_bounded<ESZ>(cur, src, n, t, wave, lane);
+        __builtin_amdgcn_s_waitcnt(0);
+      }
+      if constexpr (OP != kOpNone) zvc_c_epilogue<ESZ, OP>(cur, act, n, t, t < full, wave, lane);
+      zvc_c_classify<ESZ>(L, cur, rc, wave, lane);
+    }
+  } else if (have_p2) {
+    bool stuck = false;
+    const uint64_t X = C.P + chain_sum(agg, C.chain_lo, tp2, C.cr, &stuck, [](uint32_t v) { return v; });
+    if (lane == 0) {
+      L.excl = X;
+      if (stuck) atomicMax(reinterpret_cast<unsigned long long*>(out_bytes), kSizeInternalError);
+    }
+    C.P = X + T2;  // tp2's inclusive prefix
+  }
   __syncthreads();
 
+  // ---- phase Y ----
+  uint32_t Tn = 0;  // nonzeros of t
   if (data) {
-    if (have_cur) {
+    if (have_t) {
       // segment bases: lane l of every data wave scans the segment totals
       const uint32_t x = lane < S::SEG ? L.tot[lane] : 0u;
       const uint32_t inc = wave_incl_scan(x);
-      if (tid < S::WPT) {
-        const uint64_t g = (uint64_t)t * S::WPT + tid;
-        if (g < W) reinterpret_cast<uint32_t*>(dst)[g] = L.mask[tid];
-      }
-      uint8_t* st = L.stage[buf];
 #pragma unroll
-      for (int j = 0; j < V; ++j) {
-        uint32_t pos = ESZ * (read_lane(inc - x, wave * V + j) + ex[j]);
-#pragma unroll
-        for (int k = 0; k < S::EPL; ++k) {
-          if ((bits[j] >> k) & 1u) {
-            store_elem<ESZ>(st + pos, vec_elem<ESZ>(cur[j], k));
-            pos += ESZ;
-          }
-        }
-      }
-      if (tn < full) zvc_c_load_full<ESZ>(nxt, src, tn, wave, lane);
+      for (int j = 0; j < V; j += 2)
+        rc.base[j / 2] = read_lane(inc - x, wave * V + j) | (read_lane(inc - x, wave * V + j + 1) << 16);
+      Tn = read_lane(inc, 63);
+    }
+    if (have_p2) {
+      const uint64_t A = 4 * W + (uint64_t)ESZ * L.excl;
+      store_staged<ESZ, kDThreads>(L.stage[buf], ESZ * T2, A, dst, tid);
+      if (tp2 == num_tiles - 1 && tid == 0)
+        atomicMax(reinterpret_cast<unsigned long long*>(out_bytes), A + (uint64_t)ESZ * T2);
     }
   } else {
     // control wave
-    // publish t's aggregate: every other workgroup's chain sum may be waiting
-    // for it.  Static tiles publish before anything else; with tickets the
-    // hand-over below has to wait for the ticket anyway, and the aggregate
-    // follows it (waiting there would also wait for this store).
-    const uint32_t T = read_lane(wave_incl_scan(lane < S::SEG ? L.tot[lane] : 0u), 63);
-    if (stat && have_cur && lane == 0) {
-      L.total[buf] = T;
-      agg_publish(agg, t, T);
-    }
-    // what this wave issued last iteration (chain round, ticket) must be back
-    // before the hand-over; waiting here on every path keeps the compiler from
-    // waiting again after the ticket drawn next
-    __builtin_amdgcn_s_waitcnt(0);
-    if (lane == 0) L.next = pend;
-    if (have_cur) {
-      if (stat) {
-        pend += gridDim.x;
-      } else if (lane == 0) {
+    if (have_t) Tn = read_lane(wave_incl_scan(lane < S::SEG ? L.tot[lane] : 0u), 63);
+    if (stat) {
+      // every other workgroup's chain sums may be waiting for t's aggregate
+      if (have_t && lane == 0) agg_publish(agg, t, Tn);
+      if (lane == 0) L.next = C.pend;
+      if (have_t) C.pend += gridDim.x;
+    } else {
+      // the ticket drawn last iteration must be back before the hand-over;
+      // waiting here on every path keeps the compiler from waiting again
+      // after the ticket drawn next
+      __builtin_amdgcn_s_waitcnt(0);
+      if (lane == 0) L.next = C.pend;
+      if (have_t && lane == 0) {
         // the next ticket goes out now and has a whole iteration to come back
-        pend = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        L.total[buf] = T;
-        agg_publish(agg, t, T);
+        C.pend = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        agg_publish(agg, t, Tn);
       }
     }
-    if (have_prev) {
-      bool stuck = false;
-      const uint64_t X = P + chain_sum(agg, chain_lo, tp, cr, &stuck, [](uint32_t v) { return (uint64_t)v; });
-      if (lane == 0) {
-        L.excl = X;
-        if (stuck) atomicMax(reinterpret_cast<unsigned long long*>(out_bytes), kSizeInternalError);
-      }
-      P = X + L.total[buf ^ 1];  // tp's inclusive prefix
+    if (have_t) zvc_c_store_masks<ESZ>(L, dst, t, W, lane);
+    if (have_p1) {
+      // tp1's chain sum: the tiles between this workgroup's tile before it
+      // (tp2) and tp1; summed at the start of the next iteration
+      C.chain_lo = have_p2 ? (uint64_t)tp2 + 1 : 0;
+      chain_issue(agg, C.chain_lo, tp1, C.cr);
     }
   }
+  T2 = T1;
+  T1 = Tn;
   __syncthreads();
-
-  if (data) {
-    if (have_prev) {
-      const uint32_t T = L.total[buf ^ 1];
-      const uint64_t A = 4 * W + (uint64_t)ESZ * L.excl;
-      store_staged<ESZ, kDThreads>(L.stage[buf ^ 1], ESZ * T, A, dst, tid);
-      if (tp == num_tiles - 1 && tid == 0)
-        atomicMax(reinterpret_cast<unsigned long long*>(out_bytes), A + (uint64_t)ESZ * T);
-    }
-  } else if (have_cur) {
-    // the first round of t's chain sum goes out while the data waves store,
-    // late enough that the tiles drawn just before t are mostly classified
-    chain_lo = have_prev ? (uint64_t)tp + 1 : 0;
-    chain_issue(agg, chain_lo, t, cr);
-  }
   return __builtin_amdgcn_readfirstlane(L.next);  // uniform: keeps tile bases in SGPRs
 }
 
@@ -276,35 +401,40 @@ __global__ __launch_bounds__(kCBlock) void zvc_compress_kernel(
     L.init[wave] = stat ? blockIdx.x + wave * gridDim.x
                         : __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
-  // the first three tickets in increasing order: classify, prefetch, hand over
+  // the first three tickets in increasing order: classify, load, hand over
   const uint32_t a = __builtin_amdgcn_readfirstlane(L.init[0]);
   const uint32_t b = __builtin_amdgcn_readfirstlane(L.init[1]);
   const uint32_t c = __builtin_amdgcn_readfirstlane(L.init[2]);
   const uint32_t lo = min(a, min(b, c)), hi = max(a, max(b, c));
-  uint32_t t = lo;
-  uint32_t tn = a + b + c - lo - hi;
-  uint32_t pend = hi;        // meaningful in the control wave only
-  uint32_t tp = num_tiles;   // tile to store (none yet)
+  uint32_t t = lo;                     // classified this iteration
+  uint32_t tl = a + b + c - lo - hi;   // loaded this iteration
+  uint32_t tp1 = num_tiles, tp2 = num_tiles;  // compacted / stored this iteration (none yet)
+  ZvcCtl C;                            // control wave
+  C.chain_lo = 0;
+  C.P = 0;
+  C.pend = hi;
+  uint32_t T1 = 0, T2 = 0;
   u32x4 ra[S::V], rb[S::V];
-  ChainRound cr;           // control wave: chain sum in flight
-  uint64_t chain_lo = 0;   // control wave: first tile of that sum
-  uint64_t P = 0;          // control wave: inclusive prefix of the last resolved tile
-  if (wave < kDWaves && t < full) zvc_c_load_full<ESZ>(ra, src, t, wave, lane);
-  // two iterations per trip so the register sets swap roles without copies;
-  // an iteration with no tile left to classify only stores the last one
+  ZvcRows<S::EPL, S::V> qa, qb;
+  zvc_c_load_full<ESZ>(ra, src, t, __builtin_amdgcn_readfirstlane(wave) < kDWaves && t < full, wave, lane);
+  // Two iterations per trip so the register sets swap roles without copies.
+  // One exit, after the second iteration of a trip: an iteration with no tile
+  // to classify, compact or store only passes its barriers, and a single path
+  // back to the loop head keeps the compiler's count of loads in flight exact.
   for (;;) {
-    uint32_t tnn = zvc_c_iteration<ESZ, OP>(L, ra, rb, cr, chain_lo, P, pend, t, tn, tp, 0, full, W, src, n, dst,
-                                            out_bytes, agg, counter, num_tiles, act, tid, wave, lane, stat);
-    if (t >= num_tiles) break;
-    tp = t;
-    t = tn;
-    tn = tnn;
-    tnn = zvc_c_iteration<ESZ, OP>(L, rb, ra, cr, chain_lo, P, pend, t, tn, tp, 1, full, W, src, n, dst,
-                                   out_bytes, agg, counter, num_tiles, act, tid, wave, lane, stat);
-    if (t >= num_tiles) break;
-    tp = t;
-    t = tn;
-    tn = tnn;
+    uint32_t r = zvc_c_iteration<ESZ, OP>(L, ra, rb, qa, qb, C, T1, T2, t, tp1, tp2, tl, 0, full, W, src, n, dst,
+                                          out_bytes, agg, counter, num_tiles, act, tid, wave, lane, stat);
+    tp2 = tp1;
+    tp1 = t;
+    t = tl;
+    tl = r;
+    r = zvc_c_iteration<ESZ, OP>(L, rb, ra, qb, qa, C, T1, T2, t, tp1, tp2, tl, 1, full, W, src, n, dst, out_bytes,
+                                 agg, counter, num_tiles, act, tid, wave, lane, stat);
+    tp2 = tp1;
+    tp1 = t;
+    t = tl;
+    tl = r;
+    if (t >= num_tiles && tp1 >= num_tiles && tp2 >= num_tiles) break;
   }
 }
 

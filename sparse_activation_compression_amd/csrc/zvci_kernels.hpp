@@ -183,7 +183,7 @@ __device__ __forceinline__ uint32_t zvi_c_iteration(ZviCLds<ESZ>& L, u32x4 (&cur
     }
     if (have_prev) {
       bool stuck = false;
-      const uint64_t X = pfx + chain_sum(agg, chain_lo, tp, cr, &stuck, [](uint32_t v) { return (uint64_t)v; });
+      const uint64_t X = pfx + chain_sum(agg, chain_lo, tp, cr, &stuck, [](uint32_t v) { return v; });
       if (lane == 0) {
         L.excl = X;
         if (stuck) atomicMax(reinterpret_cast<unsigned long long*>(out_bytes), kSizeInternalError);
