@@ -46,7 +46,7 @@ _lib = None
 
 def build(src: str = _SRC, out: str = _LIB, extra=()) -> str:
     """Compile the oracle with plain gcc -O2 (no target-specific flags)."""
-    cmd = ["gcc", "-O2", "-std=c99", "-Wall", "-Wextra", "-shared", "-fPIC",
+    cmd = ["gcc", "-O2", "-std=c99", "-Wall", "-Wextra", "-shared", "-fPIC", "-pthread",
            *extra, src, "-o", out]
     subprocess.run(cmd, check=True)
     return out
@@ -79,6 +79,14 @@ def load(path: str | None = None):
         f.argtypes = [vp, u64, u64, ctypes.c_int, vp, u32p]
     lib.oracle_relu.restype = ctypes.c_int
     lib.oracle_relu.argtypes = [vp, u64, ctypes.c_int, vp]
+    for name in ("oracle_zvc_compress_mt", "oracle_rle_compress_mt"):
+        f = getattr(lib, name)
+        f.restype = ctypes.c_int
+        f.argtypes = [vp, u64, ctypes.c_int, vp, u64, u64p, ctypes.c_int]
+    for name in ("oracle_zvc_decompress_mt", "oracle_rle_decompress_mt"):
+        f = getattr(lib, name)
+        f.restype = ctypes.c_int
+        f.argtypes = [vp, u64, u64, ctypes.c_int, vp, u32p, ctypes.c_int]
     if path is None:
         _lib = lib
     return lib
@@ -104,23 +112,23 @@ def max_rle_bytes(n: int, esz: int) -> int:
     return 8 * (wr + 1) + 2 * (n + 2 * wr) + esz * n
 
 
-def _compress(fn, x, cap_fn, lib):
+def _compress(fn, x, cap_fn, lib, *extra):
     b = _bits(x)
     n, esz = b.size, b.dtype.itemsize
     out = np.zeros(max(1, cap_fn(n, esz)), dtype=np.uint8)
     size = ctypes.c_uint64(0)
-    rc = getattr(lib, fn)(b.ctypes.data, n, esz, out.ctypes.data, out.size, ctypes.byref(size))
+    rc = getattr(lib, fn)(b.ctypes.data, n, esz, out.ctypes.data, out.size, ctypes.byref(size), *extra)
     if rc != 0:
         raise RuntimeError(f"{fn} failed with {rc}")
     return out[: size.value].copy()
 
 
-def _decompress(fn, stream, n, esz, lib):
+def _decompress(fn, stream, n, esz, lib, *extra):
     s = np.ascontiguousarray(np.asarray(stream, dtype=np.uint8))
     out = np.zeros(max(1, n), dtype=np.uint32 if esz == 4 else np.uint16)
     err = ctypes.c_uint32(0)
     rc = getattr(lib, fn)(s.ctypes.data if s.size else None, s.size, n, esz,
-                          out.ctypes.data, ctypes.byref(err))
+                          out.ctypes.data, ctypes.byref(err), *extra)
     if rc != 0:
         raise RuntimeError(f"{fn} failed with {rc}")
     return out[:n], err.value
@@ -144,6 +152,26 @@ def rle_compress(x, lib=None) -> np.ndarray:
 def rle_decompress(stream, n: int, esz: int, lib=None):
     """(patterns, error bits) decoded from an RLE stream."""
     return _decompress("oracle_rle_decompress", stream, n, esz, lib or load())
+
+
+# The same definitions on several host threads: each thread counts its own
+# range of windows, a prefix places the ranges, each thread writes its range.
+# The results equal the single-threaded functions' byte for byte.
+
+def zvc_compress_mt(x, threads: int, lib=None) -> np.ndarray:
+    return _compress("oracle_zvc_compress_mt", x, max_zvc_bytes, lib or load(), int(threads))
+
+
+def zvc_decompress_mt(stream, n: int, esz: int, threads: int, lib=None):
+    return _decompress("oracle_zvc_decompress_mt", stream, n, esz, lib or load(), int(threads))
+
+
+def rle_compress_mt(x, threads: int, lib=None) -> np.ndarray:
+    return _compress("oracle_rle_compress_mt", x, max_rle_bytes, lib or load(), int(threads))
+
+
+def rle_decompress_mt(stream, n: int, esz: int, threads: int, lib=None):
+    return _decompress("oracle_rle_decompress_mt", stream, n, esz, lib or load(), int(threads))
 
 
 def max_zvci_bytes(n: int, esz: int) -> int:
