@@ -30,7 +30,7 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRC = os.path.join(_HERE, "oracle.c")
+_SRC = os.path.join(_HERE, "oracle_mt.c")  # includes oracle.c
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 # decode error bits (same meaning as the library's, defined here on their own)
@@ -79,14 +79,18 @@ def load(path: str | None = None):
         f.argtypes = [vp, u64, u64, ctypes.c_int, vp, u32p]
     lib.oracle_relu.restype = ctypes.c_int
     lib.oracle_relu.argtypes = [vp, u64, ctypes.c_int, vp]
+    # the threaded forms (oracle_mt.c); a library built from oracle.c alone
+    # (the planted-mistake tests) has only the single-threaded functions
     for name in ("oracle_zvc_compress_mt", "oracle_rle_compress_mt"):
-        f = getattr(lib, name)
-        f.restype = ctypes.c_int
-        f.argtypes = [vp, u64, ctypes.c_int, vp, u64, u64p, ctypes.c_int]
+        if hasattr(lib, name):
+            f = getattr(lib, name)
+            f.restype = ctypes.c_int
+            f.argtypes = [vp, u64, ctypes.c_int, vp, u64, u64p, ctypes.c_int]
     for name in ("oracle_zvc_decompress_mt", "oracle_rle_decompress_mt"):
-        f = getattr(lib, name)
-        f.restype = ctypes.c_int
-        f.argtypes = [vp, u64, u64, ctypes.c_int, vp, u32p, ctypes.c_int]
+        if hasattr(lib, name):
+            f = getattr(lib, name)
+            f.restype = ctypes.c_int
+            f.argtypes = [vp, u64, u64, ctypes.c_int, vp, u32p, ctypes.c_int]
     if path is None:
         _lib = lib
     return lib
