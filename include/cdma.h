@@ -47,9 +47,11 @@
  * workspaces, scratch, pinned host memory, size and error words) and keeps it
  * alive until the enqueued work has finished.  cdma_compress and
  * cdma_decompress allocate nothing.  cdma_offload_async allocates its handle,
- * a few events, a small pinned size array and one worker thread, all
- * released by cdma_offload_destroy; cdma_prefetch_async the same without the
- * thread, released by cdma_prefetch_destroy.
+ * a few events and one worker thread, released by cdma_offload_destroy, and
+ * takes a small pinned array for the chunk sizes from a pool that the library
+ * keeps for the life of the process (allocated on first need, reused by
+ * later calls); cdma_prefetch_async the same without the thread, released by
+ * cdma_prefetch_destroy.
  *
  * Errors.  Argument and capacity problems are found on the host before
  * anything is enqueued and are returned as a status.  A failing HIP call
@@ -72,6 +74,8 @@ extern "C" {
 #define CDMA_ERR_CAPACITY    2  /* destination, workspace or host buffer too small */
 #define CDMA_ERR_CORRUPT     3  /* host-side decode check: a prefetch chunk size no stream can have */
 #define CDMA_ERR_HIP         4  /* a HIP runtime call failed */
+#define CDMA_ERR_INTERNAL    5  /* offload: a chunk's compressor reported that its cross-workgroup
+                                   scan did not complete (never expected) */
 
 /* algorithms */
 #define CDMA_ALGO_ZVC  0
@@ -101,7 +105,10 @@ extern "C" {
 
 /*
  * Upper bound of the compressed size of n elements (the size of an all-dense
- * input), in bytes.  Returns 0 for an invalid algo/esz.
+ * input), in bytes: what a caller allocates for a stream before its actual
+ * size is known (§V.D sizes the host allocation from the compression ratio
+ * observed; a device buffer for one call must hold the worst case).  Returns 0
+ * for an invalid algo/esz or an n past the codec's limit.
  *   ZVC:  4*ceil(n/32) + esz*n
  *   RLE:  8*(ceil(n/E)+1) + 2*(n + 2*ceil(n/E)) + esz*n
  *   ZVCI: 4*(ceil(n/E)+1) + 4*ceil(n/32) + esz*n
@@ -110,10 +117,15 @@ uint64_t cdma_max_compressed_bytes(int algo, int esz, uint64_t n);
 
 /*
  * Device workspace (bytes) that cdma_compress / cdma_decompress need for n
- * elements: a tile counter, one 8-byte scan status word per tile and, for
- * ZVC, one 4-byte value offset per tile.  The library clears what it needs
- * itself at the start of each call.  Workspaces of calls
- * that may overlap in time must be distinct.  Returns 0 for invalid input.
+ * elements (§V.D leaves all buffers to the caller; so does this library).
+ * Layout: a 2 KB header (tile ticket counter, the two words that choose
+ * static or ticketed tiles, eight ticket-class counters, each on a 128-byte
+ * line of its own), then one 32-bit published aggregate per compress tile.
+ * ZVC decompress reuses the same space for one 32-bit value offset per 16 KB
+ * decompress tile and one total per 32 KB of masks.  The library clears what
+ * it needs itself at the start of each call (with a kernel, not a memset).
+ * Workspaces of calls that may overlap in time must be distinct.  Returns 0
+ * for invalid input.
  */
 uint64_t cdma_workspace_bytes(int algo, int esz, uint64_t n);
 
@@ -197,7 +209,10 @@ int cdma_decompress(int algo, int esz, const void *d_src, uint64_t src_capacity,
  *                 cdma_offload_wait returns CDMA_ERR_CAPACITY; nothing past
  *                 h_capacity is ever written.
  *   d_scratch     device, 256-byte aligned, scratch_bytes >=
- *                 cdma_offload_scratch_bytes(algo, esz, chunk_elems, slots).
+ *                 cdma_offload_scratch_bytes(algo, esz, chunk_elems, slots):
+ *                 per slot, a chunk stream's staging, a compress workspace
+ *                 and the device word its size is written to (copied to the
+ *                 host on compute_stream, 8 bytes per chunk).
  *   slots         staging slots, >= 1 (2 or 3 overlap compression and copy).
  *   compute_stream, copy_stream  distinct streams (void* hipStream_t); the
  *                 caller enqueues nothing else on them until the wait returns.
@@ -218,7 +233,9 @@ int cdma_offload_async(int algo, int esz, const void *d_src, uint64_t n,
  * h_dst, chunk_bytes[k] (for k < max_chunks) each chunk's stream size and
  * *n_chunks the number of chunks copied.  Any output pointer may be NULL.
  * Returns CDMA_OK, CDMA_ERR_CAPACITY (host buffer too small; the sizes cover
- * the chunks copied) or CDMA_ERR_HIP.  May be called once per handle.
+ * the chunks copied), CDMA_ERR_INTERNAL (a chunk's compressor reported an
+ * incomplete scan; no further chunk is copied) or CDMA_ERR_HIP.  May be
+ * called once per handle.
  */
 int cdma_offload_wait(cdma_offload_t h, uint64_t *total_bytes, uint64_t *chunk_bytes,
                       uint64_t max_chunks, uint64_t *n_chunks);
@@ -273,7 +290,8 @@ int cdma_prefetch_wait(cdma_prefetch_t h);
 /* Release a handle (waits for it first). */
 void cdma_prefetch_destroy(cdma_prefetch_t h);
 
-/* Static description of a status code. */
+/* Static description of a status code (the CDMA_OK ... CDMA_ERR_* values
+   above; "unknown status" otherwise).  The returned string is never freed. */
 const char *cdma_status_string(int status);
 
 /* Library version as 10000*major + 100*minor + patch. */

@@ -23,6 +23,13 @@ FMT_F32 = 0
 FMT_F16 = 1
 FMT_BF16 = 2
 
+CDMA_OK = 0
+CDMA_ERR_INVALID_ARG = 1
+CDMA_ERR_CAPACITY = 2
+CDMA_ERR_CORRUPT = 3
+CDMA_ERR_HIP = 4
+CDMA_ERR_INTERNAL = 5
+
 CDMA_E_MASK_PAST_N = 1 << 0
 CDMA_E_SIZE = 1 << 1
 CDMA_E_INDEX = 1 << 3
@@ -172,6 +179,17 @@ def _stream_handle(stream):
     return s.cuda_stream
 
 
+def _on(stream):
+    """Context in which the buffers a helper allocates for the caller (the
+    workspace, the error word, outputs) are made and zeroed on ``stream``:
+    the library's kernels run there, so the zeroing precedes them in stream
+    order and the workspace, returned to ``stream``'s pool when the helper
+    returns, is reused only by later work on that same stream."""
+    import contextlib
+    import torch
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
 def _check(fn, rc):
     if rc != 0:
         raise CdmaError(fn, rc)
@@ -195,6 +213,8 @@ def compress(x, algo="zvc", dst=None, out_bytes=None, ws=None, stream=None):
     Returns (dst, out_bytes): ``dst`` is a uint8 device buffer of the maximal
     compressed size holding the stream in its first ``out_bytes[0]`` bytes;
     ``out_bytes`` is a 1-element int64 device tensor filled in stream order.
+    With ``stream``, the work runs on that stream and any buffer made here is
+    made on it; the caller orders ``x`` (and buffers passed in) before it.
     """
     import torch
     a = _ALGOS[algo]
@@ -202,14 +222,15 @@ def compress(x, algo="zvc", dst=None, out_bytes=None, ws=None, stream=None):
         raise ValueError("input must be contiguous")
     esz, n = _esz(x), x.numel()
     cap = cdma_max_compressed_bytes(a, esz, n)
-    if dst is None:
-        dst = torch.empty(max(16, cap), dtype=torch.uint8, device=x.device)
-    if out_bytes is None:
-        out_bytes = torch.empty(1, dtype=torch.int64, device=x.device)
-    if ws is None:
-        ws = workspace(a, esz, n, x.device)
-    rc = cdma_compress(a, esz, x.data_ptr(), n, dst.data_ptr(), dst.numel(), out_bytes.data_ptr(),
-                       ws.data_ptr(), ws.numel(), _stream_handle(stream))
+    with _on(stream):
+        if dst is None:
+            dst = torch.empty(max(16, cap), dtype=torch.uint8, device=x.device)
+        if out_bytes is None:
+            out_bytes = torch.empty(1, dtype=torch.int64, device=x.device)
+        if ws is None:
+            ws = workspace(a, esz, n, x.device)
+        rc = cdma_compress(a, esz, x.data_ptr(), n, dst.data_ptr(), dst.numel(), out_bytes.data_ptr(),
+                           ws.data_ptr(), ws.numel(), _stream_handle(stream))
     _check("cdma_compress", rc)
     return dst, out_bytes
 
@@ -234,17 +255,19 @@ def relu_compress(x, algo="zvc", act=None, dst=None, out_bytes=None, ws=None, st
     if not x.is_contiguous():
         raise ValueError("input must be contiguous")
     fmt, esz, n = _fmt_of(x), x.element_size(), x.numel()
-    if act is True:
-        act = torch.empty_like(x)
     cap = cdma_max_compressed_bytes(a, esz, n)
-    if dst is None:
-        dst = torch.empty(max(16, cap), dtype=torch.uint8, device=x.device)
-    if out_bytes is None:
-        out_bytes = torch.empty(1, dtype=torch.int64, device=x.device)
-    if ws is None:
-        ws = workspace(a, esz, n, x.device)
-    rc = cdma_relu_compress(a, fmt, x.data_ptr(), n, act.data_ptr() if act is not None else None, dst.data_ptr(),
-                            dst.numel(), out_bytes.data_ptr(), ws.data_ptr(), ws.numel(), _stream_handle(stream))
+    with _on(stream):
+        if act is True:
+            act = torch.empty_like(x)
+        if dst is None:
+            dst = torch.empty(max(16, cap), dtype=torch.uint8, device=x.device)
+        if out_bytes is None:
+            out_bytes = torch.empty(1, dtype=torch.int64, device=x.device)
+        if ws is None:
+            ws = workspace(a, esz, n, x.device)
+        rc = cdma_relu_compress(a, fmt, x.data_ptr(), n, act.data_ptr() if act is not None else None,
+                                dst.data_ptr(), dst.numel(), out_bytes.data_ptr(), ws.data_ptr(), ws.numel(),
+                                _stream_handle(stream))
     _check("cdma_relu_compress", rc)
     return dst, out_bytes, act
 
@@ -260,15 +283,16 @@ def decompress(src, n: int, esz: int, algo="zvc", src_bytes=None, out=None, erro
     import torch
     a = _ALGOS[algo]
     dev = src.device
-    if out is None:
-        out = torch.empty(max(1, n), dtype=torch.int32 if esz == 4 else torch.int16, device=dev)[:n]
-    if error is None:
-        error = torch.zeros(1, dtype=torch.int32, device=dev)
-    if ws is None:
-        ws = workspace(a, esz, n, dev)
-    rc = cdma_decompress(a, esz, src.data_ptr(), src.numel(),
-                         src_bytes.data_ptr() if src_bytes is not None else None, n, out.data_ptr(),
-                         error.data_ptr(), ws.data_ptr(), ws.numel(), _stream_handle(stream))
+    with _on(stream):
+        if out is None:
+            out = torch.empty(max(1, n), dtype=torch.int32 if esz == 4 else torch.int16, device=dev)[:n]
+        if error is None:
+            error = torch.zeros(1, dtype=torch.int32, device=dev)
+        if ws is None:
+            ws = workspace(a, esz, n, dev)
+        rc = cdma_decompress(a, esz, src.data_ptr(), src.numel(),
+                             src_bytes.data_ptr() if src_bytes is not None else None, n, out.data_ptr(),
+                             error.data_ptr(), ws.data_ptr(), ws.numel(), _stream_handle(stream))
     _check("cdma_decompress", rc)
     return out, error
 

@@ -12,7 +12,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libcdma.so")
 
-SOURCES = ("kernels.hip", "cdma_api.cpp", "offload.cpp", "prefetch.cpp")
+SOURCES = ("kernels.hip", "cdma_api.cpp", "offload.cpp", "prefetch.cpp", "pinned_pool.cpp")
 
 
 def hipcc() -> str:

@@ -16,6 +16,11 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 uint64_t max_n(int algo) { return algo == CDMA_ALGO_RLE ? CDMA_RLE_MAX_N : CDMA_ZVC_MAX_N; }
 uint64_t rle_window(int esz) { return 4096u / (unsigned)esz; }
 
+// Whether compressing n elements writes stream bytes: every nonempty input
+// does, and so does an empty one for the codecs whose stream opens with an
+// index (RLE: 8 bytes, interleaved ZVC: 4 bytes).
+bool writes_stream(int algo, uint64_t n) { return n > 0 || algo != CDMA_ALGO_ZVC; }
+
 uint64_t tiles(int algo, int esz, uint64_t n) {
   if (algo == CDMA_ALGO_ZVC) return cdma::zvc_tiles(esz, n);
   return algo == CDMA_ALGO_RLE ? cdma::rle_compress_tiles(esz, n) : cdma::zvci_compress_tiles(esz, n);
@@ -45,9 +50,7 @@ int cdma_compress(int algo, int esz, const void* d_src, uint64_t n, void* d_dst,
                   uint64_t* d_out_bytes, void* d_ws, uint64_t ws_bytes, void* stream) {
   if (!algo_ok(algo) || !esz_ok(esz) || n > max_n(algo)) return CDMA_ERR_INVALID_ARG;
   if (!d_out_bytes || !aligned(d_out_bytes, 8)) return CDMA_ERR_INVALID_ARG;
-  if (!d_dst || !aligned(d_dst, 16)) {
-    if (n > 0 || algo == CDMA_ALGO_RLE) return CDMA_ERR_INVALID_ARG;  // an empty RLE stream is 8 bytes
-  }
+  if (writes_stream(algo, n) && (!d_dst || !aligned(d_dst, 16))) return CDMA_ERR_INVALID_ARG;
   if (dst_capacity < cdma_max_compressed_bytes(algo, esz, n)) return CDMA_ERR_CAPACITY;
   if (n > 0) {
     if (!d_src || !d_ws) return CDMA_ERR_INVALID_ARG;
@@ -68,9 +71,7 @@ int cdma_relu_compress(int algo, int fmt, const void* d_src, uint64_t n, void* d
   const int esz = fmt == CDMA_FMT_F32 ? 4 : 2;
   if ((algo != CDMA_ALGO_ZVC && algo != CDMA_ALGO_RLE) || n > max_n(algo)) return CDMA_ERR_INVALID_ARG;
   if (!d_out_bytes || !aligned(d_out_bytes, 8)) return CDMA_ERR_INVALID_ARG;
-  if (!d_dst || !aligned(d_dst, 16)) {
-    if (n > 0 || algo == CDMA_ALGO_RLE) return CDMA_ERR_INVALID_ARG;
-  }
+  if (writes_stream(algo, n) && (!d_dst || !aligned(d_dst, 16))) return CDMA_ERR_INVALID_ARG;
   if (dst_capacity < cdma_max_compressed_bytes(algo, esz, n)) return CDMA_ERR_CAPACITY;
   if (n > 0) {
     if (!d_src || !d_ws) return CDMA_ERR_INVALID_ARG;
@@ -99,8 +100,11 @@ int cdma_decompress(int algo, int esz, const void* d_src, uint64_t src_capacity,
   if (!algo_ok(algo) || !esz_ok(esz) || n > max_n(algo)) return CDMA_ERR_INVALID_ARG;
   if (d_src_bytes && !aligned(d_src_bytes, 8)) return CDMA_ERR_INVALID_ARG;
   if (d_error && !aligned(d_error, 4)) return CDMA_ERR_INVALID_ARG;
+  // the stream is read whatever n is (an empty RLE or interleaved stream still
+  // has its index, checked on the device)
+  if (src_capacity > 0 && !d_src) return CDMA_ERR_INVALID_ARG;
   if (n > 0) {
-    if (!d_dst || !d_ws || (src_capacity > 0 && !d_src)) return CDMA_ERR_INVALID_ARG;
+    if (!d_dst || !d_ws) return CDMA_ERR_INVALID_ARG;
     if (!aligned(d_src, 16) || !aligned(d_dst, 16) || !aligned(d_ws, 8)) return CDMA_ERR_INVALID_ARG;
     if (ws_bytes < cdma_workspace_bytes(algo, esz, n)) return CDMA_ERR_CAPACITY;
   }
@@ -121,6 +125,7 @@ const char* cdma_status_string(int status) {
     case CDMA_ERR_CAPACITY: return "buffer too small";
     case CDMA_ERR_CORRUPT: return "corrupt stream";
     case CDMA_ERR_HIP: return "HIP runtime error";
+    case CDMA_ERR_INTERNAL: return "internal error";
     default: return "unknown status";
   }
 }

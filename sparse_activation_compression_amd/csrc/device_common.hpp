@@ -1,5 +1,5 @@
-// device_common.hpp -- wave-level primitives and the decoupled-lookback scan
-// shared by the gfx950 codec kernels.
+// device_common.hpp -- wave-level primitives and the cross-workgroup offset
+// machinery shared by the gfx950 codec kernels.
 //
 // The codec is stream compaction (compress) and expansion (decompress): the
 // only arithmetic is integer compares, popcounts and prefix sums, which is
@@ -7,8 +7,9 @@
 // Deep Neural Networks" (§V.A Compression Algorithm, §V.B Compressing DMA
 // Engine Architecture) names as the cost of its hardware units.  Here the
 // prefix sums run at three levels: DPP scans inside a 64-lane wavefront, an
-// LDS pass across the 4 waves of a workgroup, and a decoupled lookback across
-// workgroups through one 64-bit status word per tile in device memory.
+// LDS pass across the wavefronts of a workgroup, and, across workgroups, a
+// chain sum per persistent workgroup over the 32-bit aggregates that every
+// compress tile publishes (see chain_sum below).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -101,8 +102,7 @@ __device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
   return v;
 }
 
-// ---- decoupled lookback ----------------------------------------------------
-//
+// Size a compressor reports when a chain sum hit its spin bound.
 constexpr uint64_t kSizeInternalError = CDMA_SIZE_INTERNAL_ERROR;
 
 // ---- tile offsets: per-workgroup chaining over published aggregates --------

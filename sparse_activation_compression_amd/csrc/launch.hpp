@@ -15,8 +15,6 @@ uint64_t zvc_compress_tiles(int esz, uint64_t n);  // compress tiles (fewer, lar
 uint64_t rle_compress_tiles(int esz, uint64_t n);  // compress tiles (fewer, larger)
 uint64_t zvci_compress_tiles(int esz, uint64_t n);
 
-// op: 0 = plain compression; 1/2/3 = ReLU of fp32/fp16/bf16 patterns coded
-// (and stored densely to act unless it is null).
 hipError_t zvc_compress_launch(int esz, int op, const void* src, uint64_t n, void* act, void* dst,
                                uint64_t* out_bytes, void* ws, hipStream_t s);
 hipError_t zvc_decompress_launch(int esz, const void* src, uint64_t src_capacity, const uint64_t* src_bytes,

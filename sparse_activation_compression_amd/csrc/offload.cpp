@@ -9,13 +9,16 @@
 // driven by the SDMA engines through hipMemcpyAsync, so the two are
 // pipelined over chunks:
 //
-//   compute stream:  [compress k] -> record comp_done[slot]
-//   worker thread:   wait comp_done[slot] -> read size_k (written by the
-//                    kernel straight into mapped pinned memory) -> check the
-//                    host capacity -> hipMemcpyAsync(size_k bytes, copy
-//                    stream) -> record copy_done[slot] -> compute stream waits
-//                    copy_done[slot] before compressing chunk k + slots into
+//   compute stream:  [compress k into slot s, size into the slot's device
+//                    size word] -> [copy the 8-byte size to pinned host
+//                    memory] -> record comp_done[s]
+//   worker thread:   wait comp_done[s] -> read size_k -> check the host
+//                    capacity -> hipMemcpyAsync(size_k bytes, copy stream)
+//                    -> record copy_done[s] -> compute stream waits
+//                    copy_done[s] before compressing chunk k + slots into
 //                    the same staging slot.
+// The size reaches the host by a copy, so nothing depends on device atomics
+// to host memory over the link.
 //
 // The copy needs the size on the host, so one host round trip per chunk is
 // unavoidable; with >= 2 slots it overlaps the previous chunk's copy.
@@ -26,12 +29,14 @@
 #include <vector>
 
 #include "cdma.h"
+#include "pinned_pool.hpp"
 
 namespace {
 
 constexpr uint64_t kAlign = 256;
 uint64_t align_up(uint64_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
+// Scratch slot = [stream staging][compress workspace][size word]
 struct SlotLayout {
   uint64_t stream_bytes, ws_bytes, slot_bytes;
 };
@@ -40,7 +45,7 @@ SlotLayout slot_layout(int algo, int esz, uint64_t chunk) {
   SlotLayout L;
   L.stream_bytes = align_up(cdma_max_compressed_bytes(algo, esz, chunk));
   L.ws_bytes = align_up(cdma_workspace_bytes(algo, esz, chunk));
-  L.slot_bytes = L.stream_bytes + L.ws_bytes;
+  L.slot_bytes = L.stream_bytes + L.ws_bytes + kAlign;
   return L;
 }
 
@@ -54,8 +59,7 @@ struct cdma_offload_s {
   uint8_t* scratch = nullptr;
   SlotLayout L{};
   hipStream_t comp = nullptr, copy = nullptr;
-  uint64_t* h_sizes = nullptr;  // pinned, mapped: compress kernels write the sizes here
-  uint64_t* d_sizes = nullptr;
+  uint64_t* h_sizes = nullptr;  // pinned (from the pool): each chunk's size, copied from its slot
   std::vector<hipEvent_t> comp_done, copy_done;
   std::vector<uint64_t> chunk_bytes;
   uint64_t total = 0, copied = 0;
@@ -65,14 +69,17 @@ struct cdma_offload_s {
 
   uint8_t* slot_stream(int s) const { return scratch + (uint64_t)s * L.slot_bytes; }
   uint8_t* slot_ws(int s) const { return slot_stream(s) + L.stream_bytes; }
+  uint64_t* slot_size(int s) const { return reinterpret_cast<uint64_t*>(slot_ws(s) + L.ws_bytes); }
 
   int enqueue_compress(uint64_t k) {
     const int s = (int)(k % (uint64_t)slots);
     const uint64_t lo = k * chunk;
     const uint64_t len = n - lo < chunk ? n - lo : chunk;
     int rc = cdma_compress(algo, esz, src + lo * (uint64_t)esz, len, slot_stream(s), L.stream_bytes,
-                           d_sizes + k, slot_ws(s), L.ws_bytes, comp);
+                           slot_size(s), slot_ws(s), L.ws_bytes, comp);
     if (rc != CDMA_OK) return rc;
+    if (hipMemcpyAsync(h_sizes + k, slot_size(s), sizeof(uint64_t), hipMemcpyDeviceToHost, comp) != hipSuccess)
+      return CDMA_ERR_HIP;
     return hipEventRecord(comp_done[s], comp) == hipSuccess ? CDMA_OK : CDMA_ERR_HIP;
   }
 
@@ -90,6 +97,10 @@ struct cdma_offload_s {
         break;
       }
       const uint64_t size = *static_cast<volatile uint64_t*>(h_sizes + k);
+      if (size == CDMA_SIZE_INTERNAL_ERROR) {  // the compressor's scan did not complete
+        rc = CDMA_ERR_INTERNAL;
+        break;
+      }
       if (size > h_cap - total) {
         rc = CDMA_ERR_CAPACITY;
         break;
@@ -128,7 +139,7 @@ struct cdma_offload_s {
     join();
     for (hipEvent_t e : comp_done) (void)hipEventDestroy(e);
     for (hipEvent_t e : copy_done) (void)hipEventDestroy(e);
-    if (h_sizes) (void)hipHostFree(h_sizes);
+    cdma::pinned_release(h_sizes);
   }
 };
 
@@ -172,9 +183,8 @@ int cdma_offload_async(int algo, int esz, const void* d_src, uint64_t n, uint64_
   h->chunk_bytes.assign(h->K, 0);
   bool ok = hipGetDevice(&h->device) == hipSuccess;
   if (ok && h->K > 0) {
-    ok = hipHostMalloc(reinterpret_cast<void**>(&h->h_sizes), h->K * sizeof(uint64_t),
-                       hipHostMallocMapped | hipHostMallocCoherent) == hipSuccess;
-    ok = ok && hipHostGetDevicePointer(reinterpret_cast<void**>(&h->d_sizes), h->h_sizes, 0) == hipSuccess;
+    h->h_sizes = static_cast<uint64_t*>(cdma::pinned_acquire(h->K * sizeof(uint64_t)));
+    ok = h->h_sizes != nullptr;
     for (int s = 0; ok && s < slots; ++s) {
       hipEvent_t a = nullptr, b = nullptr;
       ok = hipEventCreateWithFlags(&a, hipEventDisableTiming) == hipSuccess;

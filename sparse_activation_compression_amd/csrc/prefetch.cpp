@@ -26,6 +26,7 @@
 #include <vector>
 
 #include "cdma.h"
+#include "pinned_pool.hpp"
 
 namespace {
 
@@ -60,7 +61,7 @@ bool args_ok(int algo, int esz, uint64_t chunk, int slots) {
 struct cdma_prefetch_s {
   int device = 0;
   hipStream_t comp = nullptr, copy = nullptr;
-  uint64_t* h_sizes = nullptr;  // pinned copy of the chunk sizes (source of one H2D copy)
+  uint64_t* h_sizes = nullptr;  // pinned copy of the chunk sizes (source of one H2D copy), from the pool
   std::vector<hipEvent_t> copied, freed;
   hipEvent_t done = nullptr;
   int status = CDMA_OK;
@@ -85,7 +86,7 @@ struct cdma_prefetch_s {
     for (hipEvent_t e : copied) (void)hipEventDestroy(e);
     for (hipEvent_t e : freed) (void)hipEventDestroy(e);
     if (done) (void)hipEventDestroy(done);
-    if (h_sizes) (void)hipHostFree(h_sizes);
+    cdma::pinned_release(h_sizes);  // after wait(): the copy out of it has finished
   }
 };
 
@@ -141,8 +142,8 @@ int cdma_prefetch_async(int algo, int esz, const void* h_src, uint64_t h_src_byt
   uint8_t* dst = static_cast<uint8_t*>(d_dst);
 
   bool ok = hipGetDevice(&h->device) == hipSuccess;
-  ok = ok && hipHostMalloc(reinterpret_cast<void**>(&h->h_sizes), K * sizeof(uint64_t), hipHostMallocDefault) ==
-                 hipSuccess;
+  if (ok) h->h_sizes = static_cast<uint64_t*>(cdma::pinned_acquire(K * sizeof(uint64_t)));
+  ok = ok && h->h_sizes != nullptr;
   for (int s = 0; ok && s < slots; ++s) {
     hipEvent_t a = nullptr, b = nullptr;
     ok = hipEventCreateWithFlags(&a, hipEventDisableTiming) == hipSuccess;

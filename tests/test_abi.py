@@ -107,6 +107,27 @@ def test_decompress_rejects_on_host(cdma, args, status):
     assert cdma.cdma_decompress(*args) == status
 
 
+# n = 0: RLE and interleaved ZVC still write an index, so they need a
+# destination; ZVC writes nothing but the size word.  Every decoder reads the
+# stream for n = 0 too (its index, or its size check), so a NULL stream with a
+# nonzero capacity is rejected whatever n is.
+@pytest.mark.parametrize("algo", [1, 2])
+@pytest.mark.parametrize("dst", [None, P + 4])
+def test_empty_compress_needs_a_destination_when_it_writes_an_index(cdma, algo, dst):
+    assert cdma.cdma_compress(algo, 4, None, 0, dst, 10 ** 6, P, None, 0, None) == 1
+
+
+def test_empty_zvc_compress_needs_no_destination(cdma):
+    # nothing is enqueued only because the size word check fails first here
+    assert cdma.cdma_compress(0, 4, None, 0, None, 0, P + 4, None, 0, None) == 1
+
+
+@pytest.mark.parametrize("algo", [0, 1, 2])
+def test_decompress_rejects_null_stream_with_capacity_even_when_empty(cdma, algo):
+    assert cdma.cdma_decompress(algo, 4, None, 16, None, 0, None, P, None, 0, None) == 1
+    assert cdma.cdma_decompress(algo, 4, None, 16, None, 100, P, P, P, 10 ** 6, None) == 1
+
+
 def test_offload_rejects_on_host(cdma):
     sb = cdma.cdma_offload_scratch_bytes(0, 4, 4096, 2)
     assert sb > 0

@@ -135,3 +135,39 @@ def test_graph_capture_replays(algo):
         assert np.array_equal(dst[:size].cpu().numpy(), want), r
         assert int(err.item()) == 0, r
         assert torch.equal(out, xd), r
+
+
+@pytest.mark.parametrize("algo", ["zvc", "rle", "zvci"])
+def test_side_stream_with_buffers_made_by_the_binding(algo):
+    """compress/decompress with stream= and no buffers passed in: the binding
+    makes and zeroes the workspace, size and error words on that stream, so a
+    busy current stream cannot clear the error bits after the decoder set them,
+    and the round trip and the bits equal the oracle's."""
+    import torch
+    import sparse_activation_compression_amd as cdma
+    n = 300_000
+    bits = _bits(n, 0.4, seed=31)
+    xd = _to_dev(bits)
+    s = torch.cuda.Stream(device=device())
+    torch.cuda.synchronize()
+    torch.cuda._sleep(50_000_000)  # the current stream stays busy for tens of ms
+    dst, nbytes = cdma.compress(xd, algo, stream=s)
+    out, err = cdma.decompress(dst, n, 4, algo, src_bytes=nbytes, stream=s)
+    s.synchronize()
+    size = int(nbytes.item())
+    expect = ORACLE[algo](bits)
+    assert size == expect.size and np.array_equal(dst[:size].cpu().numpy(), expect)
+    assert int(err.item()) == 0 and np.array_equal(out.cpu().numpy().view(np.uint32), bits)
+    # a stream one value short: the decoder's error bits must survive
+    bad = torch.from_numpy(expect[:-4].copy()).to(device())
+    bad_size = torch.tensor([expect.size - 4], dtype=torch.int64, device=device())
+    _, want = {"zvc": oracle.zvc_decompress, "rle": oracle.rle_decompress,
+               "zvci": oracle.zvci_decompress}[algo](expect[:-4], n, 4)
+    assert want != 0
+    torch.cuda.synchronize()
+    torch.cuda._sleep(50_000_000)
+    _, err2 = cdma.decompress(bad, n, 4, algo, src_bytes=bad_size, stream=s)
+    s.synchronize()
+    got = int(err2.item())
+    torch.cuda.synchronize()
+    assert got == want, (got, want)

@@ -11,13 +11,17 @@ from gpu_util import bits_of, device, gpu_compress, gpu_decompress, random_patte
 
 pytestmark = pytest.mark.gpu
 
-TE = {4: 4096, 2: 8192}  # elements per workgroup tile
+TE = {4: 4096, 2: 8192}    # elements per decompress tile (one 256-thread workgroup, 16 KB)
+TC = {4: 15360, 2: 30720}  # elements per compress tile (15 data wavefronts x 64 lanes x 64 bytes)
 
 
 def _sizes(esz):
-    t = TE[esz]
+    t, c = TE[esz], TC[esz]
     return [1, 3, 4, 5, 8, 9, 31, 32, 33, 63, 64, 65, 255, 256, 257, 1023, 1024, 1025,
-            t - 1, t, t + 1, 2 * t + 17, 5 * t + 3, 64 * t + 100]
+            t - 1, t, t + 1, 2 * t + 17, 5 * t + 3, 64 * t + 100,
+            # compress tiles: a bounded last tile, none (exact multiples), and
+            # more tiles than a grid of one workgroup per CU takes in one round
+            c - 1, c, c + 1, 2 * c, 3 * c - 1, 3 * c + 1, 257 * c, 257 * c + 1, 513 * c - 1]
 
 
 @pytest.mark.parametrize("esz", [4, 2])
@@ -77,7 +81,8 @@ def test_specials_survive():
 
 
 def test_repeated_runs_are_identical():
-    """The lookback order changes from run to run; the stream must not."""
+    """The order in which workgroups publish their tile aggregates changes
+    from run to run; the stream must not."""
     import torch
     import sparse_activation_compression_amd as cdma
     device()
