@@ -145,6 +145,24 @@ int cdma_compress(int algo, int esz, const void *d_src, uint64_t n,
                   void *d_dst, uint64_t dst_capacity, uint64_t *d_out_bytes,
                   void *d_ws, uint64_t ws_bytes, void *stream);
 
+/*
+ * cdma_compress without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same stream, size word and errors as
+ * cdma_compress.  The workspace is a 1 MiB array that the library holds on
+ * each GPU it runs on until the process ends; that covers every n the three
+ * codecs accept (a larger need would return CDMA_ERR_CAPACITY, before
+ * anything is enqueued).  The call allocates nothing: the array's device
+ * address is looked up once per device on the first call.  Every call on one
+ * GPU shares that array, and each call clears what it needs there first, so
+ * calls that may overlap in time on one GPU (other streams, other host
+ * threads) race and must be serialised by the caller; use cdma_compress with
+ * distinct workspaces for concurrent work.
+ */
+int cdma_compress_noalloc(int algo, int esz, const void *d_src, uint64_t n,
+                          void *d_dst, uint64_t dst_capacity, uint64_t *d_out_bytes,
+                          void *stream);
+
 /* element formats of cdma_relu_compress (2- or 4-byte IEEE-style patterns) */
 #define CDMA_FMT_F32  0
 #define CDMA_FMT_F16  1

@@ -40,6 +40,7 @@ from .binding import (  # noqa: F401
     cdma_prefetch_scratch_bytes,
     cdma_prefetch_wait,
     cdma_relu_compress,
+    cdma_compress_noalloc,
     cdma_status_string,
     cdma_version,
     cdma_workspace_bytes,

@@ -62,6 +62,7 @@ def _load():
         "cdma_max_compressed_bytes": (u64, [i32, i32, u64]),
         "cdma_workspace_bytes": (u64, [i32, i32, u64]),
         "cdma_compress": (i32, [i32, i32, vp, u64, vp, u64, vp, vp, u64, vp]),
+        "cdma_compress_noalloc": (i32, [i32, i32, vp, u64, vp, u64, vp, vp]),
         "cdma_relu_compress": (i32, [i32, i32, vp, u64, vp, vp, u64, vp, vp, u64, vp]),
         "cdma_decompress": (i32, [i32, i32, vp, u64, vp, u64, vp, vp, vp, u64, vp]),
         "cdma_offload_scratch_bytes": (u64, [i32, i32, u64, i32]),
@@ -101,6 +102,10 @@ def cdma_workspace_bytes(algo: int, esz: int, n: int) -> int:
 def cdma_compress(algo, esz, d_src, n, d_dst, dst_capacity, d_out_bytes, d_ws, ws_bytes, stream) -> int:
     return int(_lib.cdma_compress(algo, esz, d_src, n, d_dst, dst_capacity, d_out_bytes, d_ws,
                                   ws_bytes, stream))
+
+
+def cdma_compress_noalloc(algo, esz, d_src, n, d_dst, dst_capacity, d_out_bytes, stream) -> int:
+    return int(_lib.cdma_compress_noalloc(algo, esz, d_src, n, d_dst, dst_capacity, d_out_bytes, stream))
 
 
 def cdma_relu_compress(algo, fmt, d_src, n, d_act, d_dst, dst_capacity, d_out_bytes, d_ws, ws_bytes,

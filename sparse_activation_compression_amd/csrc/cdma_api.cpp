@@ -65,6 +65,24 @@ int cdma_compress(int algo, int esz, const void* d_src, uint64_t n, void* d_dst,
   return e == hipSuccess ? CDMA_OK : CDMA_ERR_HIP;
 }
 
+int cdma_compress_noalloc(int algo, int esz, const void* d_src, uint64_t n, void* d_dst, uint64_t dst_capacity,
+                          uint64_t* d_out_bytes, void* stream) {
+  if (!algo_ok(algo) || !esz_ok(esz) || n > max_n(algo)) return CDMA_ERR_INVALID_ARG;
+  if (!d_out_bytes || !aligned(d_out_bytes, 8)) return CDMA_ERR_INVALID_ARG;
+  if (writes_stream(algo, n) && (!d_dst || !aligned(d_dst, 16))) return CDMA_ERR_INVALID_ARG;
+  if (dst_capacity < cdma_max_compressed_bytes(algo, esz, n)) return CDMA_ERR_CAPACITY;
+  if (n > 0 && (!d_src || !aligned(d_src, 16))) return CDMA_ERR_INVALID_ARG;
+  if (cdma::compress_workspace_bytes(algo, esz, n) > cdma::static_scratch_bytes()) return CDMA_ERR_CAPACITY;
+  void* ws = nullptr;
+  if (n > 0 && cdma::static_scratch(&ws) != hipSuccess) return CDMA_ERR_HIP;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e =
+      algo == CDMA_ALGO_ZVC   ? cdma::zvc_compress_launch(esz, 0, d_src, n, nullptr, d_dst, d_out_bytes, ws, s)
+      : algo == CDMA_ALGO_RLE ? cdma::rle_compress_launch(esz, 0, d_src, n, nullptr, d_dst, d_out_bytes, ws, s)
+                              : cdma::zvci_compress_launch(esz, d_src, n, d_dst, d_out_bytes, ws, s);
+  return e == hipSuccess ? CDMA_OK : CDMA_ERR_HIP;
+}
+
 int cdma_relu_compress(int algo, int fmt, const void* d_src, uint64_t n, void* d_act, void* d_dst,
                        uint64_t dst_capacity, uint64_t* d_out_bytes, void* d_ws, uint64_t ws_bytes, void* stream) {
   if (fmt != CDMA_FMT_F32 && fmt != CDMA_FMT_F16 && fmt != CDMA_FMT_BF16) return CDMA_ERR_INVALID_ARG;

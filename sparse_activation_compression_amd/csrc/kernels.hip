@@ -46,6 +46,40 @@ static uint32_t* ws_agg(void* ws) {
   return reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + kWsHeader);
 }
 
+// ---- the workspace of the entry point that allocates nothing ----------------
+//
+// cdma_compress_noalloc takes its workspace from this array instead of from
+// the caller: one copy per GPU, held until the process ends.  1 MiB covers
+// the 2 KB header and one 32-bit aggregate per compress tile for every n that
+// any compressor accepts (at most 2^31 / 15360 tiles).  Host code must not
+// pass the array's name to a kernel: on the host it is a stand-in, not a
+// device address; static_scratch() returns the address of the current
+// device's copy, taken once per device with hipGetSymbolAddress.
+constexpr uint64_t kStaticScratchBytes = 1ull << 20;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+uint64_t static_scratch_bytes() { return kStaticScratchBytes; }
+
+hipError_t static_scratch(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* ptr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    ptr[dev] = p;
+  }
+  *out = ptr[dev];
+  return hipSuccess;
+}
+
 uint64_t zvc_tiles(int esz, uint64_t n) {
   const uint64_t te = esz == 4 ? ZvcShape<4, kZvcV>::TE : ZvcShape<2, kZvcV>::TE;
   return (n + te - 1) / te;
@@ -276,6 +310,14 @@ hipError_t rle_decompress_launch(int esz, const void* src, uint64_t cap, const u
   }
   return esz == 4 ? rle_decompress_t<4>(src, cap, src_bytes, n, dst, error, s)
                   : rle_decompress_t<2>(src, cap, src_bytes, n, dst, error, s);
+}
+
+// Workspace bytes a compressor clears and uses: the header, then one 32-bit
+// aggregate per compress tile.
+uint64_t compress_workspace_bytes(int algo, int esz, uint64_t n) {
+  const uint64_t t = algo == 0 ? zvc_compress_tiles(esz, n) : algo == 1 ? rle_compress_tiles(esz, n)
+                                                                        : zvci_compress_tiles(esz, n);
+  return kWsHeader + 4 * t;
 }
 
 uint64_t zvci_compress_tiles(int esz, uint64_t n) {

@@ -14,7 +14,16 @@ uint64_t zvc_tiles(int esz, uint64_t n);           // decompress tiles
 uint64_t zvc_compress_tiles(int esz, uint64_t n);  // compress tiles (fewer, larger)
 uint64_t rle_compress_tiles(int esz, uint64_t n);  // compress tiles (fewer, larger)
 uint64_t zvci_compress_tiles(int esz, uint64_t n);
+// header + one 32-bit aggregate per compress tile (algo 0 ZVC, 1 RLE, 2 ZVCI)
+uint64_t compress_workspace_bytes(int algo, int esz, uint64_t n);
 
+// The per-GPU static workspace of cdma_compress_noalloc: its size, and the
+// address of the current device's copy.
+uint64_t static_scratch_bytes();
+hipError_t static_scratch(void** out);
+
+// op: 0 = plain compression; 1/2/3 = ReLU of fp32/fp16/bf16 patterns coded
+// (and stored densely to act unless it is null).
 hipError_t zvc_compress_launch(int esz, int op, const void* src, uint64_t n, void* act, void* dst,
                                uint64_t* out_bytes, void* ws, hipStream_t s);
 hipError_t zvc_decompress_launch(int esz, const void* src, uint64_t src_capacity, const uint64_t* src_bytes,
