@@ -12,10 +12,10 @@ stream, no PCIe transfer running before them):
     the longer of the two);
   * the other codecs on the same buffer: RLE, interleaved ZVC, fused ReLU + ZVC;
   * the sparsity sweep: ZVC and RLE both ways at zero fraction
-    0 / 0.25 / 0.5 / 0.75 / 0.9 / 0.99 / 1 of the 4 GiB buffer;
+    0 / 0.25 / 0.5 / 0.75 / 0.9 / 0.99 / 1 of the 4 GiB buffer, each call
+    cold (the 256 MB last-level cache emptied before it);
   * the named CNN-like workloads (single map, AlexNet conv1, the VGG-16 stack,
-    fp16 map), ZVC and RLE both ways, warm and with the 256 MB last-level
-    cache flushed before every call (cold);
+    fp16 map), ZVC and RLE both ways, warm and cold;
   * the PCIe-bound stages: compressed offload and prefetch against raw copies.
 The CPU oracle (single-threaded and on all host cores) is timed last.
 
@@ -45,7 +45,7 @@ N_ELEMS = 1 << 30
 CHUNK = 1 << 24
 SLOTS = 3
 SPIN_CYCLES = 400_000  # ~0.2 ms of device-side spin ahead of a timed call
-FLUSH_BYTES = 1 << 30  # written before a cold call: 4x the 256 MB last-level cache
+FLUSH_BYTES = 1 << 30  # read before a cold call: 4x the 256 MB last-level cache
 CPU_ST_SAMPLE = 1 << 27  # elements for the single-threaded oracle (about 2 s per round trip)
 CPU_MT_SAMPLE = 1 << 30  # elements for the oracle on all host cores (the whole buffer)
 KERNEL_SOURCES = ("sparse_activation_compression_amd/csrc/zvc_compress.hpp",
@@ -202,17 +202,21 @@ def _cpu_model() -> str:
 class Timer:
     """Times one call at a time with HIP events on the launch stream.  A short
     device-side spin is queued first so the events time GPU work, not launch
-    latency; with cold=True a 1 GiB buffer is written first so nothing of the
-    inputs is left in the last-level cache."""
+    latency; with cold=True a 1 GiB buffer is read first so nothing of the
+    inputs is left in the last-level cache.  Reading it (not writing it)
+    leaves clean lines there, so no write-back of the flush lands in the
+    timed call."""
 
     def __init__(self, torch, stream, dev):
         self.torch, self.stream, self.dev = torch, stream, dev
         self._flush = None
+        self._sink = None
 
     def flush(self):
         if self._flush is None:
-            self._flush = self.torch.empty(FLUSH_BYTES // 4, dtype=self.torch.int32, device=self.dev)
-        self._flush.fill_(1)
+            self._flush = self.torch.ones(FLUSH_BYTES // 4, dtype=self.torch.int32, device=self.dev)
+            self._sink = self.torch.zeros(1, dtype=self.torch.int64, device=self.dev)
+        self._sink.add_(self._flush.sum())
 
     def __call__(self, fn, reps: int, warmup: int = 1, cold: bool = False):
         torch = self.torch
@@ -506,7 +510,7 @@ def main() -> int:
         y = torch.empty_like(x)
         for zf in SWEEP_ZERO_FRACTIONS:
             sweep_bits_device(n, zf, seeds[zf], device=dev, out=y)
-            r = codec_rows(cdma, torch, timer, y, 4, ("zvc", "rle"), args.reps)
+            r = codec_rows(cdma, torch, timer, y, 4, ("zvc", "rle"), args.reps, cold=True)
             sweep[f"s{zf}"] = r
             checks[f"sweep_s{zf}"] = all(v.get("ok", True) for v in r.values())
         del y

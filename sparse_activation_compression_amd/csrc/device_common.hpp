@@ -46,6 +46,19 @@ __device__ __forceinline__ T ld_stream(const T* p) {
   else return *p;
 }
 
+// A load of data that is read again soon (the decoder's masks: the count
+// pass reads them, then the expand pass): without the non-temporal hint the
+// lines are kept by the memory-side cache, so the second read does not
+// reach HBM and does not interleave reads with the expand pass's writes.
+#ifndef CDMA_MASK_KEEP
+#define CDMA_MASK_KEEP 1
+#endif
+template <typename T>
+__device__ __forceinline__ T ld_keep(const T* p) {
+  if constexpr (CDMA_MASK_KEEP) return *p;
+  else return ld_stream(p);
+}
+
 template <typename T>
 __device__ __forceinline__ void st_stream(T* p, T v) {
   if constexpr (CDMA_NT_STORE) __builtin_nontemporal_store(v, p);

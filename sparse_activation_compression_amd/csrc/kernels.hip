@@ -131,18 +131,19 @@ static hipError_t zvc_compress_t(const void* src, uint64_t n, void* act, void* d
 }
 
 // Workgroups of the ZVC expand pass resident per CU.  Measured on the 4 GiB
-// fp32 sweep (percent of 8 TB/s at zero fraction 0 / 0.25 / 0.5 / 0.75 / 0.9 /
-// 0.99 / 1): 5 per CU 75.8 / 74.7 / 71.7 / 62.2 / 50.1 / 50.4 / 52.3,
-// 6 per CU 76.1 / 74.7 / 75.2 / 71.2 / 58.3 / 52.3 / 62.5,
-// 7 per CU 75.1 / 72.6 / 72.6 / 75.1 / 68.6 / 64.0 / 72.7,
-// 8 per CU (four-wave workgroups fill the CU) 75.5 / 71.7 / 71.5 / 73.3 /
-// 68.4 / 67.3 / 76.3.  Seven is the best floor across densities; the density
-// is known only on the device, after the launch is fixed.  A build option.
-// fp16 (2^30 elements, same zero fractions): 7 per CU 73.9 / 71.1 / 71.3 /
-// 69.3 / 61.8 / 57.5 / 67.0, 8 per CU 73.1 / 70.2 / 70.2 / 68.9 / 63.7 / 61.0 /
-// 70.3 (6 per CU falls to 47-52 from s = 0.9 up): eight for 16-bit elements.
+// fp32 sweep with the count pass reading the masks without the non-temporal
+// hint (percent of 8 TB/s at zero fraction 0 / 0.25 / 0.5 / 0.75 / 0.9 /
+// 0.99 / 1, the last-level cache emptied by a 1 GiB read before each call):
+// 7 per CU 77.2 / 74.5 / 75.2 / 73.8 / 65.9 / 70.2 / 76.7,
+// 8 per CU (four-wave workgroups fill the CU) 76.3 / 73.9 / 73.6 / 73.3 /
+// 66.0 / 75.0 / 76.8; with non-temporal mask reads 7 per CU gave 75.8 / 73.0
+// / 73.5 / 72.5 / 66.7 / 64.9 / 71.5.  Fewer fall off steeply from s = 0.75
+// up (5 per CU: 50 at s = 0.9 and 0.99).  Eight has the best floor across
+// densities; the density is known only on the device, after the launch is
+// fixed.  A build option.  fp16 (2^30 elements), 8 per CU: 74.3 / 72.6 /
+// 73.1 / 70.8 / 61.2 / 64.8 / 73.3.
 #ifndef CDMA_EXPAND_GROUPS
-#define CDMA_EXPAND_GROUPS 7
+#define CDMA_EXPAND_GROUPS 8
 #endif
 #ifndef CDMA_EXPAND_GROUPS16
 #define CDMA_EXPAND_GROUPS16 8
@@ -185,13 +186,14 @@ static int expand_lds_pad(const void* kernel, int groups) {
 template <int ESZ>
 static hipError_t zvc_decompress_t(const void* src, uint64_t cap, const uint64_t* src_bytes, uint64_t n,
                                    void* dst, uint32_t* error, void* ws, hipStream_t s) {
-  using C = ZvcScanShape<ESZ, kZvcV>;
+  constexpr int WPT = ZvcShape<ESZ, kZvcV>::WPT;
+  using C = ZvcScanShape<WPT>;
   const uint64_t tiles = zvc_tiles(ESZ, n);
   const uint64_t supers = (tiles + C::SUPER - 1) / C::SUPER;
   uint32_t* local = static_cast<uint32_t*>(ws);
   uint32_t* sup = local + tiles;
   hipError_t e;
-  zvc_count_kernel<ESZ, kZvcV><<<(unsigned)supers, kBlock, 0, s>>>(static_cast<const uint8_t*>(src), cap, src_bytes,
+  zvc_count_kernel<WPT><<<(unsigned)supers, kBlock, 0, s>>>(static_cast<const uint8_t*>(src), cap, src_bytes,
                                                                   n, local, sup, error, (uint32_t)tiles);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   zvc_scan_kernel<<<1, kScanBlock, 0, s>>>(sup, (uint32_t)supers);

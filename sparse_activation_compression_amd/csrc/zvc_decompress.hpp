@@ -21,28 +21,33 @@ namespace cdma {
 // Pass 2 (zvc_scan_kernel): one workgroup turns sup[] into exclusive prefixes
 // in place, with the grand total in sup[num_super].  The value offset of tile
 // t is then sup[t / SUPER] + local[t].  Neither pass waits on another
-// workgroup.
+// workgroup.  The masks are read twice, here and in the expand pass; both
+// reads leave out the non-temporal hint, so the second one is served by the
+// memory-side cache while the masks fit in it (128 MB for 2^30 elements) and
+// the expand pass's HBM traffic is then its values and its output alone.
 
-template <int ESZ, int V>
+// Super tile of decode tiles with TWPT mask words each: at most 64 tiles and
+// at most 8192 mask words (32 KB).
+template <int TWPT>
 struct ZvcScanShape {
-  using S = ZvcShape<ESZ, V>;
-  static constexpr int WORDS = 8192;                 // mask words per super tile
-  static constexpr int SUPER = WORDS / S::WPT;       // ZVC tiles per super tile
-  static_assert(SUPER <= 64 && WORDS % S::WPT == 0, "super tile shape");
+  static constexpr int WPT = TWPT;                                  // mask words per decode tile
+  static constexpr int WORDS = 64 * WPT < 8192 ? 64 * WPT : 8192;   // mask words per super tile
+  static constexpr int SUPER = WORDS / WPT;                          // decode tiles per super tile
+  static_assert(SUPER <= 64 && WORDS % WPT == 0 && WORDS % (4 * kBlock) == 0, "super tile shape");
 };
 
-template <int ESZ, int V>
+template <int TWPT>
 __global__ __launch_bounds__(kBlock) void zvc_count_kernel(
     const uint8_t* __restrict__ src, uint64_t src_capacity, const uint64_t* __restrict__ src_bytes,
     uint64_t n, uint32_t* __restrict__ local, uint32_t* __restrict__ sup, uint32_t* __restrict__ error,
     uint32_t num_tiles) {
-  using C = ZvcScanShape<ESZ, V>;
+  using C = ZvcScanShape<TWPT>;
   // Mask quad i of the super tile (16 bytes) is read by thread i % kBlock in
   // step i / kBlock, so each load instruction covers 1 KB of contiguous masks.
-  // A ZVC tile's quads are then one half-wave or one whole wave of one step.
-  constexpr int QT = C::S::WPT / 4;            // mask quads per ZVC tile
+  // A decode tile's quads are then an aligned group of QT lanes of one step.
+  constexpr int QT = C::WPT / 4;               // mask quads per decode tile
   constexpr int KQ = C::WORDS / 4 / kBlock;    // steps (quads per thread)
-  static_assert(QT == 32 || QT == 64, "a ZVC tile's masks are one half-wave or one wave of quads");
+  static_assert(QT == 8 || QT == 16 || QT == 32 || QT == 64, "a decode tile's masks are a lane group of quads");
   static_assert(KQ * kBlock * 4 == C::WORDS, "super tile shape");
   __shared__ uint32_t s_cnt[C::SUPER];
   const int tid = threadIdx.x;
@@ -57,7 +62,7 @@ __global__ __launch_bounds__(kBlock) void zvc_count_kernel(
   if (w0 + C::WORDS <= W && 4 * (w0 + C::WORDS) <= eff) {
 #pragma unroll
     for (int k = 0; k < KQ; ++k)
-      m[k] = ld_stream(reinterpret_cast<const u32x4*>(src + 4 * (w0 + 4 * (uint64_t)(k * kBlock + tid))));
+      m[k] = ld_keep(reinterpret_cast<const u32x4*>(src + 4 * (w0 + 4 * (uint64_t)(k * kBlock + tid))));
   } else {  // the last super tile: words past W count as 0, bytes past the readable size read as 0
     for (int k = 0; k < KQ; ++k) {
       const uint64_t g = w0 + 4 * (uint64_t)(k * kBlock + tid);
@@ -90,10 +95,9 @@ __global__ __launch_bounds__(kBlock) void zvc_count_kernel(
     const uint32_t inc = wave_incl_scan(cnt);
     if constexpr (QT == 64) {
       if (lane == 63) s_cnt[qi / 64] = inc;
-    } else {
-      const uint32_t lo = read_lane(inc, 31);
-      if (lane == 31) s_cnt[qi / 32] = lo;
-      if (lane == 63) s_cnt[qi / 32] = inc - lo;
+    } else {  // group total = inclusive prefix at its last lane minus that of the group before
+      const uint32_t before = __shfl(inc, (lane - QT) & 63);
+      if ((lane & (QT - 1)) == QT - 1) s_cnt[qi / QT] = inc - (lane >= QT ? before : 0u);
     }
   }
   __syncthreads();
@@ -174,7 +178,7 @@ __device__ __forceinline__ void zvc_fetch_tile(ZvcTileIn<ESZ, V>& in, const uint
     uint32_t w = 0;
     if (i < S::WPT && g < W) {
       if (4 * g + 4 <= eff) {
-        w = reinterpret_cast<const uint32_t*>(src)[g];
+        w = ld_keep(reinterpret_cast<const uint32_t*>(src) + g);
       } else {
         for (int b = 0; b < 4; ++b)
           if (4 * g + b < eff) w |= (uint32_t)src[4 * g + b] << (8 * b);
@@ -274,11 +278,11 @@ __device__ __forceinline__ uint32_t zvc_expand_tile(ZvcExpandLds<ESZ, V>& L, con
 }
 
 // Value offset of tile t (t <= num_tiles) from the two count passes.
-template <int ESZ, int V>
+template <int TWPT>
 __device__ __forceinline__ uint32_t zvc_tile_offset(const uint32_t* __restrict__ local,
                                                     const uint32_t* __restrict__ sup, uint32_t t,
                                                     uint32_t num_tiles) {
-  using C = ZvcScanShape<ESZ, V>;
+  using C = ZvcScanShape<TWPT>;
   if (t >= num_tiles) return sup[(num_tiles + C::SUPER - 1) / C::SUPER];  // the grand total
   return sup[t / C::SUPER] + local[t];
 }
@@ -304,8 +308,9 @@ __global__ __launch_bounds__(kBlock) void zvc_expand_kernel(
   const uint64_t claimed = src_bytes ? *src_bytes : src_capacity;
   const uint64_t eff = claimed < src_capacity ? claimed : src_capacity;
   ZvcTileIn<ESZ, V> in;
-  zvc_fetch_tile<ESZ, V>(in, src, eff, W, t, zvc_tile_offset<ESZ, V>(local, sup, t, num_tiles),
-                         zvc_tile_offset<ESZ, V>(local, sup, t + 1, num_tiles), tid);
+  constexpr int WPT = ZvcShape<ESZ, V>::WPT;
+  zvc_fetch_tile<ESZ, V>(in, src, eff, W, t, zvc_tile_offset<WPT>(local, sup, t, num_tiles),
+                         zvc_tile_offset<WPT>(local, sup, t + 1, num_tiles), tid);
   // E_SIZE with a size word: the masks describe another size, or the size
   // exceeds the readable capacity (bytes past the end read as 0); without
   // one: described values lie past the capacity
