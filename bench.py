@@ -98,10 +98,16 @@ def _read_csv(path):
         return list(csv.DictReader(f))
 
 
+def _newest(d: str, pattern: str) -> list:
+    """Files under d matching pattern, newest first (a rerun into the same
+    directory leaves the older run's files beside the new ones)."""
+    return sorted(glob.glob(os.path.join(d, "**", pattern), recursive=True), key=os.path.getmtime, reverse=True)
+
+
 def summarize_profile(d: str, out: str, command: str, calib_bytes: float | None) -> None:
     lines = [f"# rocprofv3 summary: {os.path.basename(out)}", "", f"Command: `{command}`", ""]
-    stats = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
-    counters = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    stats = _newest(d, "*kernel_stats.csv")
+    counters = _newest(d, "*counter_collection.csv")
     if stats:
         rows = _read_csv(stats[0])
         lines += ["| kernel | calls | average (us) | min (us) | max (us) | share |", "|---|---|---|---|---|---|"]
@@ -134,7 +140,7 @@ def summarize_traffic(fetch_dir: str, write_dir: str, out: str, command: str, ca
     the same program, each scaled by what the counter reads for the plain
     device copy of calib_bytes that the program ran (--calibrate-copy)."""
     def load(d, counter):
-        f = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)[0]
+        f = _newest(d, "*counter_collection.csv")[0]
         by_id = {}
         for r in _read_csv(f):
             if r.get("Counter_Name") == counter:
@@ -171,7 +177,7 @@ def summarize_traffic(fetch_dir: str, write_dir: str, out: str, command: str, ca
         return tot
 
     comp = total("zvc_compress_kernel<4, 0>")
-    dec = total("zvc_count_kernel<4, 4>", "zvc_scan_kernel", "zvc_expand_kernel<4, 4>")
+    dec = total("zvc_count_kernel", "zvc_scan_kernel", "zvc_expand_kernel<4, 4>")
     lines += ["", "Machine-readable (read by bench.py; valid only for the kernel sources hashed here):", ""]
     if comp is not None:
         lines.append(f"- hbm_bytes_per_launch_zvc_compress: `{comp:.0f}`")
@@ -395,7 +401,7 @@ def main() -> int:
         return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the path shards by independent chunks; see DESIGN.md)", file=sys.stderr)
+              "(the path shards by independent chunks, with no communication)", file=sys.stderr)
         return 2
 
     import numpy as np
