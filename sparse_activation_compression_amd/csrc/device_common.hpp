@@ -253,9 +253,15 @@ constexpr uint32_t kTicketClassStride = 32;   // words (128 bytes) from one clas
 struct Tickets {
   uint32_t* ctr;
   uint32_t cls, ncls;
-  __device__ __forceinline__ uint32_t draw() const {
-    return cls + ncls * __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // The counter value of a draw and the tile it stands for.  A caller that
+  // draws ahead keeps the raw value and converts it where it uses the tile:
+  // arithmetic on the atomic's result right after the draw would make the
+  // wave wait for the atomic there.
+  __device__ __forceinline__ uint32_t raw() const {
+    return __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+  __device__ __forceinline__ uint32_t tile(uint32_t r) const { return cls + ncls * r; }
+  __device__ __forceinline__ uint32_t draw() const { return tile(raw()); }
 };
 
 __device__ __forceinline__ Tickets ticket_source(uint32_t* counter, uint32_t mode) {

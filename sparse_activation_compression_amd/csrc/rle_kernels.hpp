@@ -306,9 +306,9 @@ __device__ __forceinline__ uint32_t rle_c_iteration(RleCLds<ESZ>& L, u32x4 (&cur
     // before the hand-over; waiting here on every path keeps the compiler from
     // waiting again after the ticket drawn next
     __builtin_amdgcn_s_waitcnt(0);
-    if (lane == 0) L.next = pend;
+    if (lane == 0) L.next = tk.tile(pend);
     // the next ticket goes out now and has a whole iteration to come back
-    if (lane == 0 && have_cur) pend = tk.draw();
+    if (lane == 0 && have_cur) pend = tk.raw();
     if (have_cur) {
       const uint32_t pl = lane < S::NW ? L.pw[lane] : 0u;
       const uint32_t vl = lane < S::NW ? L.vw[lane] : 0u;
@@ -375,15 +375,16 @@ __global__ __launch_bounds__(RleCShape<ESZ>::BLOCK) void rle_compress_kernel(
   if (tid == 0) L.mode = start_mode(counter);
   __syncthreads();
   const Tickets tk = ticket_source(counter, __builtin_amdgcn_readfirstlane(L.mode));
-  if (tid < 3 * 64 && lane == 0) L.init[wave] = tk.draw();
+  if (tid < 3 * 64 && lane == 0) L.init[wave] = tk.raw();
   __syncthreads();
   const uint32_t a = __builtin_amdgcn_readfirstlane(L.init[0]);
   const uint32_t b = __builtin_amdgcn_readfirstlane(L.init[1]);
   const uint32_t c = __builtin_amdgcn_readfirstlane(L.init[2]);
+  // raw counter values: a class's tiles increase with them
   const uint32_t lo = min(a, min(b, c)), hi = max(a, max(b, c));
-  uint32_t t = lo;
-  uint32_t tn = a + b + c - lo - hi;
-  uint32_t pend = hi;     // control wave: ticket to hand over next
+  uint32_t t = tk.tile(lo);
+  uint32_t tn = tk.tile(a + b + c - lo - hi);
+  uint32_t pend = hi;     // control wave: raw value of the ticket to hand over next
   uint32_t tp = num_tiles;
   u32x4 ra[S::V], rb[S::V];
   ChainRound cr;          // control wave: chain sum in flight
