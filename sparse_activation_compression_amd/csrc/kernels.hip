@@ -25,6 +25,23 @@ __global__ void store_u64_kernel(uint64_t* p, uint64_t v) {
   if (threadIdx.x == 0 && blockIdx.x == 0) *p = v;
 }
 
+// Warm the memory-side cache with the stream (see warm_quads) when its
+// readable size is at most `limit`; otherwise return at once.
+constexpr unsigned kWarmGroups = 1024;
+__global__ __launch_bounds__(256) void warm_stream_kernel(const uint8_t* __restrict__ src, uint64_t cap,
+                                                          const uint64_t* __restrict__ src_bytes, uint64_t limit) {
+  const uint64_t claimed = src_bytes ? *src_bytes : cap;
+  const uint64_t eff = claimed < cap ? claimed : cap;
+  if (eff > limit) return;
+  warm_quads(src, 0, eff / 16, (uint64_t)blockIdx.x * 256 + threadIdx.x, (uint64_t)gridDim.x * 256);
+}
+
+static hipError_t warm_stream(const void* src, uint64_t cap, const uint64_t* src_bytes, hipStream_t s) {
+  if (CDMA_WARM_BYTES == 0 || cap == 0) return hipSuccess;
+  warm_stream_kernel<<<kWarmGroups, 256, 0, s>>>(static_cast<const uint8_t*>(src), cap, src_bytes, CDMA_WARM_BYTES);
+  return hipGetLastError();
+}
+
 // Clear the workspace header (ticket counter, start-mode words) and the
 // per-tile aggregate words with a kernel (not a memset node), so the sequence
 // stays correct if a caller captures it.
@@ -194,7 +211,7 @@ static hipError_t zvc_decompress_t(const void* src, uint64_t cap, const uint64_t
   uint32_t* sup = local + tiles;
   hipError_t e;
   zvc_count_kernel<WPT><<<(unsigned)supers, kBlock, 0, s>>>(static_cast<const uint8_t*>(src), cap, src_bytes,
-                                                                  n, local, sup, error, (uint32_t)tiles);
+                                                                  n, local, sup, error, (uint32_t)tiles, CDMA_WARM_BYTES);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   zvc_scan_kernel<<<1, kScanBlock, 0, s>>>(sup, (uint32_t)supers);
   if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -274,6 +291,8 @@ static hipError_t rle_decompress_t(const void* src, uint64_t cap, const uint64_t
                                    void* dst, uint32_t* error, hipStream_t s) {
   const uint64_t wins = (n + RleShape<ESZ>::E - 1) / RleShape<ESZ>::E;
   const uint64_t groups = (wins + kRleDecWaves - 1) / kRleDecWaves;
+  const hipError_t e = warm_stream(src, cap, src_bytes, s);
+  if (e != hipSuccess) return e;
   rle_decompress_kernel<ESZ><<<(unsigned)groups, kRleDecBlock, 0, s>>>(
       static_cast<const uint8_t*>(src), cap, src_bytes, n, static_cast<uint8_t*>(dst), error, (uint32_t)groups);
   return hipGetLastError();
@@ -381,6 +400,8 @@ hipError_t zvci_decompress_launch(int esz, const void* src, uint64_t cap, const 
   const uint64_t E = 4096 / (uint64_t)esz;
   const uint64_t blocks = (n + E - 1) / E;
   const unsigned grid = (unsigned)((blocks + kWaves - 1) / kWaves);
+  const hipError_t e = warm_stream(src, cap, src_bytes, s);
+  if (e != hipSuccess) return e;
   if (esz == 4)
     zvci_decompress_kernel<4><<<grid, kBlock, 0, s>>>(static_cast<const uint8_t*>(src), cap, src_bytes, n,
                                                      static_cast<uint8_t*>(dst), error, grid);

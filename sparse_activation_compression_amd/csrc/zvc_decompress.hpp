@@ -25,6 +25,8 @@ namespace cdma {
 // reads leave out the non-temporal hint, so the second one is served by the
 // memory-side cache while the masks fit in it (128 MB for 2^30 elements) and
 // the expand pass's HBM traffic is then its values and its output alone.
+// When the whole stream fits (CDMA_WARM_BYTES), pass 1 reads the values too,
+// and the expand pass's HBM traffic is its output alone.
 
 // Super tile of decode tiles with TWPT mask words each: at most 64 tiles and
 // at most 8192 mask words (32 KB).
@@ -40,7 +42,7 @@ template <int TWPT>
 __global__ __launch_bounds__(kBlock) void zvc_count_kernel(
     const uint8_t* __restrict__ src, uint64_t src_capacity, const uint64_t* __restrict__ src_bytes,
     uint64_t n, uint32_t* __restrict__ local, uint32_t* __restrict__ sup, uint32_t* __restrict__ error,
-    uint32_t num_tiles) {
+    uint32_t num_tiles, uint64_t warm_limit) {
   using C = ZvcScanShape<TWPT>;
   // Mask quad i of the super tile (16 bytes) is read by thread i % kBlock in
   // step i / kBlock, so each load instruction covers 1 KB of contiguous masks.
@@ -109,6 +111,15 @@ __global__ __launch_bounds__(kBlock) void zvc_count_kernel(
     if (lane == 63) sup[u] = inc;
   }
   if (err && error) atomicOr(error, err);
+  // a stream that fits in the memory-side cache: every workgroup also reads
+  // its share of the values (the masks it read are kept already), so the
+  // expand pass reads the whole stream from the cache
+  if (eff <= warm_limit && eff > 4 * W) {
+    const uint64_t q0 = 4 * W / 16, q1 = eff / 16;
+    const uint64_t per = (q1 - q0 + gridDim.x - 1) / gridDim.x;
+    const uint64_t a = q0 + (uint64_t)u * per, b = a + per < q1 ? a + per : q1;
+    if (a < b) warm_quads(src, a, b, (uint64_t)tid, kBlock);
+  }
 }
 
 // Exclusive prefix sums of sup[0..count) in place, total in sup[count]; one
