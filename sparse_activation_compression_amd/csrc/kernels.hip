@@ -25,6 +25,16 @@ __global__ void store_u64_kernel(uint64_t* p, uint64_t v) {
   if (threadIdx.x == 0 && blockIdx.x == 0) *p = v;
 }
 
+// Read-ahead chunks of the ZVC expand pass: output bytes per chunk (0: no
+// read-ahead workgroups) and read-ahead workgroups per chunk.
+#ifndef CDMA_AHEAD_CHUNK_BYTES
+#define CDMA_AHEAD_CHUNK_BYTES (1ull << 30)
+#endif
+#ifndef CDMA_AHEAD_GROUPS
+#define CDMA_AHEAD_GROUPS 2048
+#endif
+constexpr uint32_t kAheadGroups = CDMA_AHEAD_GROUPS;
+
 // Warm the memory-side cache with the stream (see warm_quads) when its
 // readable size is at most `limit`; otherwise return at once.
 constexpr unsigned kWarmGroups = 1024;
@@ -109,7 +119,7 @@ uint64_t zvc_compress_tiles(int esz, uint64_t n) {
 
 // Workgroups of `kernel` that fit on the current device at once (all CUs),
 // cached per (kernel, device).
-static uint64_t resident_groups(const void* kernel, int block = kBlock) {
+static uint64_t resident_groups(const void* kernel, int block = kBlock, int dyn_lds = 0) {
   struct Entry {
     const void* k;
     int dev;
@@ -125,7 +135,7 @@ static uint64_t resident_groups(const void* kernel, int block = kBlock) {
     if (cache[i].k == kernel && cache[i].dev == dev) return cache[i].groups;
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 1;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, 0) != hipSuccess || per_cu <= 0)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, dyn_lds) != hipSuccess || per_cu <= 0)
     per_cu = 1;
   const uint64_t groups = (uint64_t)cus * (uint64_t)per_cu;
   if (used < 64) cache[used++] = Entry{kernel, dev, groups};
@@ -210,15 +220,29 @@ static hipError_t zvc_decompress_t(const void* src, uint64_t cap, const uint64_t
   uint32_t* local = static_cast<uint32_t*>(ws);
   uint32_t* sup = local + tiles;
   hipError_t e;
+  // read-ahead chunks (see zvc_expand_kernel): chunk_tiles tiles each
+  constexpr uint64_t tile_bytes = (uint64_t)ZvcShape<ESZ, kZvcV>::TE * ESZ;
+  const uint64_t chunk = CDMA_AHEAD_CHUNK_BYTES / tile_bytes;
+  const uint64_t nchunks = chunk ? (tiles + chunk - 1) / chunk : 1;  // with read-ahead
+  // a chunk is read ahead only when the stream can exceed what the count pass
+  // leaves in the cache and still be a small share of the output
+  const bool may_ahead = (uint64_t)ESZ * n / 100 * CDMA_AHEAD_MAX_PCT > (uint64_t)CDMA_WARM_BYTES;
+  const uint32_t warm = chunk && may_ahead ? kAheadGroups : 0u;
+  // read-ahead counters and flags, 128-byte aligned after sup[]
+  uint32_t* sync = reinterpret_cast<uint32_t*>((reinterpret_cast<uintptr_t>(sup + supers + 1) + 127) & ~uintptr_t(127));
   zvc_count_kernel<WPT><<<(unsigned)supers, kBlock, 0, s>>>(static_cast<const uint8_t*>(src), cap, src_bytes,
                                                                   n, local, sup, error, (uint32_t)tiles, CDMA_WARM_BYTES);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  zvc_scan_kernel<<<1, kScanBlock, 0, s>>>(sup, (uint32_t)supers);
+  zvc_scan_kernel<<<1, kScanBlock, 0, s>>>(sup, (uint32_t)supers, sync, warm ? (uint32_t)nchunks * kAheadSyncWords : 0u);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   auto kern = zvc_expand_kernel<ESZ, kZvcV>;
   const int pad = expand_lds_pad(reinterpret_cast<const void*>(kern), kExpandGroupsPerCU<ESZ>);
-  kern<<<(unsigned)tiles, kBlock, pad, s>>>(static_cast<const uint8_t*>(src), cap, src_bytes, n,
-                                            static_cast<uint8_t*>(dst), error, local, sup, (uint32_t)tiles);
+  const uint64_t window = resident_groups(reinterpret_cast<const void*>(kern), kBlock, pad);
+  const uint64_t grid = tiles + (uint64_t)warm * nchunks;
+  kern<<<(unsigned)grid, kBlock, pad, s>>>(static_cast<const uint8_t*>(src), cap, src_bytes, n,
+                                           static_cast<uint8_t*>(dst), error, local, sup, (uint32_t)tiles,
+                                           warm ? (uint32_t)chunk : (uint32_t)tiles, warm, (uint32_t)window, sync,
+                                           CDMA_WARM_BYTES);
   return hipGetLastError();
 }
 

@@ -26,7 +26,9 @@ namespace cdma {
 // memory-side cache while the masks fit in it (128 MB for 2^30 elements) and
 // the expand pass's HBM traffic is then its values and its output alone.
 // When the whole stream fits (CDMA_WARM_BYTES), pass 1 reads the values too,
-// and the expand pass's HBM traffic is its output alone.
+// and the expand pass's HBM traffic is its output alone; a larger stream that
+// is a small share of the output is read ahead chunk by chunk inside the
+// expand pass (zvc_expand_kernel).
 
 // Super tile of decode tiles with TWPT mask words each: at most 64 tiles and
 // at most 8192 mask words (32 KB).
@@ -126,13 +128,16 @@ __global__ __launch_bounds__(kBlock) void zvc_count_kernel(
 // workgroup of kScanBlock threads.
 constexpr int kScanBlock = 1024;
 
-__global__ __launch_bounds__(kScanBlock) void zvc_scan_kernel(uint32_t* __restrict__ sup, uint32_t count) {
+// It also clears the expand pass's nsync read-ahead counters.
+__global__ __launch_bounds__(kScanBlock) void zvc_scan_kernel(uint32_t* __restrict__ sup, uint32_t count,
+                                                             uint32_t* __restrict__ sync, uint32_t nsync) {
   __shared__ uint32_t s_wave[kScanBlock / 64];
   __shared__ uint32_t s_carry;
   const int tid = threadIdx.x;
   const int lane = (int)lane_id();
   const int wave = tid >> 6;
   if (tid == 0) s_carry = 0;
+  for (uint32_t i = tid; i < nsync; i += kScanBlock) sync[i] = 0;
   __syncthreads();
   for (uint32_t base = 0; base < count; base += kScanBlock) {
     const uint32_t i = base + tid;
@@ -164,7 +169,11 @@ __global__ __launch_bounds__(kScanBlock) void zvc_scan_kernel(uint32_t* __restri
 template <int ESZ, int V>
 struct ZvcExpandShape {
   using S = ZvcShape<ESZ, V>;
-  static constexpr int QPT = (S::TE * ESZ / 16 + 2 + kBlock - 1) / kBlock;  // value quads per thread
+  // A tile's values span at most TE * ESZ bytes, i.e. TE * ESZ / 16 quads
+  // plus one when the span starts mid-quad: QPT per thread, and the one
+  // extra quad (its address is uniform) by a scalar load.
+  static constexpr int QPT = S::TE * ESZ / 16 / kBlock;  // value quads per thread
+  static_assert(QPT * kBlock * 16 == S::TE * ESZ && S::STAGE >= S::TE * ESZ + 16, "expand staging shape");
   static constexpr int MPT = (S::WPT + kBlock - 1) / kBlock;                // mask words per thread
 };
 
@@ -172,6 +181,7 @@ template <int ESZ, int V>
 struct ZvcTileIn {
   using X = ZvcExpandShape<ESZ, V>;
   u32x4 q[X::QPT];
+  u32x4 qx;  // the quad after the QPT * kBlock ones (uniform)
   uint32_t m[X::MPT];
   uint64_t beg, end;  // value span in the stream
   bool short_read;
@@ -218,6 +228,22 @@ __device__ __forceinline__ void zvc_fetch_tile(ZvcTileIn<ESZ, V>& in, const uint
     }
     in.q[k] = d;
   }
+  {
+    const uint64_t q = q0 + (uint64_t)X::QPT * kBlock;
+    u32x4 d = {0u, 0u, 0u, 0u};
+    if (q < q1) {
+      const uint64_t qb = q << 4;
+      if (qb + 16 <= eff) {
+        d = *reinterpret_cast<const u32x4*>(src + qb);
+      } else {
+        for (int b = 0; b < 16; b += ESZ) {
+          if (qb + b + ESZ <= eff) vec_set<ESZ>(d, b / ESZ, load_elem<ESZ>(src + qb + b));
+          else if (qb + b >= in.beg && qb + b < in.end) in.short_read = true;
+        }
+      }
+    }
+    in.qx = d;
+  }
 }
 
 template <int ESZ, int V>
@@ -249,8 +275,10 @@ __device__ __forceinline__ uint32_t zvc_expand_tile(ZvcExpandLds<ESZ, V>& L, con
 #pragma unroll
   for (int k = 0; k < X::QPT; ++k) {
     const uint64_t q = q0 + tid + (uint64_t)k * kBlock;
-    if (q < q1 && 16 * (q - q0) + 16 <= (uint64_t)S::STAGE) *reinterpret_cast<u32x4*>(L.stage + 16 * (q - q0)) = in.q[k];
+    if (q < q1) *reinterpret_cast<u32x4*>(L.stage + 16 * (q - q0)) = in.q[k];
   }
+  if (tid == 0 && q0 + (uint64_t)X::QPT * kBlock < q1)
+    *reinterpret_cast<u32x4*>(L.stage + 16 * X::QPT * kBlock) = in.qx;
   __syncthreads();
   uint32_t bits[V], ex[V];
 #pragma unroll
@@ -298,28 +326,118 @@ __device__ __forceinline__ uint32_t zvc_tile_offset(const uint32_t* __restrict__
   return sup[t / C::SUPER] + local[t];
 }
 
-// Pass 3: one tile per workgroup, grid = tiles, no inter-workgroup dependency.
-// Workgroups are dispatched in tile order, so the tiles in flight stay one
-// narrow window of the output and of the stream.  How many are in flight per
+// Pass 3: one tile per workgroup, no inter-workgroup dependency for
+// correctness.  Workgroups are dispatched in block order, and each XCD takes
+// one contiguous range of tiles (xcd_tile), so the tiles in flight stay a few
+// narrow windows of the output and of the stream.  How many are in flight per
 // CU is set by the launcher (see expand_lds_pad): more workgroups hide the
 // latency of the mask and value reads when a tile has few values, fewer keep
 // the mixed read/write traffic efficient when it has many.
+//
+// Read-ahead chunks.  When the stream is large but a small share of the
+// output (high sparsity), its reads, scattered through the output's write
+// stream, slow HBM far more than their bytes (s = 0.9, fp32: 66 % of peak
+// against 75 % at s = 0.5).  The grid is then cut into chunks of chunk_tiles
+// tiles, each preceded by warm_groups read-ahead workgroups that read the
+// chunk's masks and values once with caching loads (a short pure-read burst
+// that leaves them in the memory-side cache).  They count themselves done on
+// two levels (sixteen sub-counters, then one top counter, so no word takes
+// more than a few dozen atomics), and the last one raises kAheadFlags copies
+// of a done flag, each on a cache line of its own.  The chunk's first expand
+// workgroups (those that can be resident before the read-ahead ends: block
+// index within the chunk below wait_window) poll one copy each, sleeping
+// between polls, with a bounded spin; a thousand waiters polling one word
+// slow the memory channel that holds it enough to stall the read-ahead
+// itself.  The expand pass then reads from the cache, and its HBM traffic is
+// its writes.  Whether a chunk is read ahead is decided on the device,
+// identically by every workgroup, from the offsets: not when the whole
+// stream fits in the cache (the count pass read it), when the stream is over
+// CDMA_AHEAD_MAX_PCT percent of the output, or when the chunk's share
+// exceeds CDMA_WARM_BYTES.  The waits only order memory traffic; the result
+// does not depend on them.
+#ifndef CDMA_AHEAD_MAX_PCT
+#define CDMA_AHEAD_MAX_PCT 20
+#endif
+#ifndef CDMA_AHEAD_SPIN
+#define CDMA_AHEAD_SPIN 1000
+#endif
+#ifndef CDMA_AHEAD_SLEEP
+#define CDMA_AHEAD_SLEEP 32
+#endif
+// Per chunk in sync[], one 128-byte line each: the top counter, kAheadSubs
+// sub-counters of finished read-ahead workgroups, and kAheadFlags copies of
+// the done flag.
+constexpr uint32_t kAheadSubs = 16;
+constexpr uint32_t kAheadFlags = 15;
+constexpr uint32_t kAheadSyncWords = 32 * (1 + kAheadSubs + kAheadFlags);
+
 template <int ESZ, int V>
 __global__ __launch_bounds__(kBlock) void zvc_expand_kernel(
     const uint8_t* __restrict__ src, uint64_t src_capacity, const uint64_t* __restrict__ src_bytes,
     uint64_t n, uint8_t* __restrict__ dst, uint32_t* __restrict__ error,
-    const uint32_t* __restrict__ local, const uint32_t* __restrict__ sup, uint32_t num_tiles) {
+    const uint32_t* __restrict__ local, const uint32_t* __restrict__ sup, uint32_t num_tiles,
+    uint32_t chunk_tiles, uint32_t warm_groups, uint32_t wait_window, uint32_t* __restrict__ sync,
+    uint64_t fits_limit) {
   __shared__ ZvcExpandLds<ESZ, V> L;
+  constexpr int WPT = ZvcShape<ESZ, V>::WPT;
   const int tid = threadIdx.x;
   const int lane = (int)lane_id();
   const int wave = tid >> 6;
-  const uint32_t t = xcd_tile(blockIdx.x, gridDim.x);  // this workgroup's tile
-  if (t >= num_tiles) return;
+  const uint32_t per = warm_groups + chunk_tiles;  // blocks per chunk
+  const uint32_t c = blockIdx.x / per, r = blockIdx.x % per;
+  const uint32_t t0 = c * chunk_tiles;
+  const uint32_t t1 = num_tiles - t0 < chunk_tiles ? num_tiles : t0 + chunk_tiles;
   const uint64_t W = (n + 31) / 32;
   const uint64_t claimed = src_bytes ? *src_bytes : src_capacity;
   const uint64_t eff = claimed < src_capacity ? claimed : src_capacity;
+  if (warm_groups && (r < warm_groups || r - warm_groups < wait_window)) {
+    uint64_t m0 = 4ull * WPT * t0, m1 = 4ull * WPT * t1;
+    if (m1 > 4 * W) m1 = 4 * W;
+    uint64_t v0 = 4 * W + (uint64_t)ESZ * zvc_tile_offset<WPT>(local, sup, t0, num_tiles);
+    uint64_t v1 = 4 * W + (uint64_t)ESZ * zvc_tile_offset<WPT>(local, sup, t1, num_tiles);
+    const uint64_t stream = 4 * W + (uint64_t)ESZ * zvc_tile_offset<WPT>(local, sup, num_tiles, num_tiles);
+    if (m1 > eff) m1 = eff;
+    if (v1 > eff) v1 = eff;
+    if (m0 > m1) m0 = m1;
+    if (v0 > v1) v0 = v1;
+    const bool ahead = stream > fits_limit && stream * 100 <= (uint64_t)ESZ * n * CDMA_AHEAD_MAX_PCT &&
+                       (m1 - m0) + (v1 - v0) <= (uint64_t)CDMA_WARM_BYTES;
+    if (r < warm_groups) {  // a read-ahead workgroup: its strided share of the chunk
+      if (!ahead) return;
+      const uint64_t start = (uint64_t)r * kBlock + tid, stride = (uint64_t)warm_groups * kBlock;
+      warm_quads(src, m0 / 16, m1 / 16, start, stride);
+      warm_quads(src, v0 / 16, v1 / 16, start, stride);
+      __syncthreads();
+      if (tid == 0) {
+        // two-level count, so that no counter takes more than a few dozen
+        // atomics: the last arrival at each sub-counter counts at the top,
+        // and the last arrival at the top raises the flag copies
+        uint32_t* cs = sync + (uint64_t)c * kAheadSyncWords;
+        const uint32_t j = r % kAheadSubs;
+        const uint32_t subs = warm_groups < kAheadSubs ? warm_groups : kAheadSubs;
+        const uint32_t expect = warm_groups / kAheadSubs + (j < warm_groups % kAheadSubs ? 1u : 0u);
+        if (__hip_atomic_fetch_add(cs + 32 * (1 + j), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                expect - 1 &&
+            __hip_atomic_fetch_add(cs, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == subs - 1)
+          for (uint32_t k = 0; k < kAheadFlags; ++k)
+            __hip_atomic_store(cs + 32 * (1 + kAheadSubs + k), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      return;
+    }
+    if (ahead) {
+      // waiters spread their polls over the flag copies (one cache line each)
+      if (tid == 0) {
+        const uint32_t* flag = sync + (uint64_t)c * kAheadSyncWords + 32 * (1 + kAheadSubs + blockIdx.x % kAheadFlags);
+        for (uint32_t k = 0; k < CDMA_AHEAD_SPIN; ++k) {
+          if (__hip_atomic_load(const_cast<uint32_t*>(flag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) break;
+          __builtin_amdgcn_s_sleep(CDMA_AHEAD_SLEEP);
+        }
+      }
+      __syncthreads();
+    }
+  }
+  const uint32_t t = t0 + xcd_tile(r - warm_groups, t1 - t0);  // this workgroup's tile
   ZvcTileIn<ESZ, V> in;
-  constexpr int WPT = ZvcShape<ESZ, V>::WPT;
   zvc_fetch_tile<ESZ, V>(in, src, eff, W, t, zvc_tile_offset<WPT>(local, sup, t, num_tiles),
                          zvc_tile_offset<WPT>(local, sup, t + 1, num_tiles), tid);
   // E_SIZE with a size word: the masks describe another size, or the size

@@ -161,3 +161,40 @@ def test_size_word_beyond_capacity(algo):
     _, err = cdma.decompress(torch.from_numpy(s.copy()).to(dev), x.size, 4, algo, src_bytes=size)
     torch.cuda.synchronize()
     assert int(err.item()) == 0
+
+
+READ_AHEAD = [(4, (1 << 30) + 4097, 0.9, 54), (4, (1 << 30) + 4097, 0.99, 55), (2, (1 << 30) + 8191, 0.95, 57)]
+
+
+@pytest.mark.parametrize("esz,n,s,seed", READ_AHEAD, ids=[f"esz{e}_s{s}" for e, _, s, _ in READ_AHEAD])
+def test_read_ahead_chunks_round_trip(esz, n, s, seed):
+    """Outputs over 1 GiB whose stream exceeds what the count pass leaves in
+    the memory-side cache but is a small share of the output: the expand
+    pass reads each 1 GiB chunk ahead (a ragged last chunk of one or two
+    tiles here).  The round trip is bit-exact with and without a size word,
+    the size matches the closed form, and a size word one value short is
+    reported as CDMA_E_SIZE."""
+    import torch
+    import sparse_activation_compression_amd as cdma
+    from synth import sweep_bits_device
+    dev = device()
+    print(f"read-ahead esz={esz} n={n} s={s}", flush=True)
+    x = sweep_bits_device(n, s, seed, device=dev)
+    if esz == 2:
+        x = (x >> 16).to(torch.int16)
+    nnz = int(torch.count_nonzero(x).item())
+    assert 0 < nnz < n // 5
+    dst, nb = cdma.compress(x, "zvc")
+    size = int(nb.item())
+    assert size == 4 * ((n + 31) // 32) + esz * nnz
+    out, err = cdma.decompress(dst, n, esz, "zvc", src_bytes=nb)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0 and torch.equal(out, x)
+    out.fill_(0)
+    out2, err2 = cdma.decompress(dst[:size], n, esz, "zvc", out=out)
+    torch.cuda.synchronize()
+    assert int(err2.item()) == 0 and torch.equal(out2, x)
+    short = torch.tensor([size - esz], dtype=torch.int64, device=dev)
+    _, err3 = cdma.decompress(dst, n, esz, "zvc", src_bytes=short, out=out)
+    torch.cuda.synchronize()
+    assert int(err3.item()) & cdma.CDMA_E_SIZE
