@@ -107,30 +107,44 @@ struct RleCShape {
 template <int ESZ>
 struct RleCLds {
   using S = RleCShape<ESZ>;
-  uint64_t excl;                        // packed exclusive prefix of the tile being stored
-  uint64_t agg[2];                      // packed aggregate of the tile in stage[b]
-  uint32_t pw[S::NW], vw[S::NW];        // per-window entries and nonzeros (read between B1 and B2)
-  uint32_t ipw[2][S::NW], ivw[2][S::NW];  // their exclusive in-tile prefixes, for the tile in stage[b]
+  uint64_t excl;                        // packed exclusive prefix of the tile stored this iteration
+  uint64_t agg2;                        // and its packed aggregate
+  uint64_t agg[2];                      // packed aggregate of the tile classified in an iteration of parity b
+  uint32_t pw[S::NW], vw[S::NW];        // per-window entries and nonzeros of the tile being classified
   uint32_t next;                        // ticket handed from the control wave to the data waves
   uint32_t mode;                        // start_mode's choice (selects the ticket source)
   uint32_t init[3];                     // the first three tickets
-  uint32_t mask[S::NW * S::WPW];
-  uint32_t pre[S::NW * S::WPW];         // nonzeros of the window before each mask word
+  uint32_t mask[2][S::NW * S::WPW];     // window masks of the tiles classified in iterations of parity b
+  uint32_t pre[2][S::NW * S::WPW];      // nonzeros of the window before each mask word
   __attribute__((aligned(16))) uint8_t stage[2][S::STAGE];
 };
 
+// What a data lane keeps of its window from the classify to the compaction
+// one iteration later.  Lw, r_w, p_w, Pb and Vb are the same on every lane.
+struct RleLane {
+  uint32_t T;      // run-boundary bits of this lane's window positions
+  uint32_t texcl;  // boundaries before this lane in the window
+  uint32_t Lw;     // window length (0: no window)
+  uint32_t r_w;    // runs in the window
+  uint32_t p_w;    // run entries (runs plus the 32-bit pad)
+  uint32_t Pb, Vb; // entries / nonzeros of the tile's windows before this one
+};
+
+// Load tile t's windows, one per data wave.  As in the ZVC compressor, a
+// buffer resource covers exactly the tile when it is full and valid, and
+// nothing otherwise, so the loads are issued on every path (an invalid
+// tile's, the control wave's and the partial tile's return zeros without
+// touching memory) and the compiler counts exactly which are in flight.
 template <int ESZ>
 __device__ __forceinline__ void rle_c_load_full(u32x4 (&v)[RleCShape<ESZ>::V], const uint8_t* __restrict__ src,
-                                                uint32_t t, int wave, int lane) {
+                                                uint32_t t, bool valid, int wave, int lane) {
   using S = RleCShape<ESZ>;
-  // uniform 64-bit tile base (SGPRs) plus a 32-bit per-lane offset; the empty
-  // asm keeps the compiler from hoisting base + offset into a 64-bit VGPR
-  // pair that would outlive the loop and spill
-  const uint8_t* p = src + (uint64_t)t * (S::NW * 4096);
-  uint32_t o = (uint32_t)(wave * 4096 + lane * 16);
-  asm volatile("" : "+v"(o));
+  const uint8_t* p = src + (uint64_t)t * (S::NW * 4096);  // uniform tile base
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p), (short)0, valid ? S::NW * 4096 : 0, kBufferFlags);
+  const uint32_t o = (uint32_t)(wave * 4096 + lane * 16);
 #pragma unroll
-  for (int j = 0; j < S::V; ++j) v[j] = ld_stream(reinterpret_cast<const u32x4*>(p + o + j * 1024));
+  for (int j = 0; j < S::V; ++j) v[j] = __builtin_amdgcn_raw_buffer_load_b128(r, o + j * 1024, 0, kLoadAux);
 }
 
 // Apply the epilogue OP to a window's vectors in place and, if act is given,
@@ -161,201 +175,237 @@ struct RleAggDec {
   __device__ uint64_t operator()(uint32_t v) const { return ((uint64_t)(v >> 15) << 31) | (v & 0x7FFFu); }
 };
 
-// One pipeline iteration (the structure of the ZVC compressor's).  Returns
-// the ticket the data waves prefetch in the next iteration.
+// Classify tile t's window of this data wave (its vectors in cur): window
+// masks and per-word nonzero prefixes to L.mask[b] / L.pre[b], the lane's
+// run boundaries and counts to q, and the window's entry and nonzero counts
+// to L.pw / L.vw.  The window's mask words are written and read by this wave
+// only, so a wave-level fence orders them.
+template <int ESZ, int OP>
+__device__ __forceinline__ void rle_c_classify(RleCLds<ESZ>& L, u32x4 (&cur)[RleCShape<ESZ>::V], RleLane& q, int b,
+                                               uint32_t t, uint32_t full, uint64_t Wr, const uint8_t* __restrict__ src,
+                                               uint64_t n, uint8_t* __restrict__ act, int wave, int lane) {
+  using S = RleCShape<ESZ>;
+  constexpr int V = S::V;
+  const uint64_t gw = (uint64_t)t * S::NW + wave;
+  const uint64_t e_win = gw * S::E;
+  q.Lw = gw < Wr ? (uint32_t)(n - e_win < (uint64_t)S::E ? n - e_win : S::E) : 0u;
+  // lane l takes SB = E/64 consecutive window positions starting at p0 (16 for
+  // 4-byte elements, 32 for 2-byte), so every lane has a share of the runs
+  constexpr uint32_t SB = (uint32_t)S::E / 64;
+  const uint32_t p0 = SB * (uint32_t)lane;
+  if (t >= full) {  // the one partial tile: load bounded, drain so nothing stays pending on cur
+    uint32_t el = (uint32_t)lane * S::EPL;
+    asm volatile("" : "+v"(el));
+    for (int j = 0; j < V; ++j) cur[j] = load_vec<ESZ>(src, e_win + (el + (uint32_t)(j * 64 * S::EPL)), n);
+    __builtin_amdgcn_s_waitcnt(0);
+  }
+  if constexpr (OP != kOpNone) rle_c_epilogue<ESZ, OP>(cur, act, n, t, e_win, t < full, wave, lane);
+  uint32_t* wm = L.mask[b] + wave * S::WPW;
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    const uint32_t bits = vec_nz_bits<ESZ>(cur[j]);
+    const uint32_t m = group_or<S::LPW>(bits << ((lane % S::LPW) * S::EPL));
+    if (lane % S::LPW == 0) wm[j * (64 / S::LPW) + lane / S::LPW] = m;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // one scan over the window's mask words gives its nonzero count and, for
+  // the value placement, the nonzeros before every word
+  uint32_t v_w;
+  {
+    const uint32_t x = lane < S::WPW ? wm[lane] : 0u;
+    const uint32_t c = (uint32_t)__builtin_popcount(x);
+    const uint32_t inc = wave_incl_scan(c);
+    if (lane < S::WPW) L.pre[b][wave * S::WPW + lane] = inc - c;
+    v_w = read_lane(inc, 63);
+  }
+  // boundary bits of this lane's positions: element i starts a run when it
+  // differs from element i-1 (the element before the window counts as zero)
+  uint32_t T = 0;
+  if (p0 < q.Lw) {
+    const uint32_t w0 = p0 / 32, sh = p0 % 32;
+    const uint32_t m = wm[w0];
+    const uint32_t before = sh ? (m >> (sh - 1)) & 1u : (w0 ? wm[w0 - 1] >> 31 : 0u);
+    if constexpr (SB == 32) {
+      T = m ^ ((m << 1) | before);
+    } else {
+      const uint32_t seg = (m >> sh) & ((1u << SB) - 1);
+      T = (seg ^ ((seg << 1) | before)) & ((1u << SB) - 1);
+    }
+    const uint32_t rem = q.Lw - p0;
+    if (rem < SB) T &= (1u << rem) - 1;
+  }
+  const uint32_t tc = (uint32_t)__builtin_popcount(T);
+  const uint32_t tinc = wave_incl_scan(tc);
+  q.T = T;
+  q.texcl = tinc - tc;
+  q.r_w = q.Lw ? 1 + read_lane(tinc, 63) : 0u;
+  q.p_w = ESZ == 4 ? q.r_w + (q.r_w & 1) : q.r_w;
+  if (lane == 0) {
+    L.pw[wave] = q.Lw ? q.p_w : 0u;
+    L.vw[wave] = q.Lw ? v_w : 0u;
+  }
+}
+
+// Write the window's block (run lengths, then its nonzeros in index order)
+// into the stage buffer st at the window's place in its tile (data waves).
+template <int ESZ>
+__device__ __forceinline__ void rle_c_compact(uint8_t* __restrict__ st, const uint32_t* __restrict__ wm,
+                                              const uint32_t* __restrict__ wp, const u32x4 (&v)[RleCShape<ESZ>::V],
+                                              const RleLane& q, int lane) {
+  using S = RleCShape<ESZ>;
+  constexpr uint32_t SB = (uint32_t)S::E / 64;
+  const uint32_t p0 = SB * (uint32_t)lane;
+  uint8_t* blk = st + 2 * q.Pb + ESZ * q.Vb;
+  // run lengths: the gap from the previous boundary (0 at the window start)
+  const uint32_t lastpos = q.T ? p0 + 31 - (uint32_t)__builtin_clz(q.T) : 0u;
+  const uint32_t imax = wave_incl_max(lastpos);
+  const uint32_t before = __shfl_up(imax, 1, 64);
+  uint32_t prev = lane ? before : 0u;
+  const uint32_t tau_last = read_lane(imax, 63);
+  uint32_t x = q.T, k = q.texcl;
+  while (x) {
+    const uint32_t bt = (uint32_t)__builtin_ctz(x);
+    x &= x - 1;
+    const uint32_t pos = p0 + bt;
+    lds_u16(blk, 2 * k, pos - prev);
+    prev = pos;
+    ++k;
+  }
+  if (lane == 0) {
+    lds_u16(blk, 2 * (q.r_w - 1), q.Lw - tau_last);
+    if (q.p_w > q.r_w) lds_u16(blk, 2 * q.r_w, 0);
+  }
+  // values follow the runs: a lane's first value of vector j comes after the
+  // nonzeros before its mask word and those below its bits there
+#pragma unroll
+  for (int j = 0; j < S::V; ++j) {
+    const uint32_t c = (uint32_t)(j * 64 + lane);
+    const uint32_t mw = wm[c / S::LPW];
+    const uint32_t sh = (c % S::LPW) * S::EPL;
+    const uint32_t bits = (mw >> sh) & ((1u << S::EPL) - 1);
+    uint32_t pos = 2 * q.p_w + ESZ * (wp[c / S::LPW] + (uint32_t)__builtin_popcount(mw & ((1u << sh) - 1)));
+#pragma unroll
+    for (int k2 = 0; k2 < S::EPL; ++k2) {
+      if ((bits >> k2) & 1u) {
+        store_elem<ESZ>(blk + pos, vec_elem<ESZ>(v[j], k2));
+        pos += ESZ;
+      }
+    }
+  }
+}
+
+// Per-iteration state of the control wave.
+struct RleCtl {
+  ChainRound cr;      // first round of the pending chain sum (issued last iteration)
+  uint64_t chain_lo;  // first tile of that sum
+  uint64_t pfx;       // packed inclusive prefix of the last tile resolved
+  uint32_t pend;      // raw counter value of the ticket to hand over next
+};
+
+// One iteration of the two-deep pipeline (the ZVC compressor's structure):
+// t is classified (its loads were issued last iteration into cur), tp1 is
+// compacted into stage[b ^ 1] from prev, whose registers then take the loads
+// of tl, and tp2 is stored from stage[b].  The control wave finishes tp2's
+// chain sum in phase X; in phase Y it hands over the next tile, publishes t's
+// aggregate and issues the first round of tp1's chain sum.  q: lane state of
+// t (written); qp: of tp1 (read); P2b / V2b: the window bases of tp2 (read,
+// then set to tp1's).  Returns the tile the data waves load next iteration,
+// with the workgroup synchronised.
 template <int ESZ, int OP>
 __device__ __forceinline__ uint32_t rle_c_iteration(RleCLds<ESZ>& L, u32x4 (&cur)[RleCShape<ESZ>::V],
-                                                    u32x4 (&nxt)[RleCShape<ESZ>::V], ChainRound& cr,
-                                                    uint64_t& chain_lo, uint64_t& pfx, uint32_t& pend, uint32_t t,
-                                                    uint32_t tn, uint32_t tp, int buf, uint32_t full, uint64_t Wr,
+                                                    u32x4 (&prev)[RleCShape<ESZ>::V], RleLane& q, const RleLane& qp,
+                                                    uint32_t& P2b, uint32_t& V2b, RleCtl& C, uint32_t t, uint32_t tp1,
+                                                    uint32_t tp2, uint32_t tl, int b, uint32_t full, uint64_t Wr,
                                                     const uint8_t* __restrict__ src, uint64_t n,
                                                     uint8_t* __restrict__ dst, uint64_t* __restrict__ out_bytes,
                                                     uint32_t* __restrict__ aggw, const Tickets& tk,
                                                     uint32_t num_tiles, uint8_t* __restrict__ act, int tid,
                                                     int wave, int lane) {
   using S = RleCShape<ESZ>;
-  constexpr int V = S::V;
-  const bool have_cur = t < num_tiles;
-  const bool have_prev = tp < num_tiles;
+  const bool have_t = t < num_tiles;
+  const bool have_p1 = tp1 < num_tiles;
+  const bool have_p2 = tp2 < num_tiles;
   const bool data = wave < S::NW;
   const uint64_t H = 8 * (Wr + 1);
 
-  // data waves: classify this wave's window and count its runs.  The window's
-  // mask words are written and read by this wave only, so a wave-level fence
-  // orders them.
-  const uint64_t gw = (uint64_t)t * S::NW + wave;
-  const uint64_t e_win = gw * S::E;
-  const uint32_t Lw = data && have_cur && gw < Wr ? (uint32_t)(n - e_win < (uint64_t)S::E ? n - e_win : S::E) : 0u;
-  // lane l takes SB = E/64 consecutive window positions starting at p0 (16 for
-  // 4-byte elements, 32 for 2-byte), so every lane has a share of the runs
-  constexpr uint32_t SB = (uint32_t)S::E / 64;
-  const uint32_t p0 = SB * (uint32_t)lane;
-  uint32_t T = 0, texcl = 0, r_w = 0, p_w = 0;
-  if (data && have_cur) {
-    if (t >= full) {  // the one partial tile: load bounded, drain so nothing stays pending on cur
-      uint32_t el = (uint32_t)lane * S::EPL;
-      asm volatile("" : "+v"(el));
-      for (int j = 0; j < V; ++j) cur[j] = load_vec<ESZ>(src, e_win + (el + (uint32_t)(j * 64 * S::EPL)), n);
-      __builtin_amdgcn_s_waitcnt(0);
-    }
-    if constexpr (OP != kOpNone) rle_c_epilogue<ESZ, OP>(cur, act, n, t, e_win, t < full, wave, lane);
-    uint32_t* wmask = L.mask + wave * S::WPW + lane / S::LPW;
-#pragma unroll
-    for (int j = 0; j < V; ++j) {
-      const uint32_t bits = vec_nz_bits<ESZ>(cur[j]);
-      const uint32_t m = group_or<S::LPW>(bits << ((lane % S::LPW) * S::EPL));
-      if (lane % S::LPW == 0) wmask[j * (64 / S::LPW)] = m;
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // one scan over the window's mask words gives its nonzero count and, for
-    // the value placement below, the nonzeros before every word
-    uint32_t v_w;
-    {
-      const uint32_t x = lane < S::WPW ? L.mask[wave * S::WPW + lane] : 0u;
-      const uint32_t c = (uint32_t)__builtin_popcount(x);
-      const uint32_t inc = wave_incl_scan(c);
-      if (lane < S::WPW) L.pre[wave * S::WPW + lane] = inc - c;
-      v_w = read_lane(inc, 63);
-    }
-    if (p0 < Lw) {
-      // boundary bits of this lane's positions: element i starts a run when it
-      // differs from element i-1 (the element before the window counts as zero)
-      const uint32_t w0 = p0 / 32, sh = p0 % 32;
-      const uint32_t m = L.mask[wave * S::WPW + w0];
-      const uint32_t before = sh ? (m >> (sh - 1)) & 1u : (w0 ? L.mask[wave * S::WPW + w0 - 1] >> 31 : 0u);
-      if constexpr (SB == 32) {
-        T = m ^ ((m << 1) | before);
-      } else {
-        const uint32_t seg = (m >> sh) & ((1u << SB) - 1);
-        T = (seg ^ ((seg << 1) | before)) & ((1u << SB) - 1);
-      }
-      const uint32_t rem = Lw - p0;
-      if (rem < SB) T &= (1u << rem) - 1;
-    }
-    const uint32_t tc = (uint32_t)__builtin_popcount(T);
-    const uint32_t tinc = wave_incl_scan(tc);
-    texcl = tinc - tc;
-    r_w = Lw ? 1 + read_lane(tinc, 63) : 0u;
-    p_w = ESZ == 4 ? r_w + (r_w & 1) : r_w;
+  // ---- phase X ----
+  if (data && have_p1 && qp.Lw)
+    rle_c_compact<ESZ>(L.stage[b ^ 1], L.mask[b ^ 1] + wave * S::WPW, L.pre[b ^ 1] + wave * S::WPW, prev, qp, lane);
+  {
+    const bool load = __builtin_amdgcn_readfirstlane(wave) < S::NW && tl < full;
+    rle_c_load_full<ESZ>(prev, src, tl, load, wave, lane);
+  }
+  if (data) {
+    if (have_t) rle_c_classify<ESZ, OP>(L, cur, q, b, t, full, Wr, src, n, act, wave, lane);
+  } else if (have_p2) {
+    bool stuck = false;
+    const uint64_t X = C.pfx + chain_sum(aggw, C.chain_lo, tp2, C.cr, &stuck, RleAggDec());
+    const uint64_t a2 = L.agg[b];  // tp2 was classified two iterations ago
     if (lane == 0) {
-      L.pw[wave] = p_w;
-      L.vw[wave] = v_w;
+      L.excl = X;
+      L.agg2 = a2;
+      if (stuck) atomicMax(reinterpret_cast<unsigned long long*>(out_bytes), kSizeInternalError);
     }
+    C.pfx = X + a2;  // tp2's inclusive prefix
   }
   __syncthreads();
 
+  // ---- phase Y ----
   if (data) {
-    if (have_cur) {
-      uint32_t P = 0, Vs = 0;  // entries and nonzeros of the windows before this one
-      for (int w = 0; w < wave; ++w) {
-        P += L.pw[w];
-        Vs += L.vw[w];
-      }
-      if (lane == 0) {
-        L.ipw[buf][wave] = P;
-        L.ivw[buf][wave] = Vs;
-      }
-      uint8_t* st = L.stage[buf] + 2 * P + ESZ * Vs;
-      if (Lw) {
-        // run lengths: the gap from the previous boundary (0 at the window start)
-        const uint32_t lastpos = T ? p0 + 31 - (uint32_t)__builtin_clz(T) : 0u;
-        const uint32_t imax = wave_incl_max(lastpos);
-        const uint32_t before = __shfl_up(imax, 1, 64);
-        uint32_t prev = lane ? before : 0u;
-        const uint32_t tau_last = read_lane(imax, 63);
-        uint32_t x = T, k = texcl;
-        while (x) {
-          const uint32_t b = (uint32_t)__builtin_ctz(x);
-          x &= x - 1;
-          const uint32_t pos = p0 + b;
-          lds_u16(st, 2 * k, pos - prev);
-          prev = pos;
-          ++k;
-        }
-        if (lane == 0) {
-          lds_u16(st, 2 * (r_w - 1), Lw - tau_last);
-          if (p_w > r_w) lds_u16(st, 2 * r_w, 0);
-        }
-        // values follow the runs: a lane's first value of vector j comes after
-        // the nonzeros before its mask word and those below its bits there
-        const uint32_t* wm = L.mask + wave * S::WPW;
-        const uint32_t* wp = L.pre + wave * S::WPW;
-#pragma unroll
-        for (int j = 0; j < V; ++j) {
-          const uint32_t c = (uint32_t)(j * 64 + lane);
-          const uint32_t mw = wm[c / S::LPW];
-          const uint32_t sh = (c % S::LPW) * S::EPL;
-          const uint32_t bits = (mw >> sh) & ((1u << S::EPL) - 1);
-          uint32_t pos = 2 * p_w + ESZ * (wp[c / S::LPW] + (uint32_t)__builtin_popcount(mw & ((1u << sh) - 1)));
-#pragma unroll
-          for (int k2 = 0; k2 < S::EPL; ++k2) {
-            if ((bits >> k2) & 1u) {
-              store_elem<ESZ>(st + pos, vec_elem<ESZ>(cur[j], k2));
-              pos += ESZ;
-            }
-          }
-        }
-      }
-      if (tn < full) rle_c_load_full<ESZ>(nxt, src, tn, wave, lane);
-    }
-  } else {
-    // control wave (see the ZVC compressor)
-    // what this wave issued last iteration (chain round, ticket) must be back
-    // before the hand-over; waiting here on every path keeps the compiler from
-    // waiting again after the ticket drawn next
-    __builtin_amdgcn_s_waitcnt(0);
-    if (lane == 0) L.next = tk.tile(pend);
-    // the next ticket goes out now and has a whole iteration to come back
-    if (lane == 0 && have_cur) pend = tk.raw();
-    if (have_cur) {
+    if (have_t) {  // t's window bases inside its tile
       const uint32_t pl = lane < S::NW ? L.pw[lane] : 0u;
       const uint32_t vl = lane < S::NW ? L.vw[lane] : 0u;
-      const uint32_t P = read_lane(wave_incl_scan(pl), 63), Vs = read_lane(wave_incl_scan(vl), 63);
-      if (lane == 0) {
-        L.agg[buf] = ((uint64_t)P << 31) | Vs;
-        agg_publish(aggw, t, (P << 15) | Vs);
-      }
+      const uint32_t pi = wave_incl_scan(pl), vi = wave_incl_scan(vl);
+      q.Pb = read_lane(pi - pl, wave);
+      q.Vb = read_lane(vi - vl, wave);
     }
-    if (have_prev) {
-      bool stuck = false;
-      const uint64_t X = pfx + chain_sum(aggw, chain_lo, tp, cr, &stuck, RleAggDec());
-      if (lane == 0) {
-        L.excl = X;
-        if (stuck) atomicMax(reinterpret_cast<unsigned long long*>(out_bytes), kSizeInternalError);
-      }
-      pfx = X + L.agg[buf ^ 1];  // tp's inclusive prefix
-    }
-  }
-  __syncthreads();
-
-  if (data) {
-    if (have_prev) {
-      const int pb = buf ^ 1;
-      const uint64_t agg = L.agg[pb];
-      const uint32_t P = (uint32_t)(agg >> 31), Vs = (uint32_t)(agg & kLow31);
+    if (have_p2) {
+      const uint64_t a2 = L.agg2;
+      const uint32_t P = (uint32_t)(a2 >> 31), Vs = (uint32_t)(a2 & kLow31);
       const uint64_t RX = L.excl >> 31, VX = L.excl & kLow31;
       const uint64_t O = H + 2 * RX + (uint64_t)ESZ * VX;  // first byte of the tile's blocks
       const uint32_t span = 2 * P + ESZ * Vs;
-      store_staged<2, S::NW * 64>(L.stage[pb], span, O, dst, tid);
-      if (tid < S::NW) {
-        const uint64_t w = (uint64_t)tp * S::NW + tid;
-        if (w < Wr) {
-          reinterpret_cast<uint32_t*>(dst)[w] = (uint32_t)(RX + L.ipw[pb][tid]);
-          reinterpret_cast<uint32_t*>(dst + 4 * (Wr + 1))[w] = (uint32_t)(VX + L.ivw[pb][tid]);
-        }
+      store_staged<2, S::NW * 64>(L.stage[b], span, O, dst, tid);
+      const uint64_t w = (uint64_t)tp2 * S::NW + wave;
+      if (lane == 0 && w < Wr) {
+        reinterpret_cast<uint32_t*>(dst)[w] = (uint32_t)(RX + P2b);
+        reinterpret_cast<uint32_t*>(dst + 4 * (Wr + 1))[w] = (uint32_t)(VX + V2b);
       }
-      if (tp == num_tiles - 1 && tid == 0) {
+      if (tp2 == num_tiles - 1 && tid == 0) {
         reinterpret_cast<uint32_t*>(dst)[Wr] = (uint32_t)(RX + P);
         reinterpret_cast<uint32_t*>(dst + 4 * (Wr + 1))[Wr] = (uint32_t)(VX + Vs);
         atomicMax(reinterpret_cast<unsigned long long*>(out_bytes), O + span);
       }
     }
-  } else if (have_cur) {
-    chain_lo = have_prev ? (uint64_t)tp + 1 : 0;
-    chain_issue(aggw, chain_lo, t, cr);
+  } else {
+    // control wave: what it issued last iteration (chain round, ticket) must
+    // be back before the hand-over; waiting here on every path keeps the
+    // compiler from waiting again after the ticket drawn next
+    __builtin_amdgcn_s_waitcnt(0);
+    if (lane == 0) L.next = tk.tile(C.pend);
+    // the next ticket goes out now and has a whole iteration to come back
+    if (lane == 0 && have_t) C.pend = tk.raw();
+    if (have_t) {
+      const uint32_t pl = lane < S::NW ? L.pw[lane] : 0u;
+      const uint32_t vl = lane < S::NW ? L.vw[lane] : 0u;
+      const uint32_t P = read_lane(wave_incl_scan(pl), 63), Vs = read_lane(wave_incl_scan(vl), 63);
+      if (lane == 0) {
+        L.agg[b] = ((uint64_t)P << 31) | Vs;
+        agg_publish(aggw, t, (P << 15) | Vs);
+      }
+    }
+    if (have_p1) {
+      // tp1's chain sum: the tiles between this workgroup's tile before it
+      // (tp2) and tp1; summed at the start of the next iteration
+      C.chain_lo = have_p2 ? (uint64_t)tp2 + 1 : 0;
+      chain_issue(aggw, C.chain_lo, tp1, C.cr);
+    }
   }
+  P2b = qp.Pb;
+  V2b = qp.Vb;
+  __syncthreads();
   return __builtin_amdgcn_readfirstlane(L.next);  // uniform: keeps tile bases in SGPRs
 }
 
@@ -377,33 +427,41 @@ __global__ __launch_bounds__(RleCShape<ESZ>::BLOCK) void rle_compress_kernel(
   const Tickets tk = ticket_source(counter, __builtin_amdgcn_readfirstlane(L.mode));
   if (tid < 3 * 64 && lane == 0) L.init[wave] = tk.raw();
   __syncthreads();
+  // raw counter values of the first three tickets in increasing order (a
+  // class's tiles increase with them): classify, load, hand over
   const uint32_t a = __builtin_amdgcn_readfirstlane(L.init[0]);
   const uint32_t b = __builtin_amdgcn_readfirstlane(L.init[1]);
   const uint32_t c = __builtin_amdgcn_readfirstlane(L.init[2]);
-  // raw counter values: a class's tiles increase with them
   const uint32_t lo = min(a, min(b, c)), hi = max(a, max(b, c));
-  uint32_t t = tk.tile(lo);
-  uint32_t tn = tk.tile(a + b + c - lo - hi);
-  uint32_t pend = hi;     // control wave: raw value of the ticket to hand over next
-  uint32_t tp = num_tiles;
+  uint32_t t = tk.tile(lo);                  // classified this iteration
+  uint32_t tl = tk.tile(a + b + c - lo - hi);  // loaded this iteration
+  uint32_t tp1 = num_tiles, tp2 = num_tiles;   // compacted / stored this iteration (none yet)
+  RleCtl C;                                    // control wave
+  C.chain_lo = 0;
+  C.pfx = 0;
+  C.pend = hi;
+  RleLane qa, qb;
+  qa.Lw = qb.Lw = 0;
+  qa.Pb = qa.Vb = qb.Pb = qb.Vb = 0;
+  uint32_t P2b = 0, V2b = 0;
   u32x4 ra[S::V], rb[S::V];
-  ChainRound cr;          // control wave: chain sum in flight
-  uint64_t chain_lo = 0;  // control wave: first tile of that sum
-  uint64_t pfx = 0;       // control wave: packed inclusive prefix of the last resolved tile
-  if (wave < S::NW && t < full) rle_c_load_full<ESZ>(ra, src, t, wave, lane);
+  rle_c_load_full<ESZ>(ra, src, t, __builtin_amdgcn_readfirstlane(wave) < S::NW && t < full, wave, lane);
+  // Two iterations per trip so the register sets swap roles without copies,
+  // and one exit after the second (see the ZVC compressor).
   for (;;) {
-    uint32_t tnn = rle_c_iteration<ESZ, OP>(L, ra, rb, cr, chain_lo, pfx, pend, t, tn, tp, 0, full, Wr, src, n,
-                                            dst, out_bytes, aggw, tk, num_tiles, act, tid, wave, lane);
-    if (t >= num_tiles) break;
-    tp = t;
-    t = tn;
-    tn = tnn;
-    tnn = rle_c_iteration<ESZ, OP>(L, rb, ra, cr, chain_lo, pfx, pend, t, tn, tp, 1, full, Wr, src, n, dst,
-                                   out_bytes, aggw, tk, num_tiles, act, tid, wave, lane);
-    if (t >= num_tiles) break;
-    tp = t;
-    t = tn;
-    tn = tnn;
+    uint32_t r = rle_c_iteration<ESZ, OP>(L, ra, rb, qa, qb, P2b, V2b, C, t, tp1, tp2, tl, 0, full, Wr, src, n, dst,
+                                          out_bytes, aggw, tk, num_tiles, act, tid, wave, lane);
+    tp2 = tp1;
+    tp1 = t;
+    t = tl;
+    tl = r;
+    r = rle_c_iteration<ESZ, OP>(L, rb, ra, qb, qa, P2b, V2b, C, t, tp1, tp2, tl, 1, full, Wr, src, n, dst,
+                                 out_bytes, aggw, tk, num_tiles, act, tid, wave, lane);
+    tp2 = tp1;
+    tp1 = t;
+    t = tl;
+    tl = r;
+    if (t >= num_tiles && tp1 >= num_tiles && tp2 >= num_tiles) break;
   }
 }
 
