@@ -219,14 +219,31 @@ __device__ __forceinline__ uint32_t start_mode(uint32_t* counter) {
 // reads mixed into that write stream cost far more than their bytes (on this
 // GPU a write stream with 3 % reads from HBM runs about ten points of peak
 // slower than one whose reads hit the 256 MB memory-side cache).  So when the
-// whole stream fits in that cache, the decoder first reads it once with
-// caching loads (a pure read pass), and the decode's own reads then hit the
-// cache.  Outputs are written with non-temporal stores, which leave the
-// cached stream in place.  Larger streams are not warmed: the decode would
-// evict them before it reached them.
+// whole stream fits in that cache (CDMA_WARM_BYTES) and is a small share of a
+// large output (at most CDMA_WARM_MAX_PCT percent of at least
+// CDMA_WARM_MIN_OUT bytes), the decoder first reads it once with caching
+// loads (a pure read pass), and the decode's own reads then hit the cache.
+// Outputs are written with non-temporal stores, which leave the cached
+// stream in place.  Larger streams are not warmed whole (the decode would
+// evict them before it reached them), and neither are streams that are a
+// large share of their output or of a small output: there the extra pass
+// costs more than it saves (the maps of a few hundred MB whose stream is half
+// their size decoded up to 50 % slower with it).
 #ifndef CDMA_WARM_BYTES
 #define CDMA_WARM_BYTES (192ull << 20)
 #endif
+#ifndef CDMA_WARM_MAX_PCT
+#define CDMA_WARM_MAX_PCT 20
+#endif
+#ifndef CDMA_WARM_MIN_OUT
+#define CDMA_WARM_MIN_OUT (512ull << 20)
+#endif
+
+// Whether a stream of eff bytes decoding to out bytes is read ahead whole.
+__host__ __device__ __forceinline__ bool warm_whole(uint64_t eff, uint64_t out) {
+  return eff <= (uint64_t)CDMA_WARM_BYTES && out >= (uint64_t)CDMA_WARM_MIN_OUT &&
+         eff * 100 <= out * CDMA_WARM_MAX_PCT;
+}
 
 // Read quads [q0, q1) of p: thread `start` of `stride` takes every
 // stride-th quad, four loads in flight per trip.

@@ -35,20 +35,21 @@ __global__ void store_u64_kernel(uint64_t* p, uint64_t v) {
 #endif
 constexpr uint32_t kAheadGroups = CDMA_AHEAD_GROUPS;
 
-// Warm the memory-side cache with the stream (see warm_quads) when its
-// readable size is at most `limit`; otherwise return at once.
+// Warm the memory-side cache with the stream (see warm_whole); otherwise
+// return at once.  Launched only when the output is large enough to warm.
 constexpr unsigned kWarmGroups = 1024;
 __global__ __launch_bounds__(256) void warm_stream_kernel(const uint8_t* __restrict__ src, uint64_t cap,
-                                                          const uint64_t* __restrict__ src_bytes, uint64_t limit) {
+                                                          const uint64_t* __restrict__ src_bytes, uint64_t out) {
   const uint64_t claimed = src_bytes ? *src_bytes : cap;
   const uint64_t eff = claimed < cap ? claimed : cap;
-  if (eff > limit) return;
+  if (!warm_whole(eff, out)) return;
   warm_quads(src, 0, eff / 16, (uint64_t)blockIdx.x * 256 + threadIdx.x, (uint64_t)gridDim.x * 256);
 }
 
-static hipError_t warm_stream(const void* src, uint64_t cap, const uint64_t* src_bytes, hipStream_t s) {
-  if (CDMA_WARM_BYTES == 0 || cap == 0) return hipSuccess;
-  warm_stream_kernel<<<kWarmGroups, 256, 0, s>>>(static_cast<const uint8_t*>(src), cap, src_bytes, CDMA_WARM_BYTES);
+static hipError_t warm_stream(const void* src, uint64_t cap, const uint64_t* src_bytes, uint64_t out,
+                              hipStream_t s) {
+  if (CDMA_WARM_BYTES == 0 || cap == 0 || out < (uint64_t)CDMA_WARM_MIN_OUT) return hipSuccess;
+  warm_stream_kernel<<<kWarmGroups, 256, 0, s>>>(static_cast<const uint8_t*>(src), cap, src_bytes, out);
   return hipGetLastError();
 }
 
@@ -226,12 +227,13 @@ static hipError_t zvc_decompress_t(const void* src, uint64_t cap, const uint64_t
   const uint64_t nchunks = chunk ? (tiles + chunk - 1) / chunk : 1;  // with read-ahead
   // a chunk is read ahead only when the stream can exceed what the count pass
   // leaves in the cache and still be a small share of the output
-  const bool may_ahead = (uint64_t)ESZ * n / 100 * CDMA_AHEAD_MAX_PCT > (uint64_t)CDMA_WARM_BYTES;
+  const bool may_ahead = (uint64_t)ESZ * n / 100 * CDMA_WARM_MAX_PCT > (uint64_t)CDMA_WARM_BYTES;
   const uint32_t warm = chunk && may_ahead ? kAheadGroups : 0u;
   // read-ahead counters and flags, 128-byte aligned after sup[]
   uint32_t* sync = reinterpret_cast<uint32_t*>((reinterpret_cast<uintptr_t>(sup + supers + 1) + 127) & ~uintptr_t(127));
   zvc_count_kernel<WPT><<<(unsigned)supers, kBlock, 0, s>>>(static_cast<const uint8_t*>(src), cap, src_bytes,
-                                                                  n, local, sup, error, (uint32_t)tiles, CDMA_WARM_BYTES);
+                                                                  n, local, sup, error, (uint32_t)tiles,
+                                                                  CDMA_WARM_BYTES > 0);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   zvc_scan_kernel<<<1, kScanBlock, 0, s>>>(sup, (uint32_t)supers, sync, warm ? (uint32_t)nchunks * kAheadSyncWords : 0u);
   if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -241,8 +243,7 @@ static hipError_t zvc_decompress_t(const void* src, uint64_t cap, const uint64_t
   const uint64_t grid = tiles + (uint64_t)warm * nchunks;
   kern<<<(unsigned)grid, kBlock, pad, s>>>(static_cast<const uint8_t*>(src), cap, src_bytes, n,
                                            static_cast<uint8_t*>(dst), error, local, sup, (uint32_t)tiles,
-                                           warm ? (uint32_t)chunk : (uint32_t)tiles, warm, (uint32_t)window, sync,
-                                           CDMA_WARM_BYTES);
+                                           warm ? (uint32_t)chunk : (uint32_t)tiles, warm, (uint32_t)window, sync);
   return hipGetLastError();
 }
 
@@ -315,7 +316,7 @@ static hipError_t rle_decompress_t(const void* src, uint64_t cap, const uint64_t
                                    void* dst, uint32_t* error, hipStream_t s) {
   const uint64_t wins = (n + RleShape<ESZ>::E - 1) / RleShape<ESZ>::E;
   const uint64_t groups = (wins + kRleDecWaves - 1) / kRleDecWaves;
-  const hipError_t e = warm_stream(src, cap, src_bytes, s);
+  const hipError_t e = warm_stream(src, cap, src_bytes, (uint64_t)ESZ * n, s);
   if (e != hipSuccess) return e;
   rle_decompress_kernel<ESZ><<<(unsigned)groups, kRleDecBlock, 0, s>>>(
       static_cast<const uint8_t*>(src), cap, src_bytes, n, static_cast<uint8_t*>(dst), error, (uint32_t)groups);
@@ -424,7 +425,7 @@ hipError_t zvci_decompress_launch(int esz, const void* src, uint64_t cap, const 
   const uint64_t E = 4096 / (uint64_t)esz;
   const uint64_t blocks = (n + E - 1) / E;
   const unsigned grid = (unsigned)((blocks + kWaves - 1) / kWaves);
-  const hipError_t e = warm_stream(src, cap, src_bytes, s);
+  const hipError_t e = warm_stream(src, cap, src_bytes, (uint64_t)esz * n, s);
   if (e != hipSuccess) return e;
   if (esz == 4)
     zvci_decompress_kernel<4><<<grid, kBlock, 0, s>>>(static_cast<const uint8_t*>(src), cap, src_bytes, n,

@@ -44,8 +44,9 @@ template <int TWPT>
 __global__ __launch_bounds__(kBlock) void zvc_count_kernel(
     const uint8_t* __restrict__ src, uint64_t src_capacity, const uint64_t* __restrict__ src_bytes,
     uint64_t n, uint32_t* __restrict__ local, uint32_t* __restrict__ sup, uint32_t* __restrict__ error,
-    uint32_t num_tiles, uint64_t warm_limit) {
+    uint32_t num_tiles, bool warm) {
   using C = ZvcScanShape<TWPT>;
+  static_assert(512 % TWPT == 0, "a decode tile is 16 KB: 32 * TWPT elements of 512 / TWPT bytes");
   // Mask quad i of the super tile (16 bytes) is read by thread i % kBlock in
   // step i / kBlock, so each load instruction covers 1 KB of contiguous masks.
   // A decode tile's quads are then an aligned group of QT lanes of one step.
@@ -113,10 +114,10 @@ __global__ __launch_bounds__(kBlock) void zvc_count_kernel(
     if (lane == 63) sup[u] = inc;
   }
   if (err && error) atomicOr(error, err);
-  // a stream that fits in the memory-side cache: every workgroup also reads
-  // its share of the values (the masks it read are kept already), so the
-  // expand pass reads the whole stream from the cache
-  if (eff <= warm_limit && eff > 4 * W) {
+  // a stream to warm whole (warm_whole): every workgroup also reads its
+  // share of the values (the masks it read are kept already), so the expand
+  // pass reads the whole stream from the cache
+  if (warm && eff > 4 * W && warm_whole(eff, (uint64_t)(512 / TWPT) * n)) {
     const uint64_t q0 = 4 * W / 16, q1 = eff / 16;
     const uint64_t per = (q1 - q0 + gridDim.x - 1) / gridDim.x;
     const uint64_t a = q0 + (uint64_t)u * per, b = a + per < q1 ? a + per : q1;
@@ -355,9 +356,6 @@ __device__ __forceinline__ uint32_t zvc_tile_offset(const uint32_t* __restrict__
 // CDMA_AHEAD_MAX_PCT percent of the output, or when the chunk's share
 // exceeds CDMA_WARM_BYTES.  The waits only order memory traffic; the result
 // does not depend on them.
-#ifndef CDMA_AHEAD_MAX_PCT
-#define CDMA_AHEAD_MAX_PCT 20
-#endif
 #ifndef CDMA_AHEAD_SPIN
 #define CDMA_AHEAD_SPIN 1000
 #endif
@@ -376,8 +374,7 @@ __global__ __launch_bounds__(kBlock) void zvc_expand_kernel(
     const uint8_t* __restrict__ src, uint64_t src_capacity, const uint64_t* __restrict__ src_bytes,
     uint64_t n, uint8_t* __restrict__ dst, uint32_t* __restrict__ error,
     const uint32_t* __restrict__ local, const uint32_t* __restrict__ sup, uint32_t num_tiles,
-    uint32_t chunk_tiles, uint32_t warm_groups, uint32_t wait_window, uint32_t* __restrict__ sync,
-    uint64_t fits_limit) {
+    uint32_t chunk_tiles, uint32_t warm_groups, uint32_t wait_window, uint32_t* __restrict__ sync) {
   __shared__ ZvcExpandLds<ESZ, V> L;
   constexpr int WPT = ZvcShape<ESZ, V>::WPT;
   const int tid = threadIdx.x;
@@ -400,7 +397,7 @@ __global__ __launch_bounds__(kBlock) void zvc_expand_kernel(
     if (v1 > eff) v1 = eff;
     if (m0 > m1) m0 = m1;
     if (v0 > v1) v0 = v1;
-    const bool ahead = stream > fits_limit && stream * 100 <= (uint64_t)ESZ * n * CDMA_AHEAD_MAX_PCT &&
+    const bool ahead = !warm_whole(stream, (uint64_t)ESZ * n) && stream * 100 <= (uint64_t)ESZ * n * CDMA_WARM_MAX_PCT &&
                        (m1 - m0) + (v1 - v0) <= (uint64_t)CDMA_WARM_BYTES;
     if (r < warm_groups) {  // a read-ahead workgroup: its strided share of the chunk
       if (!ahead) return;
