@@ -53,15 +53,28 @@ struct ZviCShape : ZviShape<ESZ> {
 template <int ESZ>
 struct ZviCLds {
   using S = ZviCShape<ESZ>;
-  uint64_t excl;                          // exclusive nonzero prefix of the tile being stored
-  uint32_t total[2];                      // nonzeros of the tile in stage[b]
-  uint32_t vw[S::NW], bw[S::NW];          // per-block nonzeros and bytes (read between B1 and B2)
-  uint32_t ivw[2][S::NW];                 // in-tile nonzero prefix of each block, for stage[b]
-  uint32_t span[2];                       // staged bytes of stage[b]
+  uint64_t excl;                          // exclusive nonzero prefix of the tile stored this iteration
+  uint32_t total2, span2;                 // and its nonzeros and staged bytes
+  uint32_t total[2], span[2];             // nonzeros / staged bytes of the tile classified in an iteration of parity b
+  uint32_t vw[S::NW], bw[S::NW];          // per-block nonzeros and bytes of the tile being classified
   uint32_t next;                          // ticket handed from the control wave to the data waves
   uint32_t mode;                          // start_mode's choice (selects the ticket source)
   uint32_t init[3];                       // the first three tickets
   __attribute__((aligned(16))) uint8_t stage[2][S::STAGE];
+};
+
+// What a data lane keeps of its block from the classify to the compaction
+// one iteration later: the element nonzero bits of its V rows (EPL bits at
+// EPL*j of bits), the block's nonzeros before the lane's elements of each row
+// (16 bits at 16*(j%2) of pre[j/2]), and the block's place in its tile (Bb
+// staged bytes and Vb nonzeros before it; nwin windows; all the same on every
+// lane).
+template <int V>
+struct ZviLane {
+  uint32_t bits;
+  uint32_t pre[V / 2];
+  uint32_t nwin, Bb, Vb;
+  __device__ __forceinline__ uint32_t pre_of(int j) const { return __builtin_amdgcn_ubfe(pre[j / 2], 16 * (j % 2), 16); }
 };
 
 // 32-bit LDS word at a 2-byte aligned address, as two halves.
@@ -74,146 +87,176 @@ __device__ __forceinline__ uint32_t lds_get_u32_at2(const uint8_t* base, uint32_
          ((uint32_t)*reinterpret_cast<const uint16_t*>(base + byte + 2) << 16);
 }
 
+// Load tile t's blocks, one per data wave, issued on every path (see
+// rle_c_load_full).
 template <int ESZ>
 __device__ __forceinline__ void zvi_c_load_full(u32x4 (&v)[ZviShape<ESZ>::V], const uint8_t* __restrict__ src,
-                                                uint32_t t, int wave, int lane) {
+                                                uint32_t t, bool valid, int wave, int lane) {
   using S = ZviCShape<ESZ>;
-  const uint8_t* p = src + (uint64_t)t * (S::NW * 4096);
-  uint32_t o = (uint32_t)(wave * 4096 + lane * 16);
-  asm volatile("" : "+v"(o));  // keep base + o from being hoisted into a 64-bit register pair
+  const uint8_t* p = src + (uint64_t)t * (S::NW * 4096);  // uniform tile base
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p), (short)0, valid ? S::NW * 4096 : 0, kBufferFlags);
+  const uint32_t o = (uint32_t)(wave * 4096 + lane * 16);
 #pragma unroll
-  for (int j = 0; j < S::V; ++j) v[j] = ld_stream(reinterpret_cast<const u32x4*>(p + o + j * 1024));
+  for (int j = 0; j < S::V; ++j) v[j] = __builtin_amdgcn_raw_buffer_load_b128(r, o + j * 1024, 0, kLoadAux);
 }
 
-// One pipeline iteration (the structure of the run-length compressor's).
-// Returns the ticket the data waves prefetch in the next iteration.
+// Classify tile t's block of this data wave (its vectors in cur): per-lane
+// row bits and in-block prefixes to q, the block's nonzeros and staged bytes
+// to L.vw / L.bw.
 template <int ESZ>
-__device__ __forceinline__ uint32_t zvi_c_iteration(ZviCLds<ESZ>& L, u32x4 (&cur)[ZviShape<ESZ>::V],
-                                                    u32x4 (&nxt)[ZviShape<ESZ>::V], ChainRound& cr,
-                                                    uint64_t& chain_lo, uint64_t& pfx, uint32_t& pend, uint32_t t,
-                                                    uint32_t tn, uint32_t tp, int buf, uint32_t full, uint64_t Wr,
-                                                    const uint8_t* __restrict__ src, uint64_t n,
-                                                    uint8_t* __restrict__ dst, uint64_t* __restrict__ out_bytes,
-                                                    uint32_t* __restrict__ agg, const Tickets& tk,
-                                                    uint32_t num_tiles, int tid, int wave, int lane) {
+__device__ __forceinline__ void zvi_c_classify(ZviCLds<ESZ>& L, u32x4 (&cur)[ZviShape<ESZ>::V],
+                                               ZviLane<ZviShape<ESZ>::V>& q, uint32_t t, uint32_t full, uint64_t Wr,
+                                               const uint8_t* __restrict__ src, uint64_t n, int wave, int lane) {
   using S = ZviCShape<ESZ>;
   constexpr int V = S::V;
-  const bool have_cur = t < num_tiles;
-  const bool have_prev = tp < num_tiles;
+  const uint64_t gw = (uint64_t)t * S::NW + wave;
+  const uint64_t e_win = gw * S::E;
+  const uint32_t Lw = gw < Wr ? (uint32_t)(n - e_win < (uint64_t)S::E ? n - e_win : S::E) : 0u;
+  q.nwin = (Lw + 31) / 32;
+  if (t >= full) {  // the one partial tile: load bounded, drain so nothing stays pending on cur
+    uint32_t el = (uint32_t)lane * S::EPL;
+    asm volatile("" : "+v"(el));
+    for (int j = 0; j < V; ++j) cur[j] = load_vec<ESZ>(src, e_win + (el + (uint32_t)(j * 64 * S::EPL)), n);
+    __builtin_amdgcn_s_waitcnt(0);
+  }
+  uint32_t v_w = 0;
+  q.bits = 0;
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    const uint32_t bits = vec_nz_bits<ESZ>(cur[j]);
+    const uint32_t cnt = (uint32_t)__builtin_popcount(bits);
+    const uint32_t inc = wave_incl_scan(cnt);
+    const uint32_t pre = v_w + inc - cnt;  // nonzeros of the block before this lane's elements of row j
+    q.bits |= bits << (S::EPL * j);
+    if (j % 2 == 0) q.pre[j / 2] = pre;
+    else q.pre[j / 2] |= pre << 16;
+    v_w += read_lane(inc, 63);
+  }
+  if (lane == 0) {
+    L.vw[wave] = v_w;
+    L.bw[wave] = 4 * q.nwin + ESZ * v_w;
+  }
+}
+
+// Write the block (mask, values, mask, values, ...) into stage st at the
+// block's place in its tile (data waves).
+template <int ESZ>
+__device__ __forceinline__ void zvi_c_compact(uint8_t* __restrict__ stage, const u32x4 (&v)[ZviShape<ESZ>::V],
+                                              const ZviLane<ZviShape<ESZ>::V>& q, int lane) {
+  using S = ZviCShape<ESZ>;
+  uint8_t* st = stage + q.Bb;
+#pragma unroll
+  for (int j = 0; j < S::V; ++j) {
+    const uint32_t bits = __builtin_amdgcn_ubfe(q.bits, S::EPL * j, S::EPL);
+    const uint32_t msk = group_or<S::LPW>(bits << ((lane % S::LPW) * S::EPL));
+    const uint32_t pre = q.pre_of(j);
+    const uint32_t wl = (uint32_t)(j * S::WPV + lane / S::LPW);  // window of this lane in the block
+    if (wl < q.nwin) {
+      // the window's mask sits after the masks and values of the windows before it
+      if (lane % S::LPW == 0) {  // the window's first lane: nothing of the window before it
+        if constexpr (ESZ == 4) *reinterpret_cast<uint32_t*>(st + 4 * wl + ESZ * pre) = msk;
+        else lds_u32_at2(st, 4 * wl + ESZ * pre, msk);
+      }
+      uint32_t pos = 4 * (wl + 1) + ESZ * pre;
+#pragma unroll
+      for (int k = 0; k < S::EPL; ++k) {
+        if ((bits >> k) & 1u) {
+          store_elem<ESZ>(st + pos, vec_elem<ESZ>(v[j], k));
+          pos += ESZ;
+        }
+      }
+    }
+  }
+}
+
+// One iteration of the two-deep pipeline (see rle_c_iteration): t is
+// classified, tp1 compacted into stage[b ^ 1] from prev (whose registers then
+// take tl's loads), tp2 stored from stage[b].  V2b: the nonzero base of tp2's
+// block of this wave (read, then set to tp1's).
+template <int ESZ>
+__device__ __forceinline__ uint32_t zvi_c_iteration(ZviCLds<ESZ>& L, u32x4 (&cur)[ZviShape<ESZ>::V],
+                                                    u32x4 (&prev)[ZviShape<ESZ>::V], ZviLane<ZviShape<ESZ>::V>& q,
+                                                    const ZviLane<ZviShape<ESZ>::V>& qp, uint32_t& V2b, RleCtl& C,
+                                                    uint32_t t, uint32_t tp1, uint32_t tp2, uint32_t tl, int b,
+                                                    uint32_t full, uint64_t Wr, const uint8_t* __restrict__ src,
+                                                    uint64_t n, uint8_t* __restrict__ dst,
+                                                    uint64_t* __restrict__ out_bytes, uint32_t* __restrict__ agg,
+                                                    const Tickets& tk, uint32_t num_tiles, int tid, int wave,
+                                                    int lane) {
+  using S = ZviCShape<ESZ>;
+  const bool have_t = t < num_tiles;
+  const bool have_p1 = tp1 < num_tiles;
+  const bool have_p2 = tp2 < num_tiles;
   const bool data = wave < S::NW;
   const uint64_t H = 4 * (Wr + 1);
 
-  // data waves: classify this wave's block, count its values and windows
-  const uint64_t gw = (uint64_t)t * S::NW + wave;
-  const uint64_t e_win = gw * S::E;
-  const uint32_t Lw = data && have_cur && gw < Wr ? (uint32_t)(n - e_win < (uint64_t)S::E ? n - e_win : S::E) : 0u;
-  const uint32_t nwin = (Lw + 31) / 32;
-  uint32_t bits[V], pre[V], msk[V];
-  uint32_t v_w = 0;
-  if (data && have_cur) {
-    if (t >= full) {  // the one partial tile: load bounded, drain so nothing stays pending on cur
-      uint32_t el = (uint32_t)lane * S::EPL;
-      asm volatile("" : "+v"(el));
-      for (int j = 0; j < V; ++j) cur[j] = load_vec<ESZ>(src, e_win + (el + (uint32_t)(j * 64 * S::EPL)), n);
-      __builtin_amdgcn_s_waitcnt(0);
-    }
-#pragma unroll
-    for (int j = 0; j < V; ++j) {
-      bits[j] = vec_nz_bits<ESZ>(cur[j]);
-      msk[j] = group_or<S::LPW>(bits[j] << ((lane % S::LPW) * S::EPL));
-      const uint32_t cnt = (uint32_t)__builtin_popcount(bits[j]);
-      const uint32_t inc = wave_incl_scan(cnt);
-      pre[j] = v_w + inc - cnt;  // nonzeros of the block before this lane's elements of row j
-      v_w += read_lane(inc, 63);
-    }
+  // ---- phase X ----
+  if (data && have_p1 && qp.nwin) zvi_c_compact<ESZ>(L.stage[b ^ 1], prev, qp, lane);
+  {
+    const bool load = __builtin_amdgcn_readfirstlane(wave) < S::NW && tl < full;
+    zvi_c_load_full<ESZ>(prev, src, tl, load, wave, lane);
+  }
+  if (data) {
+    if (have_t) zvi_c_classify<ESZ>(L, cur, q, t, full, Wr, src, n, wave, lane);
+  } else if (have_p2) {
+    bool stuck = false;
+    const uint64_t X = C.pfx + chain_sum(agg, C.chain_lo, tp2, C.cr, &stuck, [](uint32_t v) { return v; });
+    const uint32_t T2 = L.total[b];  // tp2 was classified two iterations ago
     if (lane == 0) {
-      L.vw[wave] = v_w;
-      L.bw[wave] = 4 * nwin + ESZ * v_w;
+      L.excl = X;
+      L.total2 = T2;
+      L.span2 = L.span[b];
+      if (stuck) atomicMax(reinterpret_cast<unsigned long long*>(out_bytes), kSizeInternalError);
     }
+    C.pfx = X + T2;  // tp2's inclusive prefix
   }
   __syncthreads();
 
+  // ---- phase Y ----
   if (data) {
-    if (have_cur) {
-      uint32_t B = 0, Vs = 0;  // staged bytes and nonzeros of the blocks before this one
-      for (int w = 0; w < wave; ++w) {
-        B += L.bw[w];
-        Vs += L.vw[w];
-      }
-      if (lane == 0) L.ivw[buf][wave] = Vs;
-      if (wave == S::NW - 1 && lane == 0) L.span[buf] = B + L.bw[wave];
-      uint8_t* st = L.stage[buf] + B;
-#pragma unroll
-      for (int j = 0; j < V; ++j) {
-        const uint32_t wl = (uint32_t)(j * S::WPV + lane / S::LPW);  // window of this lane in the block
-        if (wl < nwin) {
-          // the window's mask sits after the masks and values of the windows before it
-          if (lane % S::LPW == 0) {  // the window's first lane: nothing of the window before it
-            if constexpr (ESZ == 4) *reinterpret_cast<uint32_t*>(st + 4 * wl + ESZ * pre[j]) = msk[j];
-            else lds_u32_at2(st, 4 * wl + ESZ * pre[j], msk[j]);
-          }
-          uint32_t pos = 4 * (wl + 1) + ESZ * pre[j];
-#pragma unroll
-          for (int k = 0; k < S::EPL; ++k) {
-            if ((bits[j] >> k) & 1u) {
-              store_elem<ESZ>(st + pos, vec_elem<ESZ>(cur[j], k));
-              pos += ESZ;
-            }
-          }
-        }
-      }
-      if (tn < full) zvi_c_load_full<ESZ>(nxt, src, tn, wave, lane);
-    }
-  } else {
-    // control wave (see the ZVC compressor)
-    // what this wave issued last iteration (chain round, ticket) must be back
-    // before the hand-over; waiting here on every path keeps the compiler from
-    // waiting again after the ticket drawn next
-    __builtin_amdgcn_s_waitcnt(0);
-    if (lane == 0) L.next = tk.tile(pend);
-    // the next ticket goes out now and has a whole iteration to come back
-    if (lane == 0 && have_cur) pend = tk.raw();
-    if (have_cur) {
+    if (have_t) {  // t's block bases inside its tile
+      const uint32_t bl = lane < S::NW ? L.bw[lane] : 0u;
       const uint32_t vl = lane < S::NW ? L.vw[lane] : 0u;
-      const uint32_t T = read_lane(wave_incl_scan(vl), 63);
-      if (lane == 0) {
-        L.total[buf] = T;
-        agg_publish(agg, t, T);
-      }
+      const uint32_t bi = wave_incl_scan(bl), vi = wave_incl_scan(vl);
+      q.Bb = read_lane(bi - bl, wave);
+      q.Vb = read_lane(vi - vl, wave);
     }
-    if (have_prev) {
-      bool stuck = false;
-      const uint64_t X = pfx + chain_sum(agg, chain_lo, tp, cr, &stuck, [](uint32_t v) { return v; });
-      if (lane == 0) {
-        L.excl = X;
-        if (stuck) atomicMax(reinterpret_cast<unsigned long long*>(out_bytes), kSizeInternalError);
-      }
-      pfx = X + L.total[buf ^ 1];  // tp's inclusive prefix
-    }
-  }
-  __syncthreads();
-
-  if (data) {
-    if (have_prev) {
-      const int pb = buf ^ 1;
+    if (have_p2) {
       const uint64_t X = L.excl;
-      // full tiles only precede tp, so the windows before it are tp * NW * WPB
-      const uint64_t O = H + 4 * ((uint64_t)tp * S::NW * S::WPB) + (uint64_t)ESZ * X;
-      const uint32_t span = L.span[pb];
-      store_staged<ESZ == 4 ? 4 : 2, S::NW * 64>(L.stage[pb], span, O, dst, tid);
-      if (tid < S::NW) {
-        const uint64_t w = (uint64_t)tp * S::NW + tid;
-        if (w < Wr) reinterpret_cast<uint32_t*>(dst)[w] = (uint32_t)(X + L.ivw[pb][tid]);
-      }
-      if (tp == num_tiles - 1 && tid == 0) {
-        reinterpret_cast<uint32_t*>(dst)[Wr] = (uint32_t)(X + L.total[pb]);
+      // full tiles only precede tp2, so the windows before it are tp2 * NW * WPB
+      const uint64_t O = H + 4 * ((uint64_t)tp2 * S::NW * S::WPB) + (uint64_t)ESZ * X;
+      const uint32_t span = L.span2;
+      store_staged<ESZ == 4 ? 4 : 2, S::NW * 64>(L.stage[b], span, O, dst, tid);
+      const uint64_t w = (uint64_t)tp2 * S::NW + wave;
+      if (lane == 0 && w < Wr) reinterpret_cast<uint32_t*>(dst)[w] = (uint32_t)(X + V2b);
+      if (tp2 == num_tiles - 1 && tid == 0) {
+        reinterpret_cast<uint32_t*>(dst)[Wr] = (uint32_t)(X + L.total2);
         atomicMax(reinterpret_cast<unsigned long long*>(out_bytes), O + span);
       }
     }
-  } else if (have_cur) {
-    chain_lo = have_prev ? (uint64_t)tp + 1 : 0;
-    chain_issue(agg, chain_lo, t, cr);
+  } else {
+    // control wave (see rle_c_iteration)
+    __builtin_amdgcn_s_waitcnt(0);
+    if (lane == 0) L.next = tk.tile(C.pend);
+    if (lane == 0 && have_t) C.pend = tk.raw();
+    if (have_t) {
+      const uint32_t vl = lane < S::NW ? L.vw[lane] : 0u;
+      const uint32_t bl = lane < S::NW ? L.bw[lane] : 0u;
+      const uint32_t T = read_lane(wave_incl_scan(vl), 63), B = read_lane(wave_incl_scan(bl), 63);
+      if (lane == 0) {
+        L.total[b] = T;
+        L.span[b] = B;
+        agg_publish(agg, t, T);
+      }
+    }
+    if (have_p1) {
+      C.chain_lo = have_p2 ? (uint64_t)tp2 + 1 : 0;
+      chain_issue(agg, C.chain_lo, tp1, C.cr);
+    }
   }
+  V2b = qp.Vb;
+  __syncthreads();
   return __builtin_amdgcn_readfirstlane(L.next);  // uniform: keeps tile bases in SGPRs
 }
 
@@ -234,33 +277,39 @@ __global__ __launch_bounds__(ZviCShape<ESZ>::BLOCK) void zvci_compress_kernel(
   const Tickets tk = ticket_source(counter, __builtin_amdgcn_readfirstlane(L.mode));
   if (tid < 3 * 64 && lane == 0) L.init[wave] = tk.raw();
   __syncthreads();
+  // raw counter values of the first three tickets in increasing order (a
+  // class's tiles increase with them): classify, load, hand over
   const uint32_t a = __builtin_amdgcn_readfirstlane(L.init[0]);
   const uint32_t b = __builtin_amdgcn_readfirstlane(L.init[1]);
   const uint32_t c = __builtin_amdgcn_readfirstlane(L.init[2]);
-  // raw counter values: a class's tiles increase with them
   const uint32_t lo = min(a, min(b, c)), hi = max(a, max(b, c));
   uint32_t t = tk.tile(lo);
-  uint32_t tn = tk.tile(a + b + c - lo - hi);
-  uint32_t pend = hi;     // control wave: raw value of the ticket to hand over next
-  uint32_t tp = num_tiles;
+  uint32_t tl = tk.tile(a + b + c - lo - hi);
+  uint32_t tp1 = num_tiles, tp2 = num_tiles;
+  RleCtl C;
+  C.chain_lo = 0;
+  C.pfx = 0;
+  C.pend = hi;
+  ZviLane<S::V> qa, qb;
+  qa.nwin = qb.nwin = 0;
+  qa.Bb = qa.Vb = qb.Bb = qb.Vb = 0;
+  uint32_t V2b = 0;
   u32x4 ra[S::V], rb[S::V];
-  ChainRound cr;          // control wave: chain sum in flight
-  uint64_t chain_lo = 0;  // control wave: first tile of that sum
-  uint64_t pfx = 0;       // control wave: inclusive prefix of the last resolved tile
-  if (wave < S::NW && t < full) zvi_c_load_full<ESZ>(ra, src, t, wave, lane);
+  zvi_c_load_full<ESZ>(ra, src, t, __builtin_amdgcn_readfirstlane(wave) < S::NW && t < full, wave, lane);
   for (;;) {
-    uint32_t tnn = zvi_c_iteration<ESZ>(L, ra, rb, cr, chain_lo, pfx, pend, t, tn, tp, 0, full, Wr, src, n, dst,
-                                        out_bytes, agg, tk, num_tiles, tid, wave, lane);
-    if (t >= num_tiles) break;
-    tp = t;
-    t = tn;
-    tn = tnn;
-    tnn = zvi_c_iteration<ESZ>(L, rb, ra, cr, chain_lo, pfx, pend, t, tn, tp, 1, full, Wr, src, n, dst, out_bytes,
-                               agg, tk, num_tiles, tid, wave, lane);
-    if (t >= num_tiles) break;
-    tp = t;
-    t = tn;
-    tn = tnn;
+    uint32_t r = zvi_c_iteration<ESZ>(L, ra, rb, qa, qb, V2b, C, t, tp1, tp2, tl, 0, full, Wr, src, n, dst,
+                                      out_bytes, agg, tk, num_tiles, tid, wave, lane);
+    tp2 = tp1;
+    tp1 = t;
+    t = tl;
+    tl = r;
+    r = zvi_c_iteration<ESZ>(L, rb, ra, qb, qa, V2b, C, t, tp1, tp2, tl, 1, full, Wr, src, n, dst, out_bytes, agg,
+                             tk, num_tiles, tid, wave, lane);
+    tp2 = tp1;
+    tp1 = t;
+    t = tl;
+    tl = r;
+    if (t >= num_tiles && tp1 >= num_tiles && tp2 >= num_tiles) break;
   }
 }
 
