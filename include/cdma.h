@@ -122,7 +122,8 @@ uint64_t cdma_max_compressed_bytes(int algo, int esz, uint64_t n);
  * static or ticketed tiles, eight ticket-class counters, each on a 128-byte
  * line of its own), then one 32-bit published aggregate per compress tile.
  * ZVC decompress reuses the same space for one 32-bit value offset per 16 KB
- * decompress tile and one total per 32 KB of masks.  The library clears what
+ * decompress tile, one total per 32 KB of masks and, for outputs over 1 GiB,
+ * 4 KB of read-ahead counters per 1 GiB chunk.  The library clears what
  * it needs itself at the start of each call (with a kernel, not a memset).
  * Workspaces of calls that may overlap in time must be distinct.  Returns 0
  * for invalid input.
