@@ -34,6 +34,10 @@ __global__ void store_u64_kernel(uint64_t* p, uint64_t v) {
 #define CDMA_AHEAD_GROUPS 2048
 #endif
 constexpr uint32_t kAheadGroups = CDMA_AHEAD_GROUPS;
+// Expand tiles of the previous chunk that follow a chunk's read-ahead group.
+#ifndef CDMA_AHEAD_LEAD
+#define CDMA_AHEAD_LEAD 0
+#endif
 
 // Warm the memory-side cache with the stream (see warm_whole); otherwise
 // return at once.  Launched only when the output is large enough to warm.
@@ -243,7 +247,8 @@ static hipError_t zvc_decompress_t(const void* src, uint64_t cap, const uint64_t
   const uint64_t grid = tiles + (uint64_t)warm * nchunks;
   kern<<<(unsigned)grid, kBlock, pad, s>>>(static_cast<const uint8_t*>(src), cap, src_bytes, n,
                                            static_cast<uint8_t*>(dst), error, local, sup, (uint32_t)tiles,
-                                           warm ? (uint32_t)chunk : (uint32_t)tiles, warm, (uint32_t)window, sync);
+                                           warm ? (uint32_t)chunk : (uint32_t)tiles, warm, (uint32_t)window,
+                                           (uint32_t)(CDMA_AHEAD_LEAD < chunk ? CDMA_AHEAD_LEAD : 0), sync);
   return hipGetLastError();
 }
 

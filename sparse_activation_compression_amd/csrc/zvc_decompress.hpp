@@ -374,14 +374,39 @@ __global__ __launch_bounds__(kBlock) void zvc_expand_kernel(
     const uint8_t* __restrict__ src, uint64_t src_capacity, const uint64_t* __restrict__ src_bytes,
     uint64_t n, uint8_t* __restrict__ dst, uint32_t* __restrict__ error,
     const uint32_t* __restrict__ local, const uint32_t* __restrict__ sup, uint32_t num_tiles,
-    uint32_t chunk_tiles, uint32_t warm_groups, uint32_t wait_window, uint32_t* __restrict__ sync) {
+    uint32_t chunk_tiles, uint32_t warm_groups, uint32_t wait_window, uint32_t lead, uint32_t* __restrict__ sync) {
   __shared__ ZvcExpandLds<ESZ, V> L;
   constexpr int WPT = ZvcShape<ESZ, V>::WPT;
   const int tid = threadIdx.x;
   const int lane = (int)lane_id();
   const int wave = tid >> 6;
-  const uint32_t per = warm_groups + chunk_tiles;  // blocks per chunk
-  const uint32_t c = blockIdx.x / per, r = blockIdx.x % per;
+  // Block order: chunk k's read-ahead group (warm_groups blocks) sits `lead`
+  // expand blocks before chunk k's first expand block (chunk 0's first of
+  // all), so it runs during the tail of chunk k - 1.  Decode this block into
+  // (chunk c, read-ahead index r < warm_groups) or (chunk c, expand index
+  // warm_groups + i within the chunk).
+  uint32_t c = 0, r = blockIdx.x;
+  if (warm_groups) {
+    const uint32_t nch = (num_tiles + chunk_tiles - 1) / chunk_tiles;
+    uint32_t nw = 0;  // read-ahead groups before this block
+    bool warm_block = false;
+    for (uint32_t k = 0; k < nch; ++k) {
+      const uint32_t start = (k ? k * chunk_tiles - lead : 0u) + k * warm_groups;
+      if (blockIdx.x < start) break;
+      if (blockIdx.x < start + warm_groups) {
+        c = k;
+        r = blockIdx.x - start;
+        warm_block = true;
+        break;
+      }
+      nw = k + 1;
+    }
+    if (!warm_block) {
+      const uint32_t e = blockIdx.x - nw * warm_groups;  // expand block in tile order
+      c = e / chunk_tiles;
+      r = warm_groups + e % chunk_tiles;
+    }
+  }
   const uint32_t t0 = c * chunk_tiles;
   const uint32_t t1 = num_tiles - t0 < chunk_tiles ? num_tiles : t0 + chunk_tiles;
   const uint64_t W = (n + 31) / 32;
