@@ -214,12 +214,11 @@ static int expand_lds_pad(const void* kernel, int groups) {
   return pad;
 }
 
-// decompress workspace: local[tiles] then sup[supers + 1]
-template <int ESZ>
-static hipError_t zvc_decompress_t(const void* src, uint64_t cap, const uint64_t* src_bytes, uint64_t n,
-                                   void* dst, uint32_t* error, void* ws, hipStream_t s) {
+template <int ESZ, int KQ>
+static hipError_t zvc_decompress_kq(const void* src, uint64_t cap, const uint64_t* src_bytes, uint64_t n,
+                                    void* dst, uint32_t* error, void* ws, hipStream_t s) {
   constexpr int WPT = ZvcShape<ESZ, kZvcV>::WPT;
-  using C = ZvcScanShape<WPT>;
+  using C = ZvcScanShape<WPT, KQ>;
   const uint64_t tiles = zvc_tiles(ESZ, n);
   const uint64_t supers = (tiles + C::SUPER - 1) / C::SUPER;
   uint32_t* local = static_cast<uint32_t*>(ws);
@@ -235,9 +234,9 @@ static hipError_t zvc_decompress_t(const void* src, uint64_t cap, const uint64_t
   const uint32_t warm = chunk && may_ahead ? kAheadGroups : 0u;
   // read-ahead counters and flags, 128-byte aligned after sup[]
   uint32_t* sync = reinterpret_cast<uint32_t*>((reinterpret_cast<uintptr_t>(sup + supers + 1) + 127) & ~uintptr_t(127));
-  zvc_count_kernel<WPT><<<(unsigned)supers, kBlock, 0, s>>>(static_cast<const uint8_t*>(src), cap, src_bytes,
-                                                                  n, local, sup, error, (uint32_t)tiles,
-                                                                  CDMA_WARM_BYTES > 0);
+  zvc_count_kernel<WPT, KQ><<<(unsigned)supers, kBlock, 0, s>>>(static_cast<const uint8_t*>(src), cap, src_bytes,
+                                                                      n, local, sup, error, (uint32_t)tiles,
+                                                                      CDMA_WARM_BYTES > 0);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   zvc_scan_kernel<<<1, kScanBlock, 0, s>>>(sup, (uint32_t)supers, sync, warm ? (uint32_t)nchunks * kAheadSyncWords : 0u);
   if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -247,9 +246,24 @@ static hipError_t zvc_decompress_t(const void* src, uint64_t cap, const uint64_t
   const uint64_t grid = tiles + (uint64_t)warm * nchunks;
   kern<<<(unsigned)grid, kBlock, pad, s>>>(static_cast<const uint8_t*>(src), cap, src_bytes, n,
                                            static_cast<uint8_t*>(dst), error, local, sup, (uint32_t)tiles,
-                                           warm ? (uint32_t)chunk : (uint32_t)tiles, warm, (uint32_t)window,
+                                           (uint32_t)C::SHIFT, warm ? (uint32_t)chunk : (uint32_t)tiles, warm,
+                                           (uint32_t)window,
                                            (uint32_t)(CDMA_AHEAD_LEAD < chunk ? CDMA_AHEAD_LEAD : 0), sync);
   return hipGetLastError();
+}
+
+// Decode tiles up to which the count pass uses 4 KB super tiles (KQ = 1).
+#ifndef CDMA_SMALL_SUPER_TILES
+#define CDMA_SMALL_SUPER_TILES 16384
+#endif
+
+// decompress workspace: local[tiles], sup[supers + 1], then the read-ahead
+// counters
+template <int ESZ>
+static hipError_t zvc_decompress_t(const void* src, uint64_t cap, const uint64_t* src_bytes, uint64_t n,
+                                   void* dst, uint32_t* error, void* ws, hipStream_t s) {
+  return zvc_tiles(ESZ, n) <= CDMA_SMALL_SUPER_TILES ? zvc_decompress_kq<ESZ, 1>(src, cap, src_bytes, n, dst, error, ws, s)
+                                                      : zvc_decompress_kq<ESZ, 8>(src, cap, src_bytes, n, dst, error, ws, s);
 }
 
 // n = 0: the stream must be empty (ZVC) or the 8-byte zero index (RLE).

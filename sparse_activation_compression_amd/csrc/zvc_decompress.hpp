@@ -30,28 +30,35 @@ namespace cdma {
 // is a small share of the output is read ahead chunk by chunk inside the
 // expand pass (zvc_expand_kernel).
 
-// Super tile of decode tiles with TWPT mask words each: at most 64 tiles and
-// at most 8192 mask words (32 KB).
-template <int TWPT>
+// Super tile of decode tiles with TWPT mask words each: KQ quads of mask
+// words per thread, i.e. KQ * kBlock * 4 words (32 KB for KQ = 8: 64 fp32 or
+// 32 fp16 tiles; 4 KB for KQ = 1: 8 fp32 or 4 fp16 tiles), at most 64 tiles.
+// Small outputs take the small super tile, so the count pass has enough
+// workgroups to fill the GPU (a 148 MB map has 4.6 MB of masks: 142
+// workgroups of 32 KB); large ones the big one, so the one-workgroup scan
+// stays short.  SHIFT = log2(SUPER) is how the other passes find a tile's
+// super tile.
+template <int TWPT, int KQ>
 struct ZvcScanShape {
-  static constexpr int WPT = TWPT;                                  // mask words per decode tile
-  static constexpr int WORDS = 64 * WPT < 8192 ? 64 * WPT : 8192;   // mask words per super tile
-  static constexpr int SUPER = WORDS / WPT;                          // decode tiles per super tile
-  static_assert(SUPER <= 64 && WORDS % WPT == 0 && WORDS % (4 * kBlock) == 0, "super tile shape");
+  static constexpr int WPT = TWPT;                // mask words per decode tile
+  static constexpr int WORDS = KQ * kBlock * 4;   // mask words per super tile
+  static constexpr int SUPER = WORDS / WPT;       // decode tiles per super tile
+  static constexpr int SHIFT = __builtin_ctz(SUPER);
+  static_assert(SUPER <= 64 && WORDS % WPT == 0 && (SUPER & (SUPER - 1)) == 0, "super tile shape");
 };
 
-template <int TWPT>
+template <int TWPT, int KQ_>
 __global__ __launch_bounds__(kBlock) void zvc_count_kernel(
     const uint8_t* __restrict__ src, uint64_t src_capacity, const uint64_t* __restrict__ src_bytes,
     uint64_t n, uint32_t* __restrict__ local, uint32_t* __restrict__ sup, uint32_t* __restrict__ error,
     uint32_t num_tiles, bool warm) {
-  using C = ZvcScanShape<TWPT>;
+  using C = ZvcScanShape<TWPT, KQ_>;
   static_assert(512 % TWPT == 0, "a decode tile is 16 KB: 32 * TWPT elements of 512 / TWPT bytes");
   // Mask quad i of the super tile (16 bytes) is read by thread i % kBlock in
   // step i / kBlock, so each load instruction covers 1 KB of contiguous masks.
   // A decode tile's quads are then an aligned group of QT lanes of one step.
   constexpr int QT = C::WPT / 4;               // mask quads per decode tile
-  constexpr int KQ = C::WORDS / 4 / kBlock;    // steps (quads per thread)
+  constexpr int KQ = KQ_;                       // steps (quads per thread)
   static_assert(QT == 8 || QT == 16 || QT == 32 || QT == 64, "a decode tile's masks are a lane group of quads");
   static_assert(KQ * kBlock * 4 == C::WORDS, "super tile shape");
   __shared__ uint32_t s_cnt[C::SUPER];
@@ -317,14 +324,13 @@ __device__ __forceinline__ uint32_t zvc_expand_tile(ZvcExpandLds<ESZ, V>& L, con
   return total;
 }
 
-// Value offset of tile t (t <= num_tiles) from the two count passes.
-template <int TWPT>
+// Value offset of tile t (t <= num_tiles) from the two count passes, whose
+// super tiles hold 2^shift tiles.
 __device__ __forceinline__ uint32_t zvc_tile_offset(const uint32_t* __restrict__ local,
                                                     const uint32_t* __restrict__ sup, uint32_t t,
-                                                    uint32_t num_tiles) {
-  using C = ZvcScanShape<TWPT>;
-  if (t >= num_tiles) return sup[(num_tiles + C::SUPER - 1) / C::SUPER];  // the grand total
-  return sup[t / C::SUPER] + local[t];
+                                                    uint32_t num_tiles, uint32_t shift) {
+  if (t >= num_tiles) return sup[(num_tiles + (1u << shift) - 1) >> shift];  // the grand total
+  return sup[t >> shift] + local[t];
 }
 
 // Pass 3: one tile per workgroup, no inter-workgroup dependency for
@@ -373,7 +379,7 @@ template <int ESZ, int V>
 __global__ __launch_bounds__(kBlock) void zvc_expand_kernel(
     const uint8_t* __restrict__ src, uint64_t src_capacity, const uint64_t* __restrict__ src_bytes,
     uint64_t n, uint8_t* __restrict__ dst, uint32_t* __restrict__ error,
-    const uint32_t* __restrict__ local, const uint32_t* __restrict__ sup, uint32_t num_tiles,
+    const uint32_t* __restrict__ local, const uint32_t* __restrict__ sup, uint32_t num_tiles, uint32_t super_shift,
     uint32_t chunk_tiles, uint32_t warm_groups, uint32_t wait_window, uint32_t lead, uint32_t* __restrict__ sync) {
   __shared__ ZvcExpandLds<ESZ, V> L;
   constexpr int WPT = ZvcShape<ESZ, V>::WPT;
@@ -415,9 +421,9 @@ __global__ __launch_bounds__(kBlock) void zvc_expand_kernel(
   if (warm_groups && (r < warm_groups || r - warm_groups < wait_window)) {
     uint64_t m0 = 4ull * WPT * t0, m1 = 4ull * WPT * t1;
     if (m1 > 4 * W) m1 = 4 * W;
-    uint64_t v0 = 4 * W + (uint64_t)ESZ * zvc_tile_offset<WPT>(local, sup, t0, num_tiles);
-    uint64_t v1 = 4 * W + (uint64_t)ESZ * zvc_tile_offset<WPT>(local, sup, t1, num_tiles);
-    const uint64_t stream = 4 * W + (uint64_t)ESZ * zvc_tile_offset<WPT>(local, sup, num_tiles, num_tiles);
+    uint64_t v0 = 4 * W + (uint64_t)ESZ * zvc_tile_offset(local, sup, t0, num_tiles, super_shift);
+    uint64_t v1 = 4 * W + (uint64_t)ESZ * zvc_tile_offset(local, sup, t1, num_tiles, super_shift);
+    const uint64_t stream = 4 * W + (uint64_t)ESZ * zvc_tile_offset(local, sup, num_tiles, num_tiles, super_shift);
     if (m1 > eff) m1 = eff;
     if (v1 > eff) v1 = eff;
     if (m0 > m1) m0 = m1;
@@ -460,8 +466,8 @@ __global__ __launch_bounds__(kBlock) void zvc_expand_kernel(
   }
   const uint32_t t = t0 + xcd_tile(r - warm_groups, t1 - t0);  // this workgroup's tile
   ZvcTileIn<ESZ, V> in;
-  zvc_fetch_tile<ESZ, V>(in, src, eff, W, t, zvc_tile_offset<WPT>(local, sup, t, num_tiles),
-                         zvc_tile_offset<WPT>(local, sup, t + 1, num_tiles), tid);
+  zvc_fetch_tile<ESZ, V>(in, src, eff, W, t, zvc_tile_offset(local, sup, t, num_tiles, super_shift),
+                         zvc_tile_offset(local, sup, t + 1, num_tiles, super_shift), tid);
   // E_SIZE with a size word: the masks describe another size, or the size
   // exceeds the readable capacity (bytes past the end read as 0); without
   // one: described values lie past the capacity
