@@ -31,6 +31,8 @@
 //             the same expansion as ZVC.
 #pragma once
 
+#include <type_traits>
+
 #include "zvc_common.hpp"
 
 namespace cdma {
@@ -45,7 +47,12 @@ struct RleShape {
   // largest block of a window that passes every decode check (bound derived
   // below, at the compressor)
   static constexpr int BLKMAX = ESZ == 4 ? 4 * E + 8 : 3 * E + 6;
-  static constexpr int WSTAGE = BLKMAX + 32;       // decompress: one window's block + alignment
+  // decompress: the staged part of one window's block, plus alignment.  A
+  // 32-bit block always fits.  16-bit staging stops at 4448 bytes, so that a
+  // decoder wavefront's LDS stays under 5 KB and 8 wavefronts per SIMD fit;
+  // only blocks of many short runs are longer (random data at half density
+  // averages about 4.1 KB), and their remaining values are read from memory.
+  static constexpr int WSTAGE = ESZ == 4 ? BLKMAX + 32 : 4480;
   static_assert(V * 64 * EPL == E, "a wavefront must cover one window");
 };
 
@@ -505,6 +512,31 @@ __device__ __forceinline__ void stage_pieces(uint8_t* blk, const u32x4* __restri
   }
 }
 
+// Stage stream bytes [beg, end) into blk from the 16-byte piece that holds
+// beg, so that byte beg lands at blk + (beg & 15); bytes at or past eff read
+// as 0.  Returns beg & 15.
+template <int KMAX>
+__device__ __forceinline__ uint32_t stage_span(uint8_t* blk, const uint8_t* __restrict__ src, uint64_t eff,
+                                               uint64_t beg, uint64_t end, uint32_t lane) {
+  const uint32_t shift = (uint32_t)(beg & 15);
+  const uint64_t base = beg - shift;                          // 16-byte aligned
+  const uint32_t nq = (uint32_t)((end - base + 15) >> 4);     // 16-byte pieces to stage
+  const uint64_t whole = eff > base ? (eff - base) >> 4 : 0;  // pieces that end by eff
+  const uint32_t nfull = whole < nq ? (uint32_t)whole : nq;
+  stage_pieces<KMAX>(blk, reinterpret_cast<const u32x4*>(src + base), nfull, lane);
+  for (uint32_t i = nfull + lane; i < nq; i += 64) {  // the readable stream ends inside the span
+    const uint64_t qb = base + 16 * (uint64_t)i;
+    for (int k = 0; k < 16; k += 2) {
+      const uint64_t b = qb + k;
+      uint32_t e = 0;
+      if (b + 2 <= eff) e = *reinterpret_cast<const uint16_t*>(src + b);
+      else if (b < eff) e = src[b];  // the last readable byte; the one after it reads as 0
+      lds_u16(blk, 16 * i + k, e);
+    }
+  }
+  return shift;
+}
+
 // Read a little-endian u32 at stream byte off; bytes at or past eff read as 0.
 __device__ __forceinline__ uint32_t stream_u32(const uint8_t* __restrict__ src, uint64_t eff, uint64_t off) {
   if (off + 4 <= eff && (off & 3) == 0) return *reinterpret_cast<const uint32_t*>(src + off);
@@ -567,7 +599,7 @@ __global__ __launch_bounds__(kRleDecBlock) void rle_decompress_kernel(
   // this wave's block: lanes 0-3 read run_off[gw], run_off[gw+1], val_off[gw]
   // and val_off[gw+1]
   bool valid = false;
-  uint32_t p = 0, nv = 0, nvs = 0;
+  uint32_t p = 0, nv = 0, nvb = 0, nvs = 0;
   uint64_t B = 0;
   if (Lw) {
     uint32_t iw = 0;
@@ -583,48 +615,27 @@ __global__ __launch_bounds__(kRleDecBlock) void rle_decompress_kernel(
         err |= CDMA_E_RUN_FORM;
       } else {
         valid = true;
-        // Stage every run entry (2p <= 2E + 4 < BLKMAX) and as many values as
-        // fit in BLKMAX.  A block that passes every check is at most BLKMAX
-        // bytes, so a longer one is corrupt and reported through the checks,
-        // which read run entries only; its output is unspecified anyway.
+        // The block's values are the first min(nv, Lw, (BLKMAX - 2p) / ESZ):
+        // a block that passes every check is at most BLKMAX bytes, so a
+        // longer one is corrupt and reported through the checks, which read
+        // run entries only; its output is unspecified anyway.  Every run
+        // entry is staged (2p <= 2E + 4 < WSTAGE - 32) and as many of the
+        // values as fit in WSTAGE - 32 bytes; the rest are read from memory.
         const uint32_t room = ((uint32_t)S::BLKMAX - 2 * p) / ESZ;
-        nvs = nv < Lw ? nv : Lw;
-        nvs = nvs < room ? nvs : room;
+        nvb = nv < Lw ? nv : Lw;
+        nvb = nvb < room ? nvb : room;
+        const uint32_t sroom = ((uint32_t)S::WSTAGE - 32 - 2 * p) / ESZ;
+        nvs = ESZ == 4 || nvb < sroom ? nvb : sroom;
         B = H + 2 * (uint64_t)r0 + (uint64_t)ESZ * v0;
+        // no size word: the block runs past the readable capacity
+        if (!src_bytes && B + 2 * (uint64_t)p + (uint64_t)ESZ * nvb > eff) err |= CDMA_E_SIZE;
       }
     }
   }
   uint8_t* blk = s_blk[wave];
+  constexpr int KST = (S::WSTAGE + 1023) / 1024;  // pieces per lane at most: a span is < WSTAGE bytes
   uint32_t shift = 0;
-  if (valid) {
-    const uint64_t beg = B, end = B + 2 * (uint64_t)p + (uint64_t)ESZ * nvs;
-    shift = (uint32_t)(beg & 15);
-    const uint64_t base = beg - shift;                          // 16-byte aligned
-    const uint32_t nq = (uint32_t)((end - base + 15) >> 4);     // 16-byte pieces to stage
-    const uint64_t whole = eff > base ? (eff - base) >> 4 : 0;  // pieces that end by eff
-    const uint32_t nfull = whole < nq ? (uint32_t)whole : nq;
-    const u32x4* g = reinterpret_cast<const u32x4*>(src + base);
-    // pieces per lane at most: nq * 16 <= S::WSTAGE
-    stage_pieces<(S::WSTAGE + 1023) / 1024>(blk, g, nfull, (uint32_t)lane);
-    if (nfull < nq) {  // the readable stream ends inside the block: bytes past it read as 0
-      bool short_read = false;
-      for (uint32_t i = nfull + (uint32_t)lane; i < nq; i += 64) {
-        const uint64_t qb = base + 16 * (uint64_t)i;
-        for (int k = 0; k < 16; k += 2) {
-          const uint64_t b = qb + k;
-          uint32_t e = 0;
-          if (b + 2 <= eff) {
-            e = *reinterpret_cast<const uint16_t*>(src + b);
-          } else {
-            if (b < eff) e = src[b];  // the last readable byte; the one after it reads as 0
-            if (b >= beg && b < end) short_read = true;
-          }
-          lds_u16(blk, 16 * i + k, e);
-        }
-      }
-      if (!src_bytes && __ballot(short_read)) err |= CDMA_E_SIZE;  // no size word: data past capacity
-    }
-  }
+  if (valid) shift = stage_span<KST>(blk, src, eff, B, B + 2 * (uint64_t)p + (uint64_t)ESZ * nvs, (uint32_t)lane);
   // each wave only touches its own block and its own part of the bitmap
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -725,6 +736,18 @@ __global__ __launch_bounds__(kRleDecBlock) void rle_decompress_kernel(
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
+  // A 16-bit block longer than the stage: once the run entries are read, its
+  // remaining values are staged from the start of the buffer.  They are
+  // ESZ * (nvb - nvs) < E * ESZ - (WSTAGE - 32) + 2p + ESZ bytes, which with
+  // their alignment end before the first staged value at shift + 2p.
+  uint32_t tshift = 0;
+  if constexpr (ESZ == 2) {
+    static_assert(S::WSTAGE - 32 >= S::E * ESZ + 32, "the tail must end before the staged values");
+    if (nvb > nvs) {
+      const uint64_t tb = B + 2 * (uint64_t)p + (uint64_t)ESZ * nvs;
+      tshift = stage_span<KST>(blk, src, eff, tb, tb + (uint64_t)ESZ * (nvb - nvs), (uint32_t)lane);
+    }
+  }
   // boundaries -> nonzero bitmap (prefix XOR across the window), and the
   // nonzeros before each mask word (wave prefix sum of its popcounts)
   if (!zero_win) {
@@ -763,24 +786,34 @@ __global__ __launch_bounds__(kRleDecBlock) void rle_decompress_kernel(
       else store_vec<ESZ>(dst, e_win + (uint64_t)c * S::EPL, n, z);
     }
   } else {
+    // tail: the window's values are in two staged pieces (uniform per wave)
+    auto expand = [&](auto tail) {
 #pragma unroll
-    for (int j = 0; j < V; ++j) {
-      const uint32_t c = (uint32_t)(j * 64 + lane);
-      const uint2 m = map[c / S::LPW];
-      const uint32_t sh = (c % S::LPW) * S::EPL;
-      const uint32_t b = (m.x >> sh) & ((1u << S::EPL) - 1);
-      uint32_t q = m.y + (uint32_t)__builtin_popcount(m.x & ((1u << sh) - 1));
-      u32x4 o = {0u, 0u, 0u, 0u};
+      for (int j = 0; j < V; ++j) {
+        const uint32_t c = (uint32_t)(j * 64 + lane);
+        const uint2 m = map[c / S::LPW];
+        const uint32_t sh = (c % S::LPW) * S::EPL;
+        const uint32_t b = (m.x >> sh) & ((1u << S::EPL) - 1);
+        uint32_t q = m.y + (uint32_t)__builtin_popcount(m.x & ((1u << sh) - 1));
+        u32x4 o = {0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int k = 0; k < S::EPL; ++k) {
-        if ((b >> k) & 1u) {
-          if (q < nvs) vec_set<ESZ>(o, k, load_elem<ESZ>(blk + vals + ESZ * q));
-          ++q;
+        for (int k = 0; k < S::EPL; ++k) {
+          if ((b >> k) & 1u) {
+            if constexpr (decltype(tail)::value) {
+              const uint32_t a = q < nvs ? vals + ESZ * q : tshift + ESZ * (q - nvs);
+              if (q < nvb) vec_set<ESZ>(o, k, load_elem<ESZ>(blk + a));
+            } else {
+              if (q < nvs) vec_set<ESZ>(o, k, load_elem<ESZ>(blk + vals + ESZ * q));
+            }
+            ++q;
+          }
         }
+        if (full) st_stream(reinterpret_cast<u32x4*>(dst + (e_win + (uint64_t)c * S::EPL) * ESZ), o);
+        else if (Lw) store_vec<ESZ>(dst, e_win + (uint64_t)c * S::EPL, n, o);
       }
-      if (full) st_stream(reinterpret_cast<u32x4*>(dst + (e_win + (uint64_t)c * S::EPL) * ESZ), o);
-      else if (Lw) store_vec<ESZ>(dst, e_win + (uint64_t)c * S::EPL, n, o);
-    }
+    };
+    if (ESZ == 2 && nvb > nvs) expand(std::true_type{});
+    else expand(std::false_type{});
   }
 
   if (err) atomicOr(&s_err, err);

@@ -154,6 +154,33 @@ def test_largest_blocks(esz):
             _check(x, esz)
 
 
+@pytest.mark.parametrize("esz", [4, 2])
+def test_largest_blocks_cut_in_their_values(esz):
+    """Windows of the most run entries, with the stream cut inside the values
+    at their end: 16-bit blocks this long are staged only in part and the rest
+    of their values come from memory, where bytes past the readable capacity
+    must read and report as they do for staged bytes."""
+    device()
+    e = E[esz]
+    n = 2 * e
+    x = np.zeros(n, dtype=np.uint32 if esz == 4 else np.uint16)
+    x[1::2] = random_patterns(e, esz, 1.0, seed=41)
+    s = oracle.rle_compress(x)
+    for exact in (True, False):
+        out, err = gpu_decompress(s, n, esz, "rle", exact_size=exact, capacity_pad=0 if exact else 64)
+        assert err == 0 and np.array_equal(out, x), exact
+    # with or without a size word, a cut stream reports E_SIZE only, and the
+    # bytes that are missing read as 0 in both decoders
+    for cut in (1, 2, 3, esz + 1, 200, 999):
+        c = s[:-cut]
+        want_out, want = oracle.rle_decompress(c, n, esz)
+        assert want == oracle.E_SIZE, cut
+        for exact in (True, False):
+            out, got = gpu_decompress(c, n, esz, "rle", exact_size=exact)
+            assert got == want, (cut, exact, got, want)
+            assert np.array_equal(out, want_out), (cut, exact)
+
+
 def _one_window_stream(esz, runs, nv, seed):
     """A hand-built one-window RLE stream: index, the given run entries, then
     nv random nonzero values (the index claims nv values)."""
