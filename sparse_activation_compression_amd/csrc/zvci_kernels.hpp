@@ -337,7 +337,7 @@ __global__ __launch_bounds__(kBlock) void zvci_decompress_kernel(
   constexpr int WSTAGE = S::BLKMAX + 32;
   __shared__ uint32_t s_err;
   __shared__ uint32_t s_mask[kWaves][S::WPB];  // each window's mask (bits past n cleared)
-  __shared__ uint32_t s_vpos[kWaves][S::WPB];  // staged byte of each window's first value
+  __shared__ uint32_t s_vpos[kWaves][S::WPB];  // staged byte of each window's mask
   __shared__ __attribute__((aligned(16))) uint8_t s_blk[kWaves][WSTAGE];
   __shared__ uint32_t s_span[kWaves], s_shift[kWaves], s_nv[kWaves], s_valid[kWaves];  // for the walk
   __shared__ uint32_t s_zero[kWaves];  // block known to hold only zero masks: no walk
@@ -432,7 +432,7 @@ __global__ __launch_bounds__(kBlock) void zvci_decompress_kernel(
     zero_blk = __ballot(m != 0) == 0;
     if (zero_blk && (uint32_t)lane < nwin) {
       s_mask[wave][lane] = 0;
-      s_vpos[wave][lane] = q + 4;
+      s_vpos[wave][lane] = q;
     }
   }
   if (lane == 0) {
@@ -456,7 +456,30 @@ __global__ __launch_bounds__(kBlock) void zvci_decompress_kernel(
   constexpr uint64_t kPct = ESZ == 4 ? CDMA_ZVCI_SHARED_PCT : CDMA_ZVCI_SHARED_PCT16;
   const bool shared_walk = (uint64_t)tot * 100 < kPct * kWaves * S::E;
   const int b = shared_walk ? lane : wave;
-  if (shared_walk ? (wave == 0 && lane < kWaves) : true) {
+  // every block of the tile holds E elements (all tiles but the last)
+  const bool full_tile = (uint64_t)(t + 1) * kWaves * S::E <= n;
+  if (full_tile) {
+    // Straight-line steps: a mask that starts past the span reads as 0, and
+    // the value count is read off the final position.  Each step adds at
+    // most 4 + 32 ESZ bytes, so window w's mask lies below
+    // w (4 + 32 ESZ) + 4 <= BLKMAX: every read stays in the stage.
+    if (shared_walk ? (wave == 0 && lane < kWaves) : lane == 0) {
+      if (s_valid[b] && !s_zero[b]) {
+        const uint32_t spb = s_span[b];
+        const uint8_t* base = s_blk[b] + s_shift[b];
+        uint32_t p = 0;
+#pragma unroll 4
+        for (uint32_t w = 0; w < (uint32_t)S::WPB; ++w) {
+          uint32_t m = ESZ == 4 ? *reinterpret_cast<const uint32_t*>(base + p) : lds_get_u32_at2(base, p);
+          m = p + 4 <= spb ? m : 0u;
+          s_mask[b][w] = m;
+          s_vpos[b][w] = p;
+          p += 4 + ESZ * (uint32_t)__builtin_popcount(m);
+        }
+        if ((p - 4 * (uint32_t)S::WPB) / ESZ != s_nv[b]) err |= CDMA_E_VAL_COUNT;
+      }
+    }
+  } else if (shared_walk ? (wave == 0 && lane < kWaves) : true) {
     if (s_valid[b] && !s_zero[b]) {
       const bool writer = shared_walk || lane == 0;
       const uint64_t gb = (uint64_t)t * kWaves + b;
@@ -481,7 +504,7 @@ __global__ __launch_bounds__(kBlock) void zvci_decompress_kernel(
         }
         if (writer) {
           s_mask[b][w] = m;
-          s_vpos[b][w] = p + 4;
+          s_vpos[b][w] = p;
         }
         p += 4 + ESZ * (uint32_t)__builtin_popcount(m);
       }
@@ -491,6 +514,30 @@ __global__ __launch_bounds__(kBlock) void zvci_decompress_kernel(
   __syncthreads();
 
   // expand
+  if (full_tile && valid) {
+    // Straight-line: every element reads the value its bit would take and
+    // keeps it only if the bit is set.  Without an error, every set bit's
+    // value lies in the span; with one, the output is unspecified, and the
+    // reads stay below the window's mask position + 4 + 32 ESZ <= BLKMAX.
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      const uint32_t wl = (uint32_t)(j * S::WPV + lane / S::LPW);
+      const uint32_t c = (uint32_t)(j * 64 + lane);
+      const uint32_t m = s_mask[wave][wl];
+      const uint32_t sub = (lane % S::LPW) * S::EPL;
+      const uint32_t bits = __builtin_amdgcn_ubfe(m, sub, S::EPL);
+      const uint8_t* q =
+          blk + shift + s_vpos[wave][wl] + 4 + ESZ * (uint32_t)__builtin_popcount(__builtin_amdgcn_ubfe(m, 0, sub));
+      u32x4 o = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int e = 0; e < S::EPL; ++e) {
+        const int32_t keep = __builtin_amdgcn_sbfe((int32_t)bits, e, 1);  // 0 or -1
+        vec_set<ESZ>(o, e, load_elem<ESZ>(q) & (uint32_t)keep);
+        q -= ESZ * keep;
+      }
+      st_stream(reinterpret_cast<u32x4*>(dst + (e_win + (uint64_t)c * S::EPL) * ESZ), o);
+    }
+  } else {
 #pragma unroll
   for (int j = 0; j < V; ++j) {
     const uint32_t wl = (uint32_t)(j * S::WPV + lane / S::LPW);
@@ -500,7 +547,7 @@ __global__ __launch_bounds__(kBlock) void zvci_decompress_kernel(
       const uint32_t m = s_mask[wave][wl];
       const uint32_t sub = (lane % S::LPW) * S::EPL;
       const uint32_t b = (m >> sub) & ((1u << S::EPL) - 1u);
-      uint32_t at = s_vpos[wave][wl] + ESZ * (uint32_t)__builtin_popcount(m & ((1u << sub) - 1u));
+      uint32_t at = s_vpos[wave][wl] + 4 + ESZ * (uint32_t)__builtin_popcount(m & ((1u << sub) - 1u));
 #pragma unroll
       for (int k = 0; k < S::EPL; ++k) {
         if ((b >> k) & 1u) {
@@ -511,6 +558,7 @@ __global__ __launch_bounds__(kBlock) void zvci_decompress_kernel(
     }
     if (Lw == (uint32_t)S::E) st_stream(reinterpret_cast<u32x4*>(dst + (e_win + (uint64_t)c * S::EPL) * ESZ), o);
     else if (Lw) store_vec<ESZ>(dst, e_win + (uint64_t)c * S::EPL, n, o);
+  }
   }
 
   if (err) atomicOr(&s_err, err);
