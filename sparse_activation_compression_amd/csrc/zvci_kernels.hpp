@@ -459,24 +459,26 @@ __global__ __launch_bounds__(kBlock) void zvci_decompress_kernel(
   // every block of the tile holds E elements (all tiles but the last)
   const bool full_tile = (uint64_t)(t + 1) * kWaves * S::E <= n;
   if (full_tile) {
-    // Straight-line steps: a mask that starts past the span reads as 0, and
-    // the value count is read off the final position.  Each step adds at
-    // most 4 + 32 ESZ bytes, so window w's mask lies below
-    // w (4 + 32 ESZ) + 4 <= BLKMAX: every read stays in the stage.
+    // Straight-line steps, two dependent ALU operations each: the value
+    // count is read off the final position.  Masks are read where the chain
+    // puts them, also past the span: the first mask that starts past it
+    // follows more values than the index claims (4(w + 1) + ESZ C > span
+    // = 4 WPB + ESZ nv gives C > nv), so the count check fails then, as it
+    // does when such masks read as 0.  Each step adds at most 4 + 32 ESZ
+    // bytes, so window w's mask lies below w (4 + 32 ESZ) + 4 <= BLKMAX:
+    // every read stays in the stage.
     if (shared_walk ? (wave == 0 && lane < kWaves) : lane == 0) {
       if (s_valid[b] && !s_zero[b]) {
-        const uint32_t spb = s_span[b];
         const uint8_t* base = s_blk[b] + s_shift[b];
-        uint32_t p = 0;
+        const uint8_t* q = base;  // the chain runs on the LDS address itself
 #pragma unroll 4
         for (uint32_t w = 0; w < (uint32_t)S::WPB; ++w) {
-          uint32_t m = ESZ == 4 ? *reinterpret_cast<const uint32_t*>(base + p) : lds_get_u32_at2(base, p);
-          m = p + 4 <= spb ? m : 0u;
+          const uint32_t m = ESZ == 4 ? *reinterpret_cast<const uint32_t*>(q) : lds_get_u32_at2(q, 0);
           s_mask[b][w] = m;
-          s_vpos[b][w] = p;
-          p += 4 + ESZ * (uint32_t)__builtin_popcount(m);
+          s_vpos[b][w] = (uint32_t)(q - base);
+          q += ESZ * ((uint32_t)__builtin_popcount(m) + 4 / ESZ);
         }
-        if ((p - 4 * (uint32_t)S::WPB) / ESZ != s_nv[b]) err |= CDMA_E_VAL_COUNT;
+        if (((uint32_t)(q - base) - 4 * (uint32_t)S::WPB) / ESZ != s_nv[b]) err |= CDMA_E_VAL_COUNT;
       }
     }
   } else if (shared_walk ? (wave == 0 && lane < kWaves) : true) {
