@@ -796,16 +796,29 @@ __global__ __launch_bounds__(kRleDecBlock) void rle_decompress_kernel(
         const uint32_t b = (m.x >> sh) & ((1u << S::EPL) - 1);
         uint32_t q = m.y + (uint32_t)__builtin_popcount(m.x & ((1u << sh) - 1));
         u32x4 o = {0u, 0u, 0u, 0u};
+        if constexpr (decltype(tail)::value) {
 #pragma unroll
-        for (int k = 0; k < S::EPL; ++k) {
-          if ((b >> k) & 1u) {
-            if constexpr (decltype(tail)::value) {
+          for (int k = 0; k < S::EPL; ++k) {
+            if ((b >> k) & 1u) {
               const uint32_t a = q < nvs ? vals + ESZ * q : tshift + ESZ * (q - nvs);
               if (q < nvb) vec_set<ESZ>(o, k, load_elem<ESZ>(blk + a));
-            } else {
-              if (q < nvs) vec_set<ESZ>(o, k, load_elem<ESZ>(blk + vals + ESZ * q));
+              ++q;
             }
-            ++q;
+          }
+        } else {
+          // Straight-line: every element reads the value its bit would take
+          // and keeps it only if the bit is set.  In a window without an
+          // error every set bit's value is staged (the bitmap holds nv
+          // bits); otherwise the output is unspecified and the base is
+          // clamped so that the reads stay in the stage.
+          uint32_t off = vals + ESZ * q;
+          off = off < (uint32_t)(S::WSTAGE - ESZ * S::EPL) ? off : (uint32_t)(S::WSTAGE - ESZ * S::EPL);
+          const uint8_t* pv = blk + off;
+#pragma unroll
+          for (int k = 0; k < S::EPL; ++k) {
+            const int32_t keep = __builtin_amdgcn_sbfe((int32_t)b, k, 1);  // 0 or -1
+            vec_set<ESZ>(o, k, load_elem<ESZ>(pv) & (uint32_t)keep);
+            pv -= ESZ * keep;
           }
         }
         if (full) st_stream(reinterpret_cast<u32x4*>(dst + (e_win + (uint64_t)c * S::EPL) * ESZ), o);
