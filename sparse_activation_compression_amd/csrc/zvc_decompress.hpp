@@ -301,22 +301,22 @@ __device__ __forceinline__ uint32_t zvc_expand_tile(ZvcExpandLds<ESZ, V>& L, con
   __syncthreads();
   uint32_t base[V];
   const uint32_t total = segment_bases<V>(L.tot, wave, base);
-  // values the offsets give this tile (never more than a tile holds)
-  const uint64_t span = (in.end - in.beg) / ESZ;
-  const uint32_t avail = span < (uint64_t)S::TE ? (uint32_t)span : (uint32_t)S::TE;
+  // The offsets come from the same masks, so the tile's values are exactly
+  // its set bits and every bit's value is staged.  Straight-line: every
+  // element reads the value its bit would take (at most value index TE,
+  // inside the stage) and keeps it only if the bit is set.
   const uint32_t shift = (uint32_t)(in.beg & 15);
   const uint64_t e_tile = (uint64_t)t * S::TE;
 #pragma unroll
   for (int j = 0; j < V; ++j) {
     const uint32_t c = (uint32_t)((wave * V + j) * 64 + lane);
-    uint32_t r = base[j] + ex[j];
+    const uint8_t* pv = L.stage + shift + ESZ * (base[j] + ex[j]);
     u32x4 o = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int k = 0; k < S::EPL; ++k) {
-      if ((bits[j] >> k) & 1u) {
-        if (r < avail) vec_set<ESZ>(o, k, load_elem<ESZ>(L.stage + shift + ESZ * r));
-        ++r;
-      }
+      const int32_t keep = __builtin_amdgcn_sbfe((int32_t)bits[j], k, 1);  // 0 or -1
+      vec_set<ESZ>(o, k, load_elem<ESZ>(pv) & (uint32_t)keep);
+      pv -= ESZ * keep;
     }
     store_vec<ESZ>(dst, e_tile + (uint64_t)c * S::EPL, n, o);
   }
