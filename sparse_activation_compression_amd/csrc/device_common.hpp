@@ -326,13 +326,34 @@ __device__ __forceinline__ Tickets ticket_source(uint32_t* counter, uint32_t mod
 // (issued from lo).  Unpublished words are read again until they appear;
 // further rounds are issued as needed.  Uniform result; *stuck is set (and the
 // result meaningless) if the spin bound was hit.  Called by a whole wave.
-template <typename Dec>
+template <bool kFirstRoundApart = false, typename Dec>
 __device__ __forceinline__ uint64_t chain_sum(const uint32_t* agg, uint64_t lo, uint64_t hi, ChainRound& r,
                                               bool* stuck, Dec dec) {
   const uint32_t lane = lane_id();
   *stuck = false;
   uint64_t sum = 0, base = lo;
   uint32_t spins = 0;
+  // Optionally the first round's check comes before the loop, where it
+  // waits only for the round's own loads and what precedes them (the loop's
+  // reloads make the compiler wait for every memory operation of the wave).
+  if constexpr (kFirstRoundApart) {
+    bool missing = false;
+#pragma unroll
+    for (int k = 0; k < kChainK; ++k) {
+      if constexpr (CDMA_CHAIN_LAZY)
+        if (base + (uint64_t)(k * 64) + lane >= hi) r.w[k] = 1u;
+      missing |= r.w[k] == 0;
+    }
+    if (!__ballot(missing)) {
+      uint64_t part = 0;
+#pragma unroll
+      for (int k = 0; k < kChainK; ++k) part += dec(r.w[k] - 1);
+      sum += wave_sum_u64(part);
+      base += 64 * kChainK;
+      if (base >= hi) return sum;
+      chain_issue(agg, base, hi, r);
+    }
+  }
   for (;;) {
     bool missing = false;
 #pragma unroll

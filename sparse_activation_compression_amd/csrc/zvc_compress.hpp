@@ -43,15 +43,23 @@ namespace cdma {
 //   B1
 //   phase Y  data waves:   segment bases of t_i; store t_{i-2}'s staged
 //                          values from stage[b]
-//            control wave: publish t_i's aggregate, hand the data waves the
-//                          tile they load next iteration (drawing a ticket
-//                          when tiles are not static), store t_i's masks,
-//                          issue the first round of t_{i-1}'s chain sum
+//            control wave: hand the data waves the tile they load next
+//                          iteration (drawing a ticket when tiles are not
+//                          static), issue the first round of t_{i-1}'s chain
+//                          sum, publish t_i's aggregate, store t_i's masks
+//                          (16-bit elements: publish and masks first)
 //   B2
 // The loads of t_{i+1} are issued by every wave on every path (the control
 // wave's and a missing tile's cover no bytes), so the compiler sees the same
 // loads after the other register set on every path and waits only for that
-// set when it classifies.
+// set when it classifies.  For the same reason the control wave's aggregate
+// and mask stores come after its chain loads and are a fixed number of buffer
+// stores: memory operations retire in issue order, and a chain sum that
+// waited for them as well (its round's loads behind the stores) took a store's
+// latency every iteration (fp32, 4 GiB: 71.3 against 68.0 % of 8 TB/s at
+// s = 0.99, 74.8 against 69.7 % at s = 1).  With 16-bit elements the
+// masks' four quads per lane would not fit in registers beside the chain
+// words, so that order is kept for 32-bit elements.
 // The size is reported with 64-bit atomic max operations on a word cleared
 // before the launch: the last tile writes the stream size and a control wave
 // whose chain sum hit the spin bound writes the all-ones error value, which
@@ -272,6 +280,29 @@ __device__ __forceinline__ void zvc_c_store_masks(const ZvcCLds<ESZ>& L, uint8_t
   }
 }
 
+// The same for a full tile (every mask word below W), with a fixed number of
+// 16-byte buffer stores per lane whatever the tile: lanes past the tile's
+// quads, and every lane when !valid, store out of range (dropped).  A fixed
+// count lets the compiler wait for loads issued before these stores without
+// waiting for the stores.
+template <int ESZ>
+__device__ __forceinline__ void zvc_c_store_masks_full(const ZvcCLds<ESZ>& L, uint8_t* __restrict__ dst, uint32_t t,
+                                                       bool valid, int lane) {
+  using S = ZvcCShape<ESZ>;
+  constexpr int KQ = (S::WPT / 4 + 63) / 64;  // mask quads per lane
+  uint8_t* out = dst + (uint64_t)t * S::WPT * 4;
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(out, (short)0, valid ? S::WPT * 4 : 0, kBufferFlags);
+#pragma unroll
+  for (int k = 0; k < KQ; ++k) {
+    const int q = k * 64 + lane;
+    const int qc = q < S::WPT / 4 ? q : 0;
+    const u32x4 m = *reinterpret_cast<const u32x4*>(&L.mask[4 * qc]);
+    __builtin_amdgcn_raw_buffer_store_b128(m, r, q < S::WPT / 4 ? (uint32_t)(16 * q) : (uint32_t)(S::WPT * 4), 0,
+                                           CDMA_NT_STORE ? 2 : 0);
+  }
+}
+
 // Per-iteration state of the control wave.
 struct ZvcCtl {
   ChainRound cr;      // first round of the pending chain sum (issued last iteration)
@@ -317,7 +348,7 @@ __device__ __forceinline__ uint32_t zvc_c_iteration(
     }
   } else if (have_p2) {
     bool stuck = false;
-    const uint64_t X = C.P + chain_sum(agg, C.chain_lo, tp2, C.cr, &stuck, [](uint32_t v) { return v; });
+    const uint64_t X = C.P + chain_sum<ESZ == 4>(agg, C.chain_lo, tp2, C.cr, &stuck, [](uint32_t v) { return v; });
     if (lane == 0) {
       L.excl = X;
       if (stuck) atomicMax(reinterpret_cast<unsigned long long*>(out_bytes), kSizeInternalError);
@@ -348,8 +379,10 @@ __device__ __forceinline__ uint32_t zvc_c_iteration(
     // control wave
     if (have_t) Tn = read_lane(wave_incl_scan(lane < S::SEG ? L.tot[lane] : 0u), 63);
     if (stat) {
-      // every other workgroup's chain sums may be waiting for t's aggregate
-      if (have_t && lane == 0) agg_publish(agg, t, Tn);
+      if constexpr (ESZ == 2) {
+        // every other workgroup's chain sums may be waiting for t's aggregate
+        if (have_t && lane == 0) agg_publish(agg, t, Tn);
+      }
       if (lane == 0) L.next = C.pend;
       if (have_t) C.pend += gridDim.x;
     } else {
@@ -358,18 +391,38 @@ __device__ __forceinline__ uint32_t zvc_c_iteration(
       // after the ticket drawn next
       __builtin_amdgcn_s_waitcnt(0);
       if (lane == 0) L.next = C.pend;
+      // the next ticket goes out now and has a whole iteration to come back
       if (have_t && lane == 0) {
-        // the next ticket goes out now and has a whole iteration to come back
         C.pend = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        agg_publish(agg, t, Tn);
+        if constexpr (ESZ == 2) agg_publish(agg, t, Tn);
       }
     }
-    if (have_t) zvc_c_store_masks<ESZ>(L, dst, t, W, lane);
-    if (have_p1) {
-      // tp1's chain sum: the tiles between this workgroup's tile before it
-      // (tp2) and tp1; summed at the start of the next iteration
-      C.chain_lo = have_p2 ? (uint64_t)tp2 + 1 : 0;
-      chain_issue(agg, C.chain_lo, tp1, C.cr);
+    if constexpr (ESZ == 4) {
+      // The chain loads go out before t's aggregate and masks, which are a
+      // fixed count of stores, so the chain sum of the next iteration waits
+      // only for its loads (memory operations retire in order).  The
+      // partial tile's masks go out before the chain loads.
+      if (have_t && t >= full) zvc_c_store_masks<ESZ>(L, dst, t, W, lane);
+      if (have_p1) {
+        // tp1's chain sum: the tiles between this workgroup's tile before it
+        // (tp2) and tp1; summed at the start of the next iteration
+        C.chain_lo = have_p2 ? (uint64_t)tp2 + 1 : 0;
+        chain_issue(agg, C.chain_lo, tp1, C.cr);
+      }
+      // t's aggregate (lane 0; other workgroups' chain sums may be waiting
+      // for it): a buffer store with the agent-scope policy of agg_publish,
+      // out of range on the other lanes and when there is no t
+      const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(agg, (short)0, num_tiles * 4, kBufferFlags);
+      __builtin_amdgcn_raw_buffer_store_b32(Tn + 1, ra, lane == 0 ? 4 * t : 4 * num_tiles, 0, 16 /* sc1 */);
+      zvc_c_store_masks_full<ESZ>(L, dst, t, have_t && t < full, lane);
+    } else {
+      // 16-bit elements: the two extra quads of masks per lane would not fit
+      // in registers beside the chain words (they spilled)
+      if (have_t) zvc_c_store_masks<ESZ>(L, dst, t, W, lane);
+      if (have_p1) {
+        C.chain_lo = have_p2 ? (uint64_t)tp2 + 1 : 0;
+        chain_issue(agg, C.chain_lo, tp1, C.cr);
+      }
     }
   }
   T2 = T1;
