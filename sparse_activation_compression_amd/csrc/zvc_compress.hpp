@@ -47,7 +47,8 @@ namespace cdma {
 //                          iteration (drawing a ticket when tiles are not
 //                          static), issue the first round of t_{i-1}'s chain
 //                          sum, publish t_i's aggregate, store t_i's masks
-//                          (16-bit elements: publish and masks first)
+//                          (16-bit elements and the fused epilogue:
+//                          publish and masks first)
 //   B2
 // The loads of t_{i+1} are issued by every wave on every path (the control
 // wave's and a missing tile's cover no bytes), so the compiler sees the same
@@ -326,6 +327,11 @@ __device__ __forceinline__ uint32_t zvc_c_iteration(
     int tid, int wave, int lane, bool stat) {
   using S = ZvcCShape<ESZ>;
   constexpr int V = S::V;
+  // The control wave's stores after its chain loads (see the top of this
+  // file): the plain 32-bit compressor only.  The 16-bit kernel has no
+  // registers for it, and the fused epilogue (ticket tiles, whose draw comes
+  // before the chain loads anyway) measured 2 % slower with it.
+  constexpr bool kLateStores = ESZ == 4 && OP == kOpNone;
   const bool have_t = t < num_tiles;
   const bool have_p1 = tp1 < num_tiles;
   const bool have_p2 = tp2 < num_tiles;
@@ -348,7 +354,7 @@ __device__ __forceinline__ uint32_t zvc_c_iteration(
     }
   } else if (have_p2) {
     bool stuck = false;
-    const uint64_t X = C.P + chain_sum<ESZ == 4>(agg, C.chain_lo, tp2, C.cr, &stuck, [](uint32_t v) { return v; });
+    const uint64_t X = C.P + chain_sum<kLateStores>(agg, C.chain_lo, tp2, C.cr, &stuck, [](uint32_t v) { return v; });
     if (lane == 0) {
       L.excl = X;
       if (stuck) atomicMax(reinterpret_cast<unsigned long long*>(out_bytes), kSizeInternalError);
@@ -379,7 +385,7 @@ __device__ __forceinline__ uint32_t zvc_c_iteration(
     // control wave
     if (have_t) Tn = read_lane(wave_incl_scan(lane < S::SEG ? L.tot[lane] : 0u), 63);
     if (stat) {
-      if constexpr (ESZ == 2) {
+      if constexpr (!kLateStores) {
         // every other workgroup's chain sums may be waiting for t's aggregate
         if (have_t && lane == 0) agg_publish(agg, t, Tn);
       }
@@ -394,10 +400,10 @@ __device__ __forceinline__ uint32_t zvc_c_iteration(
       // the next ticket goes out now and has a whole iteration to come back
       if (have_t && lane == 0) {
         C.pend = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if constexpr (ESZ == 2) agg_publish(agg, t, Tn);
+        if constexpr (!kLateStores) agg_publish(agg, t, Tn);
       }
     }
-    if constexpr (ESZ == 4) {
+    if constexpr (kLateStores) {
       // The chain loads go out before t's aggregate and masks, which are a
       // fixed count of stores, so the chain sum of the next iteration waits
       // only for its loads (memory operations retire in order).  The
@@ -416,8 +422,7 @@ __device__ __forceinline__ uint32_t zvc_c_iteration(
       __builtin_amdgcn_raw_buffer_store_b32(Tn + 1, ra, lane == 0 ? 4 * t : 4 * num_tiles, 0, 16 /* sc1 */);
       zvc_c_store_masks_full<ESZ>(L, dst, t, have_t && t < full, lane);
     } else {
-      // 16-bit elements: the two extra quads of masks per lane would not fit
-      // in registers beside the chain words (they spilled)
+      // the order before: aggregate (above) and masks, then the chain loads
       if (have_t) zvc_c_store_masks<ESZ>(L, dst, t, W, lane);
       if (have_p1) {
         C.chain_lo = have_p2 ? (uint64_t)tp2 + 1 : 0;
