@@ -546,12 +546,14 @@ __device__ __forceinline__ uint32_t stream_u32(const uint8_t* __restrict__ src, 
   return v;
 }
 
-// Waves (windows) per decoder workgroup.  The windows are independent and a
-// workgroup keeps its LDS until its slowest window is done, so one window per
-// workgroup frees each window's LDS as soon as it ends (measured 1-2 points of
-// HBM peak better than 2 or 4 per workgroup at every density).
+// Waves (windows) per decoder workgroup.  The windows are independent; a
+// workgroup keeps its LDS until its slowest window is done, but half as many
+// workgroups start per byte.  Two per workgroup: 59.6 against 55.7 % of HBM
+// peak at s = 0.99 (fp32, 4 GiB; fp16 56.6 against 53.2), within a point
+// elsewhere except s = 1 (79.0 against 81.0); four: no better at s = 0.99 and
+// 76.6 % at s = 1.
 #ifndef CDMA_RLE_DEC_WAVES
-#define CDMA_RLE_DEC_WAVES 1
+#define CDMA_RLE_DEC_WAVES 2
 #endif
 constexpr int kRleDecWaves = CDMA_RLE_DEC_WAVES;
 constexpr int kRleDecBlock = 64 * kRleDecWaves;
