@@ -285,7 +285,9 @@ __device__ __forceinline__ void rle_c_compact(uint8_t* __restrict__ st, const ui
     if (q.p_w > q.r_w) lds_u16(blk, 2 * q.r_w, 0);
   }
   // values follow the runs: a lane's first value of vector j comes after the
-  // nonzeros before its mask word and those below its bits there
+  // nonzeros before its mask word and those below its bits there.  A window
+  // without run boundaries holds no nonzero: its per-element tests are skipped.
+  if (!__ballot(q.T != 0)) return;
 #pragma unroll
   for (int j = 0; j < S::V; ++j) {
     const uint32_t c = (uint32_t)(j * 64 + lane);

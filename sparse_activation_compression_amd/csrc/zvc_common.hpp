@@ -60,26 +60,6 @@ __device__ __forceinline__ u32x4 apply_op(u32x4 v) {
   return v;
 }
 
-// Per-element nonzero bits of one 16-byte vector (bit k = element k).
-template <int ESZ>
-__device__ __forceinline__ uint32_t vec_nz_bits(u32x4 v) {
-  if constexpr (ESZ == 4) {
-    return (uint32_t)(v.x != 0) | ((uint32_t)(v.y != 0) << 1) | ((uint32_t)(v.z != 0) << 2) |
-           ((uint32_t)(v.w != 0) << 3);
-  } else {
-    uint32_t r = 0;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t w = v[k];
-      r |= ((uint32_t)((w & 0xFFFFu) != 0) << (2 * k)) | ((uint32_t)((w >> 16) != 0) << (2 * k + 1));
-    }
-    return r;
-  }
-}
-
-// Per-element nonzero bits of one 16-byte vector placed at bit sh of a
-// window mask (bit sh + k = element k), with min(x, 1) as the 0/1 test so
-// each element costs one min and one shift-or.
 // min(x, 1): 0 for 0, else 1.  Written as the instruction itself because the
 // compiler turns the plain expression into a compare and a select (two
 // instructions and a hazard wait).
@@ -89,6 +69,33 @@ __device__ __forceinline__ uint32_t nz01(uint32_t x) {
   return r;
 }
 
+// min(x, 1) on each 16-bit half of x at once: 0 for a zero half, else 1, at
+// bits 0 and 16.
+__device__ __forceinline__ uint32_t pk_nz01(uint32_t x) {
+  uint32_t r;
+  asm("v_pk_min_u16 %0, %1, %2" : "=v"(r) : "v"(x), "s"(0x00010001u));
+  return r;
+}
+
+// Per-element nonzero bits of one 16-byte vector (bit k = element k).  For
+// 16-bit elements one packed min gives a word's two 0/1 tests at bits 0 and
+// 16; the four words' results are interleaved into element order with three
+// shift-ors and one fold of the high half down by 15 bits.
+template <int ESZ>
+__device__ __forceinline__ uint32_t vec_nz_bits(u32x4 v) {
+  if constexpr (ESZ == 4) {
+    return nz01(v.x) | (nz01(v.y) << 1) | (nz01(v.z) << 2) | (nz01(v.w) << 3);
+  } else {
+    const uint32_t a = pk_nz01(v.x) | (pk_nz01(v.y) << 2);  // bits 0, 2 and 16, 18
+    const uint32_t b = pk_nz01(v.z) | (pk_nz01(v.w) << 2);
+    const uint32_t c = a | (b << 4);  // low halves at even bits 0-6, high halves at 16-22
+    return (c | (c >> 15)) & 0xFFu;
+  }
+}
+
+// Per-element nonzero bits of one 16-byte vector placed at bit sh of a
+// window mask (bit sh + k = element k), with min(x, 1) as the 0/1 test so
+// each element costs one min and one shift-or.
 template <int ESZ>
 __device__ __forceinline__ uint32_t vec_nz_at(u32x4 v, uint32_t sh) {
   if constexpr (ESZ == 4) {
