@@ -109,6 +109,7 @@ struct RleCShape {
   static constexpr int BLKMAX = RleShape<ESZ>::BLKMAX;
   static constexpr int STAGE = NW * BLKMAX + 16;
   static_assert(V * 64 * EPL == E, "a wavefront must cover one window");
+  static_assert(NW * (E + 2) < (1 << 15), "a tile's entries and nonzeros fit 15-bit fields");
 };
 
 template <int ESZ>
@@ -117,7 +118,7 @@ struct RleCLds {
   uint64_t excl;                        // packed exclusive prefix of the tile stored this iteration
   uint64_t agg2;                        // and its packed aggregate
   uint64_t agg[2];                      // packed aggregate of the tile classified in an iteration of parity b
-  uint32_t pw[S::NW], vw[S::NW];        // per-window entries and nonzeros of the tile being classified
+  uint32_t pv[S::NW];                   // per-window entries | nonzeros << 16 of the tile being classified
   uint32_t next;                        // ticket handed from the control wave to the data waves
   uint32_t mode;                        // start_mode's choice (selects the ticket source)
   uint32_t init[3];                     // the first three tickets
@@ -185,7 +186,7 @@ struct RleAggDec {
 // Classify tile t's window of this data wave (its vectors in cur): window
 // masks and per-word nonzero prefixes to L.mask[b] / L.pre[b], the lane's
 // run boundaries and counts to q, and the window's entry and nonzero counts
-// to L.pw / L.vw.  The window's mask words are written and read by this wave
+// to L.pv.  The window's mask words are written and read by this wave
 // only, so a wave-level fence orders them.
 template <int ESZ, int OP>
 __device__ __forceinline__ void rle_c_classify(RleCLds<ESZ>& L, u32x4 (&cur)[RleCShape<ESZ>::V], RleLane& q, int b,
@@ -217,16 +218,8 @@ __device__ __forceinline__ void rle_c_classify(RleCLds<ESZ>& L, u32x4 (&cur)[Rle
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  // one scan over the window's mask words gives its nonzero count and, for
-  // the value placement, the nonzeros before every word
-  uint32_t v_w;
-  {
-    const uint32_t x = lane < S::WPW ? wm[lane] : 0u;
-    const uint32_t c = (uint32_t)__builtin_popcount(x);
-    const uint32_t inc = wave_incl_scan(c);
-    if (lane < S::WPW) L.pre[b][wave * S::WPW + lane] = inc - c;
-    v_w = read_lane(inc, 63);
-  }
+  // nonzeros of the mask word this lane reads (lanes below WPW)
+  const uint32_t c = (uint32_t)__builtin_popcount(lane < S::WPW ? wm[lane] : 0u);
   // boundary bits of this lane's positions: element i starts a run when it
   // differs from element i-1 (the element before the window counts as zero)
   uint32_t T = 0;
@@ -244,15 +237,22 @@ __device__ __forceinline__ void rle_c_classify(RleCLds<ESZ>& L, u32x4 (&cur)[Rle
     if (rem < SB) T &= (1u << rem) - 1;
   }
   const uint32_t tc = (uint32_t)__builtin_popcount(T);
-  const uint32_t tinc = wave_incl_scan(tc);
+  // One scan for both counts: the word's nonzeros in the low half, the
+  // lane's boundaries in the high half (each totals at most E < 2^16, so the
+  // halves never carry).  It gives the window's nonzeros and, for the value
+  // placement, the nonzeros before every word; the window's runs and the
+  // boundaries before this lane.
+  static_assert(S::E < (1 << 16), "16-bit count fields");
+  const uint32_t x = c | (tc << 16);
+  const uint32_t inc = wave_incl_scan(x);
+  const uint32_t ex = inc - x, tot = read_lane(inc, 63);
+  if (lane < S::WPW) L.pre[b][wave * S::WPW + lane] = ex & 0xFFFFu;
+  const uint32_t v_w = tot & 0xFFFFu;
   q.T = T;
-  q.texcl = tinc - tc;
-  q.r_w = q.Lw ? 1 + read_lane(tinc, 63) : 0u;
+  q.texcl = ex >> 16;
+  q.r_w = q.Lw ? 1 + (tot >> 16) : 0u;
   q.p_w = ESZ == 4 ? q.r_w + (q.r_w & 1) : q.r_w;
-  if (lane == 0) {
-    L.pw[wave] = q.Lw ? q.p_w : 0u;
-    L.vw[wave] = q.Lw ? v_w : 0u;
-  }
+  if (lane == 0) L.pv[wave] = q.Lw ? q.p_w | (v_w << 16) : 0u;
 }
 
 // Write the window's block (run lengths, then its nonzeros in index order)
@@ -363,12 +363,11 @@ __device__ __forceinline__ uint32_t rle_c_iteration(RleCLds<ESZ>& L, u32x4 (&cur
 
   // ---- phase Y ----
   if (data) {
-    if (have_t) {  // t's window bases inside its tile
-      const uint32_t pl = lane < S::NW ? L.pw[lane] : 0u;
-      const uint32_t vl = lane < S::NW ? L.vw[lane] : 0u;
-      const uint32_t pi = wave_incl_scan(pl), vi = wave_incl_scan(vl);
-      q.Pb = read_lane(pi - pl, wave);
-      q.Vb = read_lane(vi - vl, wave);
+    if (have_t) {  // t's window bases inside its tile: one scan of the packed counts
+      const uint32_t x = lane < S::NW ? L.pv[lane] : 0u;
+      const uint32_t ex = read_lane(wave_incl_scan(x) - x, wave);
+      q.Pb = ex & 0xFFFFu;
+      q.Vb = ex >> 16;
     }
     if (have_p2) {
       const uint64_t a2 = L.agg2;
@@ -397,9 +396,8 @@ __device__ __forceinline__ uint32_t rle_c_iteration(RleCLds<ESZ>& L, u32x4 (&cur
     // the next ticket goes out now and has a whole iteration to come back
     if (lane == 0 && have_t) C.pend = tk.raw();
     if (have_t) {
-      const uint32_t pl = lane < S::NW ? L.pw[lane] : 0u;
-      const uint32_t vl = lane < S::NW ? L.vw[lane] : 0u;
-      const uint32_t P = read_lane(wave_incl_scan(pl), 63), Vs = read_lane(wave_incl_scan(vl), 63);
+      const uint32_t tot = read_lane(wave_incl_scan(lane < S::NW ? L.pv[lane] : 0u), 63);
+      const uint32_t P = tot & 0xFFFFu, Vs = tot >> 16;
       if (lane == 0) {
         L.agg[b] = ((uint64_t)P << 31) | Vs;
         agg_publish(aggw, t, (P << 15) | Vs);
