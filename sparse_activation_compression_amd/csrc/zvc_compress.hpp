@@ -102,6 +102,7 @@ struct ZvcCLds {
   uint32_t mode;         // kModeStatic or kModeTickets (start_mode)
   uint32_t init[3];      // the first tickets
   uint32_t tot[S::SEG];
+  uint32_t dump[64];     // one word per lane for the 32-bit compaction's discarded writes
   __attribute__((aligned(16))) uint32_t mask[S::WPT];
   __attribute__((aligned(16))) uint8_t stage[2][S::STAGE];
 };
@@ -235,10 +236,16 @@ __device__ __forceinline__ void zvc_c_classify(ZvcCLds<ESZ>& L, const u32x4 (&v)
 }
 
 // Write the nonzeros of the tile held in v into stage, in index order, at the
-// places R gives (data waves).
+// places R gives (data waves).  32-bit elements are written without a branch:
+// in increasing element order every element is stored at its nonzero rank, so
+// a zero writes the slot that the lane's next nonzero overwrites right after
+// (a wave's LDS writes complete in order); zeros after the row's last nonzero
+// go to the lane's dump word instead of the next lane's first slot.  16-bit
+// elements keep a branch per element: the branch-free form spilled there.
 template <int ESZ>
 __device__ __forceinline__ void zvc_c_compact(uint8_t* __restrict__ st, const u32x4 (&v)[ZvcCShape<ESZ>::V],
-                                              const ZvcRows<ZvcCShape<ESZ>::EPL, ZvcCShape<ESZ>::V>& R) {
+                                              const ZvcRows<ZvcCShape<ESZ>::EPL, ZvcCShape<ESZ>::V>& R,
+                                              uint8_t* __restrict__ dump) {
   using S = ZvcCShape<ESZ>;
 #pragma unroll
   for (int j = 0; j < S::V; ++j) {
@@ -246,7 +253,11 @@ __device__ __forceinline__ void zvc_c_compact(uint8_t* __restrict__ st, const u3
     const uint32_t bits = R.bits_of(j);
 #pragma unroll
     for (int k = 0; k < S::EPL; ++k) {
-      if ((bits >> k) & 1u) {
+      if constexpr (ESZ == 4) {
+        uint8_t* a = (bits >> k) ? st + pos : dump;
+        store_elem<ESZ>(a, vec_elem<ESZ>(v[j], k));
+        pos += ESZ * ((bits >> k) & 1u);
+      } else if ((bits >> k) & 1u) {
         store_elem<ESZ>(st + pos, vec_elem<ESZ>(v[j], k));
         pos += ESZ;
       }
@@ -338,7 +349,7 @@ __device__ __forceinline__ uint32_t zvc_c_iteration(
   const bool data = wave < kDWaves;
 
   // ---- phase X ----
-  if (data && have_p1) zvc_c_compact<ESZ>(L.stage[buf ^ 1], prev, rp);
+  if (data && have_p1) zvc_c_compact<ESZ>(L.stage[buf ^ 1], prev, rp, reinterpret_cast<uint8_t*>(&L.dump[lane]));
   {
     const bool load = __builtin_amdgcn_readfirstlane(wave) < kDWaves && tl < full;
     zvc_c_load_full<ESZ>(prev, src, tl, load, wave, lane);
