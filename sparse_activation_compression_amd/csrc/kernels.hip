@@ -153,6 +153,15 @@ static hipError_t zvc_compress_t(const void* src, uint64_t n, void* act, void* d
   const uint64_t tiles = zvc_compress_tiles(ESZ, n);
   hipError_t e = clear_workspace(ws, tiles, out_bytes, s);
   if (e != hipSuccess) return e;
+  if constexpr (OP == kOpNone) {
+    // at most one tile per resident workgroup: one workgroup per tile, single pass
+    auto one = zvc_compress_single_kernel<ESZ>;
+    if (tiles <= resident_groups(reinterpret_cast<const void*>(one), kCBlock)) {
+      one<<<(unsigned)tiles, kCBlock, 0, s>>>(static_cast<const uint8_t*>(src), n, static_cast<uint8_t*>(dst),
+                                              out_bytes, ws_counter(ws), ws_agg(ws), (uint32_t)tiles);
+      return hipGetLastError();
+    }
+  }
   // persistent grid: about one workgroup per CU, tiles static or by ticket
   auto kern = zvc_compress_kernel<ESZ, OP>;
   const uint64_t res = resident_groups(reinterpret_cast<const void*>(kern), kCBlock);

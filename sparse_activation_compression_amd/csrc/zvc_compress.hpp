@@ -507,4 +507,72 @@ __global__ __launch_bounds__(kCBlock) void zvc_compress_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// single pass: maps of at most one tile per resident workgroup
+// ---------------------------------------------------------------------------
+//
+// Such a map would give every workgroup of the persistent grid at most one
+// tile, which the pipeline above takes through three iterations (load;
+// classify and compact; chain sum and store) before storing it.  Here each
+// workgroup draws one tile and runs the same steps back to back: load,
+// classify, publish the tile's aggregate and store its masks (their place
+// depends only on the tile), compact the values, sum the aggregates of all
+// tiles before it, store the values.  A workgroup only waits for tiles drawn
+// before its own, by workgroups that have started and publish without
+// waiting, so every wait ends (the chain sum's spin bound still applies).
+template <int ESZ>
+__global__ __launch_bounds__(kCBlock) void zvc_compress_single_kernel(
+    const uint8_t* __restrict__ src, uint64_t n, uint8_t* __restrict__ dst, uint64_t* __restrict__ out_bytes,
+    uint32_t* __restrict__ counter, uint32_t* __restrict__ agg, uint32_t num_tiles) {
+  using S = ZvcCShape<ESZ>;
+  constexpr int V = S::V;
+  __shared__ ZvcCLds<ESZ> L;
+  const int tid = threadIdx.x;
+  const int lane = (int)lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool data = wave < kDWaves;
+  const uint64_t W = (n + 31) / 32;
+  const uint32_t full = (uint32_t)(n / S::TE);  // tiles with no element past n
+  if (tid == 0) L.next = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  // one workgroup per tile, so every ticket names a tile below num_tiles
+  const uint32_t t = __builtin_amdgcn_readfirstlane(L.next);
+  ZvcRows<S::EPL, V> R;
+  u32x4 v[V];
+  if (data) {
+    if (t < full) zvc_c_load_full<ESZ>(v, src, t, true, wave, lane);
+    else zvc_c_load_bounded<ESZ>(v, src, n, t, wave, lane);
+    zvc_c_classify<ESZ>(L, v, R, wave, lane);
+  }
+  __syncthreads();
+  // segment bases and the tile's nonzeros (every wave scans the segment totals)
+  const uint32_t x = lane < S::SEG ? L.tot[lane] : 0u;
+  const uint32_t inc = wave_incl_scan(x);
+  const uint32_t Tn = read_lane(inc, 63);
+  if (data) {
+#pragma unroll
+    for (int j = 0; j < V; j += 2)
+      R.base[j / 2] = read_lane(inc - x, wave * V + j) | (read_lane(inc - x, wave * V + j + 1) << 16);
+    zvc_c_compact<ESZ>(L.stage[0], v, R, reinterpret_cast<uint8_t*>(&L.dump[lane]));
+  } else {
+    if (lane == 0) agg_publish(agg, t, Tn);
+    zvc_c_store_masks<ESZ>(L, dst, t, W, lane);
+    ChainRound cr;
+    chain_issue(agg, 0, t, cr);
+    bool stuck = false;
+    const uint64_t X = chain_sum(agg, 0, t, cr, &stuck, [](uint32_t a) { return a; });
+    if (lane == 0) {
+      L.excl = X;
+      if (stuck) atomicMax(reinterpret_cast<unsigned long long*>(out_bytes), kSizeInternalError);
+    }
+  }
+  __syncthreads();
+  if (data) {
+    const uint64_t A = 4 * W + (uint64_t)ESZ * L.excl;
+    store_staged<ESZ, kDThreads>(L.stage[0], ESZ * Tn, A, dst, tid);
+    if (t == num_tiles - 1 && tid == 0)
+      atomicMax(reinterpret_cast<unsigned long long*>(out_bytes), A + (uint64_t)ESZ * Tn);
+  }
+}
+
 }  // namespace cdma
