@@ -20,8 +20,12 @@ def _sizes(esz):
     return [1, 3, 4, 5, 8, 9, 31, 32, 33, 63, 64, 65, 255, 256, 257, 1023, 1024, 1025,
             t - 1, t, t + 1, 2 * t + 17, 5 * t + 3, 64 * t + 100,
             # compress tiles: a bounded last tile, none (exact multiples), and
-            # more tiles than a grid of one workgroup per CU takes in one round
-            c - 1, c, c + 1, 2 * c, 3 * c - 1, 3 * c + 1, 257 * c, 257 * c + 1, 513 * c - 1]
+            # more tiles than a grid of one workgroup per CU takes in one round;
+            # 255-256 tiles take the single-pass kernel (one workgroup per tile,
+            # up to one per resident workgroup: 256 on a 256-CU GPU), 257 and
+            # more the persistent one
+            c - 1, c, c + 1, 2 * c, 3 * c - 1, 3 * c + 1, 255 * c + 7, 256 * c, 257 * c, 257 * c + 1,
+            513 * c - 1]
 
 
 @pytest.mark.parametrize("esz", [4, 2])
