@@ -216,10 +216,8 @@ __device__ __forceinline__ void zvc_c_classify(ZvcCLds<ESZ>& L, const u32x4 (&v)
       for (int j = 0; j < V; ++j) L.tot[wave * V + j] = tot[j];
     }
   } else {
-    // 16-bit elements: one scan per row measured faster than the packed form
+    uint32_t cnt[V], ex[V], tot[V];
     R.bits = 0;
-#pragma unroll
-    for (int g = 0; g < V / R.PER; ++g) R.ex[g] = 0;
 #pragma unroll
     for (int j = 0; j < V; ++j) {
       const uint32_t c = (uint32_t)((wave * V + j) * 64 + lane);
@@ -227,10 +225,18 @@ __device__ __forceinline__ void zvc_c_classify(ZvcCLds<ESZ>& L, const u32x4 (&v)
       R.bits |= b << (S::EPL * j);
       const uint32_t m = group_or<S::LPW>(b << ((lane % S::LPW) * S::EPL));
       if (lane % S::LPW == 0) L.mask[c / S::LPW] = m;
-      const uint32_t cnt = (uint32_t)__builtin_popcount(b);
-      const uint32_t inc = wave_incl_scan(cnt);
-      R.ex[j / R.PER] |= (inc - cnt) << (R.F * (j % R.PER));
-      if (lane == 63) L.tot[wave * V + j] = inc;
+      cnt[j] = (uint32_t)__builtin_popcount(b);
+    }
+    packed_row_scan<S::EPL, V>(cnt, ex, tot);
+#pragma unroll
+    for (int g = 0; g < V / R.PER; ++g) {
+      R.ex[g] = 0;
+#pragma unroll
+      for (int i = 0; i < R.PER; ++i) R.ex[g] |= ex[g * R.PER + i] << (R.F * i);
+    }
+    if (lane == 63) {
+#pragma unroll
+      for (int j = 0; j < V; ++j) L.tot[wave * V + j] = tot[j];
     }
   }
 }
