@@ -541,8 +541,14 @@ __global__ __launch_bounds__(kCBlock) void zvc_compress_single_kernel(
   const uint32_t full = (uint32_t)(n / S::TE);  // tiles with no element past n
   if (tid == 0) L.next = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
-  // one workgroup per tile, so every ticket names a tile below num_tiles
+  // One workgroup per tile, so every ticket names a tile below num_tiles when
+  // the counter starts cleared.  A call that overlaps another on the same
+  // workspace breaks that: report it instead of reading past the input.
   const uint32_t t = __builtin_amdgcn_readfirstlane(L.next);
+  if (t >= num_tiles) {
+    if (tid == 0) atomicMax(reinterpret_cast<unsigned long long*>(out_bytes), kSizeInternalError);
+    return;
+  }
   ZvcRows<S::EPL, V> R;
   u32x4 v[V];
   if (data) {
