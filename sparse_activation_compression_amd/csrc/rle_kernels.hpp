@@ -676,39 +676,45 @@ __global__ __launch_bounds__(kRleDecBlock) void rle_decompress_kernel(
       const uint32_t jpad = r < p ? np - 1 : ~0u;
       const uint32_t* pw = reinterpret_cast<const uint32_t*>(blk + shift);
       // words past j1 (at most per - 1 of them) still lie in the stage buffer
-      // and are read, then ignored
-      uint32_t w[kMaxPer];
+      // and are read, then ignored.  K bounds per at compile time: 1 (at most
+      // 64 pairs, the sparse windows) or the largest a window can have.
+      auto pairs = [&](auto kc) {
+        constexpr int K = decltype(kc)::value;
+        uint32_t w[K];
 #pragma unroll
-      for (int i = 0; i < kMaxPer; ++i)
-        if ((uint32_t)i < per) w[i] = pw[j0 + i];
-      uint32_t bad = 0;
+        for (int i = 0; i < K; ++i)
+          if ((uint32_t)i < per) w[i] = pw[j0 + i];
+        uint32_t bad = 0;
 #pragma unroll
-      for (int i = 0; i < kMaxPer; ++i) {
-        if ((uint32_t)i < per) {
-          const uint32_t j = j0 + i;
-          const uint32_t x = j < j1 ? w[i] : 0u;
-          const uint32_t z = x & 0xFFFFu, nz = x >> 16;
-          sum += z + nz;
-          odd += nz;
-          bad |= (uint32_t)(j < j1) & (((uint32_t)(z == 0) & (uint32_t)(j != 0)) |
-                                       ((uint32_t)(nz == 0) & (uint32_t)(j != jpad)));
+        for (int i = 0; i < K; ++i) {
+          if ((uint32_t)i < per) {
+            const uint32_t j = j0 + i;
+            const uint32_t x = j < j1 ? w[i] : 0u;
+            const uint32_t z = x & 0xFFFFu, nz = x >> 16;
+            sum += z + nz;
+            odd += nz;
+            bad |= (uint32_t)(j < j1) & (((uint32_t)(z == 0) & (uint32_t)(j != 0)) |
+                                         ((uint32_t)(nz == 0) & (uint32_t)(j != jpad)));
+          }
         }
-      }
-      zero_len = bad != 0;
-      inc = wave_incl_scan(sum);
-      uint32_t start = inc - sum;
+        zero_len = bad != 0;
+        inc = wave_incl_scan(sum);
+        uint32_t start = inc - sum;
 #pragma unroll
-      for (int i = 0; i < kMaxPer; ++i) {
-        if ((uint32_t)i < per) {
-          const uint32_t j = j0 + i;
-          const bool in = j < j1;
-          const uint32_t z = w[i] & 0xFFFFu, nz = w[i] >> 16;
-          if (in && j > 0 && start < Lw) toggle(start);
-          const uint32_t s2 = start + z;
-          if (in && j != jpad && s2 < Lw) toggle(s2);
-          start = s2 + nz;
+        for (int i = 0; i < K; ++i) {
+          if ((uint32_t)i < per) {
+            const uint32_t j = j0 + i;
+            const bool in = j < j1;
+            const uint32_t z = w[i] & 0xFFFFu, nz = w[i] >> 16;
+            if (in && j > 0 && start < Lw) toggle(start);
+            const uint32_t s2 = start + z;
+            if (in && j != jpad && s2 < Lw) toggle(s2);
+            start = s2 + nz;
+          }
         }
-      }
+      };
+      if (per == 1) pairs(std::integral_constant<int, 1>{});
+      else pairs(std::integral_constant<int, kMaxPer>{});
     } else {
       // one u16 entry at a time, each lane a contiguous range of entries
       const uint32_t per = (r + 63) / 64;
